@@ -1,0 +1,188 @@
+"""CPU oracle for the Mamba2 decode-step selective_state_update.
+
+TEST INFRASTRUCTURE ONLY: imported by ``tests/``, by ``__graft_entry__.smoke()``
+and by the CPU-baseline leg of ``bench.py``; never by the product package. It
+shares no code with the GPU library.
+
+This module marshals numpy arrays into the plain-C fp64 oracle in
+``ssu_ref.c`` (see that file for the definition it computes and the passages it
+follows). Arrays are passed with their own strides, so the packed xBC views and
+the per-head broadcasts reach the oracle exactly as they are stored.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+from .build import LIB_PATH, build_oracle
+
+_i32, _i64 = ctypes.c_int32, ctypes.c_int64
+_vp = ctypes.c_void_p
+
+
+class RefArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", _i32), ("nheads", _i32), ("headdim", _i32), ("dstate", _i32),
+        ("ngroups", _i32), ("dt_softplus", _i32), ("nsteps", _i32), ("nthreads", _i32),
+        ("pool_slots", _i64),
+        ("state", _vp), ("st_slot", _i64), ("st_head", _i64), ("st_row", _i64),
+        ("idx", _vp),
+        ("x", _vp), ("x_t", _i64), ("x_b", _i64), ("x_h", _i64), ("x_p", _i64),
+        ("B", _vp), ("B_t", _i64), ("B_b", _i64), ("B_g", _i64), ("B_n", _i64),
+        ("C", _vp), ("C_t", _i64), ("C_b", _i64), ("C_g", _i64), ("C_n", _i64),
+        ("dt", _vp), ("dt_t", _i64), ("dt_b", _i64), ("dt_h", _i64),
+        ("dt_bias", _vp), ("dt_bias_h", _i64),
+        ("A", _vp), ("A_h", _i64),
+        ("D", _vp), ("D_h", _i64),
+        ("out", _vp), ("out_t", _i64), ("out_b", _i64), ("out_h", _i64), ("out_p", _i64),
+        ("state_ref", _vp), ("y_ref", _vp), ("tau_ref", _vp),
+    ]
+
+
+def _estrides(a: np.ndarray):
+    """Element strides of a numpy array (byte strides / itemsize)."""
+    out = []
+    for s in a.strides:
+        if s % a.itemsize:
+            raise ValueError("stride not a multiple of the element size")
+        out.append(s // a.itemsize)
+    return out
+
+
+def _ptr(a):
+    return None if a is None else a.ctypes.data
+
+
+class Oracle:
+    """Handle on one build of the oracle library (the default build, or any other
+    path, which the tests use to load deliberately broken copies)."""
+
+    def __init__(self, path: str | None = None):
+        if path is None:
+            path = LIB_PATH
+            if not os.path.exists(path):
+                build_oracle()
+        self.path = path
+        lib = ctypes.CDLL(path)
+        lib.ssu_ref_run.argtypes = [ctypes.POINTER(RefArgs)]
+        lib.ssu_ref_run.restype = _i32
+        lib.ssu_ref_softplus.argtypes = [ctypes.c_double]
+        lib.ssu_ref_softplus.restype = ctypes.c_double
+        lib.ssu_ref_discretize.argtypes = [ctypes.c_double, ctypes.c_double, ctypes.c_double, _i32,
+                                           ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_double)]
+        lib.ssu_ref_discretize.restype = None
+        lib.ssu_ref_bf16_rne.argtypes = [ctypes.c_float]
+        lib.ssu_ref_bf16_rne.restype = ctypes.c_uint16
+        lib.ssu_ref_max_threads.argtypes = []
+        lib.ssu_ref_max_threads.restype = _i32
+        self.lib = lib
+
+    # -- scalar pieces -------------------------------------------------------
+    def softplus(self, u: float) -> float:
+        return self.lib.ssu_ref_softplus(float(u))
+
+    def discretize(self, dt: float, dt_bias: float, A: float, softplus: bool = True):
+        d, a = ctypes.c_double(), ctypes.c_double()
+        self.lib.ssu_ref_discretize(float(dt), float(dt_bias), float(A), int(bool(softplus)),
+                                    ctypes.byref(d), ctypes.byref(a))
+        return d.value, a.value
+
+    def bf16_rne(self, values) -> np.ndarray:
+        v = np.asarray(values, dtype=np.float32).ravel()
+        return np.array([self.lib.ssu_ref_bf16_rne(float(f)) for f in v], dtype=np.uint16)
+
+    def max_threads(self) -> int:
+        return int(self.lib.ssu_ref_max_threads())
+
+    # -- the step ------------------------------------------------------------
+    def run(self, pool, idx, x, B, C, dt, A, dt_bias=None, D=None, dt_softplus=True,
+            want_state=True, want_y=True, nthreads=0, out=None):
+        """Advance ``pool`` (float32 numpy array [slots, H, P, N], updated in place)
+        by one token (x [bs,H,P], B/C [bs,G,N], dt [bs,H]) or by K tokens
+        (x [K,bs,H,P], B/C [K,bs,G,N], dt [K,bs,H]).
+
+        Returns a dict: ``out`` (uint16 bf16 bits, shaped like x), ``y`` and
+        ``tau`` (fp64, shaped like x) and ``state`` (fp64 [bs,H,P,N], S' after
+        the last token) when requested.
+        """
+        single = x.ndim == 3
+        if single:
+            x, B, C, dt = x[None], B[None], C[None], dt[None]
+        K, bs, H, P = x.shape
+        G, N = B.shape[2], B.shape[3]
+        if pool.dtype != np.float32 or pool.ndim != 4 or pool.shape[1:] != (H, P, N):
+            raise ValueError(f"pool must be float32 [slots,{H},{P},{N}], got {pool.dtype} {pool.shape}")
+        if pool.strides[3] != 4:
+            raise ValueError("pool's dstate axis must be contiguous")
+        if not pool.flags.writeable:
+            raise ValueError("pool must be writeable")
+        for name, arr, shp in (("B", B, (K, bs, G, N)), ("C", C, (K, bs, G, N)), ("dt", dt, (K, bs, H))):
+            if arr.shape != shp:
+                raise ValueError(f"{name} shape {arr.shape} != {shp}")
+        for name, arr in (("x", x), ("B", B), ("C", C), ("dt", dt)):
+            if arr.dtype != np.uint16:
+                raise ValueError(f"{name} must hold bf16 bits (uint16)")
+        idx = np.ascontiguousarray(idx, dtype=np.int32)
+        if idx.shape != (bs,):
+            raise ValueError("idx must be [bs]")
+        A = np.ascontiguousarray(A, dtype=np.float32)
+        dt_bias = None if dt_bias is None else np.ascontiguousarray(dt_bias, dtype=np.float32)
+        D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+        for name, arr in (("A", A), ("dt_bias", dt_bias), ("D", D)):
+            if arr is not None and arr.shape != (H,):
+                raise ValueError(f"{name} must be [H]")
+        if out is None:
+            out = np.zeros((K, bs, H, P), dtype=np.uint16)
+        elif single:
+            out = out[None]
+        y = np.full((K, bs, H, P), np.nan) if want_y else None
+        tau = np.full((K, bs, H, P), np.nan) if want_y else None
+        state = np.full((bs, H, P, N), np.nan) if want_state else None
+
+        a = RefArgs()
+        a.batch, a.nheads, a.headdim, a.dstate, a.ngroups = bs, H, P, N, G
+        a.dt_softplus, a.nsteps, a.nthreads = int(bool(dt_softplus)), K, int(nthreads)
+        a.pool_slots = pool.shape[0]
+        a.state = _ptr(pool)
+        a.st_slot, a.st_head, a.st_row, _ = _estrides(pool)
+        a.idx = _ptr(idx)
+        a.x = _ptr(x)
+        a.x_t, a.x_b, a.x_h, a.x_p = _estrides(x)
+        a.B = _ptr(B)
+        a.B_t, a.B_b, a.B_g, a.B_n = _estrides(B)
+        a.C = _ptr(C)
+        a.C_t, a.C_b, a.C_g, a.C_n = _estrides(C)
+        a.dt = _ptr(dt)
+        a.dt_t, a.dt_b, a.dt_h = _estrides(dt)
+        a.dt_bias, a.dt_bias_h = _ptr(dt_bias), 1
+        a.A, a.A_h = _ptr(A), 1
+        a.D, a.D_h = _ptr(D), 1
+        a.out = _ptr(out)
+        a.out_t, a.out_b, a.out_h, a.out_p = _estrides(out)
+        a.state_ref, a.y_ref, a.tau_ref = _ptr(state), _ptr(y), _ptr(tau)
+        # keep every array alive across the call
+        keep = (pool, idx, x, B, C, dt, A, dt_bias, D, out, y, tau, state)
+        rc = self.lib.ssu_ref_run(ctypes.byref(a))
+        del keep
+        if rc != 0:
+            raise ValueError({1: "bad shape", 2: "null pointer", 3: "duplicate slot index"}.get(rc, rc))
+        res = {"out": out[0] if single else out}
+        if want_y:
+            res["y"] = y[0] if single else y
+            res["tau"] = tau[0] if single else tau
+        if want_state:
+            res["state"] = state
+        return res
+
+
+_default: Oracle | None = None
+
+
+def get() -> Oracle:
+    """The oracle built from oracle/ssu_ref.c (built on first use if missing)."""
+    global _default
+    if _default is None:
+        _default = Oracle()
+    return _default

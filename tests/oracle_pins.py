@@ -1,0 +1,347 @@
+"""Pins of the CPU oracle against things other than itself.
+
+Each ``pin_*`` takes an ``oracle.Oracle`` and raises AssertionError when the
+oracle disagrees with what the mathematics or a library routine fixes. They are
+run against the real oracle (tests/test_oracle_pins.py) and against copies of
+it with planted mistakes (tests/test_oracle_mutants.py), which must each fail
+at least one pin.
+
+What pins what:
+  * discretisation  -- softplus closed forms and numpy.logaddexp; the dt_bias
+    generator's inverse softplus; exp(A * 0) = 1;
+  * bf16 rounding   -- torch's float32 -> bfloat16 conversion (ties, overflow,
+    subnormals, signed zero, NaN);
+  * rank-1 update   -- numpy a*S + delta*outer(x, B) in fp64; write-back is the
+    fp32 rounding of it;
+  * output          -- numpy S' @ C + D*x (matrix-vector product) in fp64;
+  * gather          -- untouched slots bitwise unchanged; permuting requests
+    permutes outputs; padding entries skipped; duplicates rejected;
+  * special cases   -- dt = 0 (softplus off, no bias) leaves the state unchanged;
+    A -> -1e9 collapses the state to delta*x*B; B = 0 is a pure decay; C = 0
+    gives out = bf16(D*x) exactly;
+  * groups          -- g(h) = h // (H/G) checked head by head;
+  * K steps         -- the fp64 scan equals the closed form of the unrolled
+    recurrence, and K single steps with fp32 storage stay within rounding of it;
+  * everything      -- an independent pure-Python brute force (tests/brute.py).
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+import ssu_inputs as si
+
+from . import brute
+
+
+def _rng(seed):
+    return np.random.Generator(np.random.PCG64(seed))
+
+
+def _small(H=3, P=8, N=16, G=1, bs=3, slots=7, seed=11, softplus=True):
+    return si.make_problem(H, P, N, G, bs, slots, seed, dt_softplus=softplus)
+
+
+def _run(o, p, pool=None, **kw):
+    pool = p.pool.copy() if pool is None else pool
+    args = dict(dt_bias=p.dt_bias, D=p.D, dt_softplus=p.dt_softplus)
+    args.update(kw)
+    r = o.run(pool, p.idx, p.x, p.B, p.C, p.dt, args.pop("A", p.A), **args)
+    return pool, r
+
+
+def _np_delta(dt_bits, bias, softplus):
+    u = si.bf16_values(dt_bits).astype(np.float64) + np.asarray(bias, dtype=np.float64)
+    return np.logaddexp(0.0, u) if softplus else u
+
+
+# --------------------------------------------------------------------------- #
+def pin_softplus_closed_forms(o):
+    assert abs(o.softplus(0.0) - math.log(2.0)) <= 1e-16
+    for u in np.concatenate([np.linspace(-50, 50, 201), [-700.0, 1000.0, 1e-300, -1e-300]]):
+        want = np.logaddexp(0.0, u)
+        got = o.softplus(u)
+        assert abs(got - want) <= 4e-16 * max(abs(want), 1e-300), (u, got, want)
+    # the dt_bias generator's inverse softplus: softplus(log(expm1(y))) = y
+    y = _rng(5).uniform(1e-3, 0.1, size=64)
+    for yy in y:
+        got = o.softplus(float(np.log(np.expm1(yy))))
+        assert abs(got - yy) <= 1e-14 * yy, (yy, got)
+    # discretisation: delta = u (softplus off), a = exp(A * delta); A*0 -> a = 1
+    d, a = o.discretize(0.0, 0.0, -3.5, softplus=False)
+    assert d == 0.0 and a == 1.0
+    d, a = o.discretize(0.25, 0.5, 0.0, softplus=True)
+    assert a == 1.0 and abs(d - np.logaddexp(0.0, 0.75)) <= 1e-16
+    for dt, bias, A, sp in ((0.3, -0.1, -2.0, False), (-1.5, 0.05, -7.25, True), (4.0, 0.02, -16.0, True)):
+        d, a = o.discretize(dt, bias, A, softplus=sp)
+        dd = np.logaddexp(0.0, dt + bias) if sp else dt + bias
+        assert abs(d - dd) <= 1e-15 * abs(dd)
+        assert abs(a - math.exp(A * dd)) <= 1e-15 * math.exp(A * dd)
+
+
+def pin_bf16_rounding(o):
+    import torch
+
+    rng = _rng(6)
+    vals = [rng.standard_normal(2000).astype(np.float32),
+            (rng.standard_normal(500) * 1e-39).astype(np.float32),    # subnormals
+            (rng.standard_normal(500) * 1e30).astype(np.float32)]
+    # exact ties: low half-word 0x8000, even and odd kept halves
+    hi = rng.integers(0, 0x7F7F, size=400, dtype=np.uint32)
+    vals.append(((hi << 16) | 0x8000).view(np.float32))
+    vals.append((((hi << 16) | 0x8000) | 0x80000000).view(np.float32))
+    vals.append(np.array([0.0, -0.0, np.inf, -np.inf, 3.3895313892515355e38, -3.4e38,
+                          np.finfo(np.float32).max, 1.0, -1.0, 2 ** -133, -(2 ** -140)],
+                         dtype=np.float32))
+    f = np.concatenate(vals)
+    want = torch.from_numpy(f).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    got = o.bf16_rne(f)
+    assert np.array_equal(got, want), np.nonzero(got != want)[0][:5]
+    nan = o.bf16_rne(np.array([np.nan], dtype=np.float32))[0]
+    assert (nan & 0x7F80) == 0x7F80 and (nan & 0x7F) != 0
+
+
+def pin_rank1_update(o):
+    for seed, softplus in ((21, True), (22, False)):
+        p = _small(seed=seed, softplus=softplus)
+        before = p.pool.copy()
+        pool, r = _run(o, p)
+        delta = _np_delta(p.dt, p.dt_bias[None, :], softplus)
+        for b in range(p.batch):
+            for h in range(p.nheads):
+                S0 = before[p.idx[b], h].astype(np.float64)
+                a = np.exp(np.float64(p.A[h]) * delta[b, h])
+                x = si.bf16_values(p.x[b, h]).astype(np.float64)
+                Bv = si.bf16_values(p.B[b, 0]).astype(np.float64)
+                want = a * S0 + delta[b, h] * np.outer(x, Bv)
+                got = r["state"][b, h]
+                assert np.allclose(got, want, rtol=1e-14, atol=1e-14), (b, h, np.abs(got - want).max())
+        # write-back is the fp32 rounding of S'
+        assert np.array_equal(pool[p.idx], r["state"].astype(np.float32))
+
+
+def pin_output_gemv(o):
+    p = _small(H=4, P=8, N=32, bs=3, slots=5, seed=31)
+    _, r = _run(o, p)
+    for b in range(p.batch):
+        for h in range(p.nheads):
+            S = r["state"][b, h]
+            Cv = si.bf16_values(p.C[b, 0]).astype(np.float64)
+            x = si.bf16_values(p.x[b, h]).astype(np.float64)
+            terms = S * Cv[None, :]
+            want = S @ Cv + np.float64(p.D[h]) * x
+            tau = np.abs(terms).sum(axis=1) + np.abs(np.float64(p.D[h]) * x)
+            assert np.all(np.abs(r["y"][b, h] - want) <= 1e-13 * tau), (b, h)
+            assert np.allclose(r["tau"][b, h], tau, rtol=1e-13)
+    import torch
+
+    y32 = torch.from_numpy(r["y"].astype(np.float32))
+    assert np.array_equal(r["out"], y32.to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16))
+
+
+def pin_gather(o):
+    p = _small(H=2, P=8, N=16, bs=4, slots=11, seed=41)
+    before = p.pool.copy()
+    pool, r = _run(o, p)
+    untouched = np.setdiff1d(np.arange(p.pool_slots), p.idx)
+    assert np.array_equal(pool[untouched].view(np.uint32), before[untouched].view(np.uint32))
+    assert not np.array_equal(pool[p.idx], before[p.idx])
+    # permuting the requests (idx, x, B, C, dt together) permutes the outputs
+    perm = np.array([2, 0, 3, 1])
+    q = si.make_problem(2, 8, 16, 1, 4, 11, 41, idx=p.idx[perm])
+    q.xbc = p.xbc[perm].copy()
+    q.dt = p.dt[perm].copy()
+    q.pool = before.copy()
+    pool2, r2 = _run(o, q)
+    assert np.array_equal(r2["out"], r["out"][perm])
+    assert np.array_equal(pool2.view(np.uint32), pool.view(np.uint32))
+    # slot ids outside [0, pool_slots) are padding: state and out rows untouched
+    q.idx = np.array([p.idx[2], -1, p.idx[3], p.pool_slots], dtype=np.int32)
+    q.xbc, q.dt = p.xbc.copy(), p.dt.copy()
+    pool3 = before.copy()
+    sentinel = np.full((4, 2, 8), 0x7FC1, dtype=np.uint16)
+    r3 = o.run(pool3, q.idx, q.x, q.B, q.C, q.dt, q.A, q.dt_bias, q.D, out=sentinel)
+    assert np.all(r3["out"][1] == 0x7FC1) and np.all(r3["out"][3] == 0x7FC1)
+    assert not np.any(r3["out"][[0, 2]] == 0x7FC1)
+    keep = np.setdiff1d(np.arange(p.pool_slots), q.idx[[0, 2]])
+    assert np.array_equal(pool3[keep].view(np.uint32), before[keep].view(np.uint32))
+    # duplicates are rejected
+    q.idx = np.array([1, 2, 1, 3], dtype=np.int32)
+    try:
+        o.run(before.copy(), q.idx, q.x, q.B, q.C, q.dt, q.A, q.dt_bias, q.D)
+    except ValueError as e:
+        assert "duplicate" in str(e)
+    else:
+        raise AssertionError("duplicate slot ids accepted")
+
+
+def pin_dt_zero(o):
+    p = _small(H=3, P=8, N=16, bs=3, slots=6, seed=51, softplus=False)
+    p.dt[:] = 0
+    before = p.pool.copy()
+    pool, r = _run(o, p, dt_bias=np.zeros(p.nheads, dtype=np.float32))
+    assert np.array_equal(pool.view(np.uint32), before.view(np.uint32))
+    for b in range(p.batch):
+        for h in range(p.nheads):
+            S0 = before[p.idx[b], h].astype(np.float64)
+            Cv = si.bf16_values(p.C[b, 0]).astype(np.float64)
+            x = si.bf16_values(p.x[b, h]).astype(np.float64)
+            want = S0 @ Cv + np.float64(p.D[h]) * x
+            tau = np.abs(S0 * Cv).sum(1) + np.abs(np.float64(p.D[h]) * x)
+            assert np.all(np.abs(r["y"][b, h] - want) <= 1e-13 * tau)
+
+
+def pin_A_very_negative(o):
+    p = _small(H=3, P=8, N=16, bs=3, slots=6, seed=61)
+    p.dt[:] = 0  # delta = softplus(dt_bias) in [1e-3, 0.1], so A*delta <= -1e6
+    A = np.full(p.nheads, -1e9, dtype=np.float32)
+    pool, r = _run(o, p, A=A)
+    delta = np.logaddexp(0.0, p.dt_bias.astype(np.float64))
+    for b in range(p.batch):
+        for h in range(p.nheads):
+            x = si.bf16_values(p.x[b, h]).astype(np.float64)
+            Bv = si.bf16_values(p.B[b, 0]).astype(np.float64)
+            Cv = si.bf16_values(p.C[b, 0]).astype(np.float64)
+            want_state = np.outer(delta[h] * x, Bv)
+            assert np.array_equal(pool[p.idx[b], h], want_state.astype(np.float32))
+            want_y = x * (delta[h] * (Bv @ Cv) + np.float64(p.D[h]))
+            scale = np.abs(x) * (delta[h] * np.abs(Bv) @ np.abs(Cv) + abs(float(p.D[h])))
+            assert np.all(np.abs(r["y"][b, h] - want_y) <= 1e-13 * scale + 1e-300)
+
+
+def pin_B_zero(o):
+    p = _small(H=3, P=8, N=16, bs=3, slots=6, seed=71)
+    o_ = p.nheads * p.headdim
+    p.xbc[:, o_ : o_ + p.dstate] = 0
+    before = p.pool.copy()
+    pool, _ = _run(o, p)
+    delta = _np_delta(p.dt, p.dt_bias[None, :], True)
+    for b in range(p.batch):
+        for h in range(p.nheads):
+            a = np.exp(np.float64(p.A[h]) * delta[b, h])
+            want = (a * before[p.idx[b], h].astype(np.float64)).astype(np.float32)
+            assert np.array_equal(pool[p.idx[b], h], want)
+
+
+def pin_C_zero(o):
+    import torch
+
+    p = _small(H=3, P=8, N=16, bs=3, slots=6, seed=81)
+    o_ = p.nheads * p.headdim + p.dstate
+    p.xbc[:, o_ : o_ + p.dstate] = 0
+    _, r = _run(o, p)
+    dx = torch.from_numpy(p.D[None, :, None].astype(np.float64) * si.bf16_values(p.x).astype(np.float64))
+    want = dx.float().to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(r["out"], want)
+
+
+def pin_groups(o):
+    H, G, P, N, bs = 4, 2, 4, 8, 2
+    p = si.make_problem(H, P, N, G, bs, 4, 91)
+    before = p.pool.copy()
+    pool, r = _run(o, p)
+    delta = _np_delta(p.dt, p.dt_bias[None, :], True)
+    for b in range(bs):
+        for h in range(H):
+            g = h // (H // G)
+            a = np.exp(np.float64(p.A[h]) * delta[b, h])
+            x = si.bf16_values(p.x[b, h]).astype(np.float64)
+            Bv = si.bf16_values(p.B[b, g]).astype(np.float64)
+            Cv = si.bf16_values(p.C[b, g]).astype(np.float64)
+            S = a * before[p.idx[b], h].astype(np.float64) + delta[b, h] * np.outer(x, Bv)
+            assert np.allclose(r["state"][b, h], S, rtol=1e-14, atol=1e-14), (b, h)
+            want = S @ Cv + np.float64(p.D[h]) * x
+            assert np.allclose(r["y"][b, h], want, rtol=1e-12, atol=1e-12), (b, h)
+
+
+def _scan_inputs(K, seed, H=2, P=4, N=8, bs=2, slots=5):
+    base = si.make_problem(H, P, N, 1, bs, slots, seed)
+    steps = [si.make_problem(H, P, N, 1, bs, slots, seed * 100 + t + 1, idx=base.idx) for t in range(K)]
+    x = np.stack([s.x for s in steps])
+    B = np.stack([s.B for s in steps])
+    C = np.stack([s.C for s in steps])
+    dt = np.stack([s.dt for s in steps])
+    return base, x, B, C, dt
+
+
+def pin_kstep(o):
+    for K in (1, 2, 7, 32):
+        base, x, B, C, dt = _scan_inputs(K, seed=100 + K)
+        H, P, N, bs = base.nheads, base.headdim, base.dstate, base.batch
+        S0 = base.pool.copy()
+        pool_scan = S0.copy()
+        r = o.run(pool_scan, base.idx, x, B, C, dt, base.A, base.dt_bias, base.D)
+        delta = np.logaddexp(0.0, si.bf16_values(dt).astype(np.float64) + base.dt_bias[None, None, :])
+        for b in range(bs):
+            for h in range(H):
+                Ah = np.float64(base.A[h])
+                tot = delta[:, b, h].sum()
+                want = np.exp(Ah * tot) * S0[base.idx[b], h].astype(np.float64)
+                for t in range(K):
+                    later = delta[t + 1 :, b, h].sum()
+                    xt = si.bf16_values(x[t, b, h]).astype(np.float64)
+                    Bt = si.bf16_values(B[t, b, 0]).astype(np.float64)
+                    want = want + np.exp(Ah * later) * delta[t, b, h] * np.outer(xt, Bt)
+                got = r["state"][b, h]
+                assert np.allclose(got, want, rtol=1e-12, atol=1e-12), (K, b, h, np.abs(got - want).max())
+                # y_t uses the state after token t (closed form at t)
+                t = K - 1
+                Ct = si.bf16_values(C[t, b, 0]).astype(np.float64)
+                xt = si.bf16_values(x[t, b, h]).astype(np.float64)
+                yw = want @ Ct + np.float64(base.D[h]) * xt
+                assert np.allclose(r["y"][t, b, h], yw, rtol=1e-11, atol=1e-11)
+        # K single steps with fp32 storage in between stay within rounding of the scan
+        pool_steps = S0.copy()
+        for t in range(K):
+            o.run(pool_steps, base.idx, x[t], B[t], C[t], dt[t], base.A, base.dt_bias, base.D)
+        ref = r["state"]
+        got = pool_steps[base.idx].astype(np.float64)
+        assert np.all(np.abs(got - ref) <= K * 2.0 ** -23 * (1.0 + np.abs(ref)))
+
+
+def pin_brute_force(o):
+    rng = _rng(7)
+    cases = [dict(H=2, P=64, N=128, G=1, bs=4, slots=8, seed=0)]  # the tiny workload itself
+    for i in range(8):
+        H = int(rng.integers(1, 5))
+        G = int(rng.choice([g for g in range(1, H + 1) if H % g == 0]))
+        cases.append(dict(H=H, P=int(rng.integers(1, 9)), N=int(rng.integers(1, 17)), G=G,
+                          bs=int(rng.integers(1, 5)), slots=int(rng.integers(5, 9)), seed=200 + i))
+    for c in cases:
+        for softplus in (True, False):
+            p = si.make_problem(c["H"], c["P"], c["N"], c["G"], c["bs"], c["slots"], c["seed"],
+                                dt_softplus=softplus)
+            before = p.pool.copy()
+            pool, r = _run(o, p)
+            new, y, out = brute.step(before.tolist(), p.idx.tolist(), p.x.tolist(), p.B.tolist(),
+                                     p.C.tolist(), p.dt.tolist(), p.A.tolist(), p.dt_bias.tolist(),
+                                     p.D.tolist(), softplus)
+            new = np.array(new)
+            S = new[p.idx]
+            assert np.all(np.abs(r["state"] - S) <= 1e-13 * (1 + np.abs(S))), c
+            assert np.array_equal(pool, new.astype(np.float32)), c
+            y = np.array(y)
+            assert np.all(np.abs(r["y"] - y) <= 1e-13 * (r["tau"] + 1e-300)), c
+            out = np.array(out, dtype=np.uint16)
+            agree = out == r["out"]
+            if not agree.all():
+                # only where the two sums' last-bit difference crosses a rounding boundary
+                dist = np.abs(out[~agree].astype(np.int64) - r["out"][~agree].astype(np.int64))
+                assert np.all(dist == 1) and np.all(r["y"][~agree] != y[~agree]), c
+
+
+PINS = [
+    pin_softplus_closed_forms,
+    pin_bf16_rounding,
+    pin_rank1_update,
+    pin_output_gemv,
+    pin_gather,
+    pin_dt_zero,
+    pin_A_very_negative,
+    pin_B_zero,
+    pin_C_zero,
+    pin_groups,
+    pin_kstep,
+    pin_brute_force,
+]

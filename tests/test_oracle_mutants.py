@@ -1,0 +1,80 @@
+"""Planted mistakes in the oracle must each fail at least one pin.
+
+Each mutant is a copy of oracle/ssu_ref.c with one plausible mistake (a dropped
+term, a wrong sign, a wrong index or operand, a wrong rounding), built with gcc
+into a temporary library and run through every pin on the CPU. Every mistake
+keeps all memory accesses in bounds. A mutant that no pin notices would mean
+the pins leave that part of the oracle unchecked.
+"""
+import os
+
+import pytest
+
+import oracle
+from oracle.build import SRC, build_oracle
+
+from .oracle_pins import PINS
+
+# (name, text in ssu_ref.c, replacement)
+MUTANTS = [
+    ("update_sign", "Sp[n] * a + (delta * xp)", "Sp[n] * a - (delta * xp)"),
+    ("drop_decay", "Sp[n] = Sp[n] * a + ", "Sp[n] = Sp[n] + "),
+    ("drop_input_term", "Sp[n] = Sp[n] * a + (delta * xp) * ref_bf16_value(Br[n * g->B_n]);",
+     "Sp[n] = Sp[n] * a;"),
+    ("drop_delta_in_input", "(delta * xp) * ref_bf16_value(Br", "(xp) * ref_bf16_value(Br"),
+    ("B_for_C_in_update", "ref_bf16_value(Br[n * g->B_n])", "ref_bf16_value(Cr[n * g->C_n])"),
+    ("C_for_B_in_output", "Sp[n] * ref_bf16_value(Cr[n * g->C_n])", "Sp[n] * ref_bf16_value(Br[n * g->B_n])"),
+    ("drop_skip_D", "    y += Dv * xp;\n", "\n"),
+    ("skip_uses_B", "y += Dv * xp;", "y += Dv * ref_bf16_value(Br[p % N * g->B_n]);"),
+    ("decay_sign", "*a = exp(A * d);", "*a = exp(-A * d);"),
+    ("decay_uses_u", "*a = exp(A * d);", "*a = exp(A * u);"),
+    ("drop_bias", "double u = dt + dt_bias;", "double u = dt;"),
+    ("softplus_sign", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
+    ("softplus_naive", "return fmax(u, 0.0) + log1p(exp(-fabs(u)));", "return log(1.0 + exp(u));"),
+    ("softplus_ignored", "double d = softplus ? ssu_ref_softplus(u) : u;", "double d = u;"),
+    ("group_map", "(((int64_t)h * G) / H)", "(h % G)"),
+    ("slot_is_request", "g->state + slot * g->st_slot", "g->state + (int64_t)b * g->st_slot"),
+    ("head_ignored", "+ (int64_t)h * g->st_head;", ";"),
+    ("x_row_index", "xr[p * g->x_p]", "xr[(P - 1 - p) * g->x_p]"),
+    ("output_old_state", "const double term = Sp[n] * ref_bf16_value",
+     "const double term = (double)pool[(int64_t)p * g->st_row + n] * ref_bf16_value"),
+    ("no_write_back", "pool[(int64_t)p * g->st_row + n] = (float)v;", "(void)v;"),
+    ("bf16_truncate", "w += 0x7FFFu + lsb;", "w += 0u * lsb;"),
+    ("bf16_ties_away", "w += 0x7FFFu + lsb;", "w += 0x8000u + 0u * lsb;"),
+    ("tau_signed", "tau += fabs(term);", "tau += term;"),
+    ("no_carry_between_tokens", "for (int32_t t = 0; t < K; ++t) {",
+     "for (int32_t t = 0; t < K; ++t) {\n"
+     "                for (int32_t q = 0; q < P * N; ++q) S[q] = (double)pool[(q / N) * g->st_row + q % N];"),
+    ("skip_check_off", "if (slot < 0 || slot >= g->pool_slots)\n                continue;",
+     "if (slot < 0 || slot >= g->pool_slots)\n                slot = 0;"),
+    ("dups_allowed", "if (seen[s]) {", "if (0 && seen[s]) {"),
+]
+
+
+def _caught(o):
+    names = []
+    for pin in PINS:
+        try:
+            pin(o)
+        except Exception:  # noqa: BLE001 - any failure counts as caught
+            names.append(pin.__name__)
+    return names
+
+
+@pytest.mark.parametrize("name,old,new", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(tmp_path, name, old, new):
+    src = open(SRC).read()
+    if name == "skip_check_off":
+        # 'slot' is const in the original; the mutant needs a mutable copy
+        src = src.replace("const int64_t slot = g->idx[b];", "int64_t slot = g->idx[b];")
+        # keep the mutant in bounds: slot 0 exists whenever pool_slots > 0
+    assert src.count(old) >= 1, f"mutation anchor not found: {old!r}"
+    msrc = tmp_path / f"ssu_ref_{name}.c"
+    msrc.write_text(src.replace(old, new, 1))
+    lib = build_oracle(src=str(msrc), out=str(tmp_path / f"libssu_ref_{name}.so"),
+                       extra_flags=["-Wno-unused-variable", "-Wno-unused-parameter",
+                                    "-Wno-unused-but-set-variable"], quiet=True)
+    caught = _caught(oracle.Oracle(lib))
+    print(f"{name}: caught by {caught}")
+    assert caught, f"mutant {name} passes every pin"
+    os.remove(lib)
