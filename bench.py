@@ -1,0 +1,460 @@
+#!/usr/bin/env python3
+"""Benchmark of libssu's decode-step selective_state_update on one MI355X.
+
+Method (sglang PR #41223, "[Perf] Mamba2 selective_state_update up to 2x
+faster on B200 via 8x1 launch config for dstate 128", section "Kernel
+measurement"): many calls captured in one graph, each call reading a different
+set of state slots; the sets are disjoint and together hold at least three
+times the last-level cache, so every call streams its state from HBM, as in
+real decode where each layer's state is touched once per step. Here the graph
+is a HIP graph and the last-level cache is MI355X's 256 MB Infinity Cache, so
+the sets total >= 768 MiB.
+
+A "step" is one ssu_update call over one batch. The default workload is the
+headline one: H=16, P=64, N=128, batch 512, fp32 state, bf16 x/B/C as strided
+views of one tensor, per-head dt/A/D/dt_bias broadcasts.
+
+Output: one JSON line (see the keys below). `value` is HBM GB/s computed from
+the algorithmic bytes of a call; the roofline object prices the kernel against
+the 8 TB/s HBM3E peak; cpu_baseline times the fp64 CPU oracle on the host on a
+bounded sample of the same workload.
+
+    python bench.py [--steps K] [--warmup W] [--config 1|2|3] [--tile T]
+    python bench.py --sweep [--heads 16] [--out FILE]   per-point GB/s (no JSON line)
+    python bench.py --counters                          short eager run for rocprofv3 --pmc
+    python bench.py --summarize-counters DIR --write-profile NAME
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import statistics
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+import ssu_inputs as si  # noqa: E402
+
+HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
+LLC_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
+ROTATION_BYTES = 3 * LLC_BYTES  # >= 3x the last-level cache
+KERNEL_SRC = os.path.join(ROOT, "selective_state_update_amd", "csrc", "ssu.hip")
+COUNTER_PROFILE = os.path.join(ROOT, "profiles", "ssu_decode_h16_bs512_counters.md")
+
+WORKLOADS = {
+    1: dict(H=16, P=64, N=128, G=1, batch=8),
+    2: dict(H=16, P=64, N=128, G=1, batch=128),
+    3: dict(H=16, P=64, N=128, G=1, batch=512),
+}
+
+
+def state_bytes(H, P, N, batch):
+    """fp32 state read + written once per call."""
+    return 8 * batch * H * P * N
+
+
+def algorithmic_bytes(H, P, N, G, batch):
+    """Bytes one call must move: state read+write (fp32), x (bf16), B and C
+    (bf16, once per request and group), dt (bf16 per request and head), idx
+    (int32), A, D, dt_bias (fp32 per head) and out (bf16)."""
+    return (8 * batch * H * P * N + 2 * batch * H * P + 4 * batch * G * N + 2 * batch * H
+            + 4 * batch + 12 * H + 2 * batch * H * P)
+
+
+def source_digest() -> str:
+    with open(KERNEL_SRC, "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+# --------------------------------------------------------------------------- #
+class Rotation:
+    """K disjoint slot sets of `batch` requests over a pool of K*batch slots,
+    with per-set x/B/C, dt and out buffers, all resident in HBM."""
+
+    def __init__(self, H, P, N, G, batch, seed, device="cuda", min_bytes=ROTATION_BYTES):
+        import torch
+
+        self.H, self.P, self.N, self.G, self.batch = H, P, N, G, batch
+        per_call = batch * H * P * N * 4
+        self.K, sets = si.rotation_sets(per_call, batch, min_bytes, seed)
+        self.pool = torch.empty((self.K * batch, H, P, N), dtype=torch.float32, device=device)
+        si.draw_pool_on_device(self.pool, seed)
+        self.sets = []
+        for k in range(self.K):
+            p = si.make_problem(H, P, N, G, batch, self.K * batch, seed * 1000 + k, host_pool=False,
+                                idx=sets[k])
+            xbc = torch.from_numpy(p.xbc.view(np.int16)).view(torch.bfloat16).to(device)
+            row = xbc.stride(0)
+            self.sets.append(dict(
+                problem=p,
+                idx=torch.from_numpy(p.idx).to(device),
+                x=xbc.as_strided((batch, H, P), (row, P, 1), 0),
+                B=xbc.as_strided((batch, G, N), (row, N, 1), H * P),
+                C=xbc.as_strided((batch, G, N), (row, N, 1), H * P + G * N),
+                xbc=xbc,
+                dt=torch.from_numpy(p.dt.view(np.int16)).view(torch.bfloat16).to(device),
+                out=torch.empty((batch, H, P), dtype=torch.bfloat16, device=device),
+            ))
+        p0 = self.sets[0]["problem"]
+        self.A = torch.from_numpy(p0.A).to(device)
+        self.D = torch.from_numpy(p0.D).to(device)
+        self.dt_bias = torch.from_numpy(p0.dt_bias).to(device)
+
+    def args(self, handle):
+        """Prepared ssu_args per set (marshalled once, outside the timed region)."""
+        out = []
+        for s in self.sets:
+            out.append(handle.make_args(self.pool, s["idx"], s["x"], s["B"], s["C"], s["dt"], self.A,
+                                        self.D, self.dt_bias, s["out"]))
+        return out
+
+
+def capture(handle, args, first, count):
+    """A HIP graph of `count` calls; call i uses set (first + i) mod K."""
+    import torch
+
+    g = torch.cuda.CUDAGraph()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        handle.launch(args[first % len(args)])  # warm the launch path outside capture
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        for i in range(count):
+            handle.launch(args[(first + i) % len(args)])
+    return g
+
+
+def time_graph(g, replays):
+    """Seconds for `replays` back-to-back replays, bracketed by events on the
+    stream the kernels run on (torch's current stream)."""
+    import torch
+
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record(st)
+    for _ in range(replays):
+        g.replay()
+    e1.record(st)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
+def cpu_oracle_baseline(H, P, N, G, batch, seed, budget_s=20.0):
+    """The CPU oracle (fp64, OpenMP over (request, head)) on host cores, on a
+    bounded sample: whole calls of the same workload, repeated until about
+    `budget_s` of CPU time has passed (at least 2 calls, at most 5)."""
+    import oracle
+
+    ref = oracle.get()
+    threads = len(os.sched_getaffinity(0))
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    if env_threads and env_threads.isdigit():
+        threads = min(threads, int(env_threads))
+    slots = batch  # exactly the slots one call touches
+    p = si.make_problem(H, P, N, G, batch, slots, seed)
+    times = []
+    t_start = time.perf_counter()
+    while len(times) < 5 and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
+        pool = p.pool.copy()
+        t0 = time.perf_counter()
+        ref.run(pool, p.idx, p.x, p.B, p.C, p.dt, p.A, p.dt_bias, p.D, True, want_state=False,
+                want_y=False, nthreads=threads)
+        times.append(time.perf_counter() - t0)
+    med = statistics.median(times)
+    gbs = algorithmic_bytes(H, P, N, G, batch) / med / 1e9
+    cpu_model = ""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                cpu_model = line.split(":", 1)[1].strip()
+                break
+    except OSError:
+        pass
+    return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
+            "sample": f"{len(times)} whole calls of H{H} P{P} N{N} batch {batch} (median "
+                      f"{med * 1e3:.1f} ms/call, fp64 C oracle, OpenMP {threads} threads, {cpu_model})",
+            "us_per_call": round(med * 1e6, 1)}
+
+
+def counter_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, if it
+    was taken on the current kernel source (else None)."""
+    if not os.path.exists(COUNTER_PROFILE):
+        return None
+    fields = {}
+    for line in open(COUNTER_PROFILE):
+        if ":" in line and line.startswith("- "):
+            k, v = line[2:].split(":", 1)
+            fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256_16") != source_digest():
+        return None
+    try:
+        return int(float(fields["traffic_bytes_per_launch"]))
+    except (KeyError, ValueError):
+        return None
+
+
+# --------------------------------------------------------------------------- #
+def run_bench(a):
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    w = WORKLOADS[a.config]
+    H, P, N, G, bs = w["H"], w["P"], w["N"], w["G"], w["batch"]
+    nbytes = algorithmic_bytes(H, P, N, G, bs)
+    torch.cuda.init()
+    rot = Rotation(H, P, N, G, bs, seed=a.config)
+    h = ssu.Handle(H, P, N, G, True, a.tile)
+    tile = h.selected_tile(bs)
+    tdesc = ssu.tiles()[tile]
+    args = rot.args(h)
+    calls = max(20, rot.K)
+    g = capture(h, args, 0, calls)
+    K_steps = a.steps
+    full, tail = divmod(K_steps, calls)
+    g_tail = capture(h, args, 0, tail) if tail else None
+    torch.cuda.synchronize()
+    print(f"# workload H{H} P{P} N{N} G{G} bs{bs}: {nbytes} B/call, K={rot.K} sets, "
+          f"{calls} calls/graph, tile {tdesc['name']}", file=sys.stderr, flush=True)
+
+    # warmup: at least W calls
+    for _ in range(max(1, -(-a.warmup // calls))):
+        g.replay()
+    torch.cuda.synchronize()
+
+    # timed region: exactly K steps
+    st = torch.cuda.current_stream()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    e0.record(st)
+    for _ in range(full):
+        g.replay()
+    if g_tail is not None:
+        g_tail.replay()
+    e1.record(st)
+    e1.synchronize()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    elapsed = e0.elapsed_time(e1) * 1e-3
+    per_call = elapsed / K_steps
+    gbs = nbytes / per_call / 1e9
+
+    # the pages' statistic: median of 5 x (20 replays of the graph)
+    reps = [time_graph(g, 20) / (20 * calls) for _ in range(5)]
+    med = statistics.median(reps)
+
+    cpu = None
+    if not a.no_cpu_baseline:
+        cpu = cpu_oracle_baseline(H, P, N, G, bs, seed=a.config, budget_s=a.cpu_budget)
+
+    traffic = counter_traffic()
+    line = {
+        "metric": "selective_state_update HBM GB/s (% of peak) + µs/call, H16 P64 N128 bs512",
+        "value": round(gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": K_steps,
+        "warmup": a.warmup,
+        "ms_per_step": round(per_call * 1e3, 6),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f32",
+        "data": "synthetic",
+        "config": {
+            "workload": f"selective_state_update decode step H{H} P{P} N{N} G{G} batch {bs}, fp32 state, "
+                        f"bf16 x/B/C packed, per-head dt/A/D/dt_bias, {rot.K} disjoint slot sets "
+                        f"({rot.K * bs * H * P * N * 4 >> 20} MiB) rotated in a HIP graph of {calls} calls",
+            "heads": H, "headdim": P, "dstate": N, "ngroups": G, "batch": bs,
+            "tile": tdesc["name"],
+        },
+        "us_per_call": round(per_call * 1e6, 3),
+        "pct_of_peak": round(100.0 * gbs / HBM_PEAK_GBS, 2),
+        "median5_us_per_call": round(med * 1e6, 3),
+        "bytes_per_call": nbytes,
+        "wall_s": round(wall, 4),
+        "roofline": {
+            "bound": "hbm",
+            "achieved": round(gbs, 2),
+            "peak": HBM_PEAK_GBS,
+            "unit": "GB/s",
+            "frac": round(gbs / HBM_PEAK_GBS, 4),
+            "traffic": traffic,
+        },
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+def run_sweep(a):
+    """GB/s and us/call per (heads, batch) point of the bitwise-sweep grid,
+    same rotation method; one text line per point."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    heads = [int(x) for x in a.heads.split(",")] if a.heads else [8, 16, 32, 64, 128]
+    batches = sorted({bs for (_, bs) in si.sweep_points()}) if not a.batches else \
+        [int(x) for x in a.batches.split(",")]
+    out = open(a.out, "w") if a.out else sys.stdout
+    print("heads batch tile K calls us_per_call GBps pct_peak", file=out, flush=True)
+    for H in heads:
+        for bs in batches:
+            rot = Rotation(H, 64, 128, 1, bs, seed=si.sweep_seed(H, bs))
+            h = ssu.Handle(H, 64, 128, 1, True, a.tile)
+            args = rot.args(h)
+            calls = max(20, rot.K)
+            g = capture(h, args, 0, calls)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = [time_graph(g, 5) / (5 * calls) for _ in range(3)]
+            us = statistics.median(reps) * 1e6
+            gbs = algorithmic_bytes(H, 64, 128, 1, bs) / (us * 1e-6) / 1e9
+            print(f"{H} {bs} {ssu.tiles()[h.selected_tile(bs)]['name']} {rot.K} {calls} {us:.3f} "
+                  f"{gbs:.1f} {100 * gbs / HBM_PEAK_GBS:.2f}", file=out, flush=True)
+            del g, rot, args
+            torch.cuda.empty_cache()
+
+
+def run_counters(a):
+    """Eager calls for a rocprofv3 --pmc pass: `a.steps` headline calls rotating
+    over the slot sets, then a plain device copy of a known size (256 MiB read
+    + 256 MiB written) to scale the counters."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    w = WORKLOADS[a.config]
+    H, P, N, G, bs = w["H"], w["P"], w["N"], w["G"], w["batch"]
+    rot = Rotation(H, P, N, G, bs, seed=a.config)
+    h = ssu.Handle(H, P, N, G, True, a.tile)
+    args = rot.args(h)
+    for i in range(a.steps):
+        h.launch(args[i % len(args)])
+    torch.cuda.synchronize()
+    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    bufs = [torch.empty_like(src) for _ in range(3)]  # evict src from the cache between copies
+    for i in range(4):
+        for b in bufs:
+            b.fill_(float(i))
+        torch.mul(src, 2.0, out=dst)  # one elementwise kernel: reads src once, writes dst once
+    torch.cuda.synchronize()
+    print(f"# counters pass: {a.steps} ssu calls, 4 copies of {src.numel() * 4} bytes", flush=True)
+
+
+def summarize_counters(a):
+    """Read rocprofv3 --pmc CSV output (FETCH_SIZE and WRITE_SIZE runs) and write
+    the counter summary that the JSON line's roofline.traffic comes from."""
+    import csv
+    import glob
+
+    def load(dirpath, counter):
+        rows = []
+        for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+            with open(f) as fh:
+                for r in csv.DictReader(fh):
+                    if r.get("Counter_Name") == counter:
+                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+        return rows
+
+    fetch_dir, write_dir = a.summarize_counters.split(",")
+    fetch = load(fetch_dir, "FETCH_SIZE")
+    write = load(write_dir, "WRITE_SIZE")
+    if not fetch or not write:
+        raise SystemExit("no counter rows found")
+
+    def split(rows):
+        ssu_v = [v for k, v in rows if "ssu_decode_kernel" in k]
+        copy_v = [v for k, v in rows if "MulFunctor" in k]
+        return ssu_v, copy_v
+
+    fs, fc = split(fetch)
+    ws, wc = split(write)
+    copy_bytes = 64 * 1024 * 1024 * 4
+    # counters are in KiB per dispatch; scale by what a copy of known size reads
+    f_scale = copy_bytes / (statistics.median(fc) * 1024) if fc else 1.0
+    w_scale = copy_bytes / (statistics.median(wc) * 1024) if wc else 1.0
+    w = WORKLOADS[a.config]
+    nbytes = algorithmic_bytes(w["H"], w["P"], w["N"], w["G"], w["batch"])
+    f_b = statistics.median(fs) * 1024 * f_scale
+    w_b = statistics.median(ws) * 1024 * w_scale
+    text = f"""# rocprofv3 HBM counters: ssu_decode_kernel, H{w['H']} P{w['P']} N{w['N']} batch {w['batch']}
+
+Commands (run from the repository root on one MI355X):
+
+    rocprofv3 --pmc FETCH_SIZE -d {a.fetch_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
+    rocprofv3 --pmc WRITE_SIZE -d {a.write_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
+    python3 bench.py --summarize-counters <fetch_dir>,<write_dir> --write-profile
+
+Counters are KiB per dispatch. Each is scaled by the ratio (known bytes / counter)
+measured on a plain device copy of 268435456 bytes read + 268435456 written in the
+same run.
+
+- kernel_source_sha256_16: `{source_digest()}`
+- ssu_dispatches: {len(fs)}
+- fetch_kib_median: {statistics.median(fs):.1f}
+- write_kib_median: {statistics.median(ws):.1f}
+- copy_fetch_kib_median: {statistics.median(fc) if fc else float('nan'):.1f}
+- copy_write_kib_median: {statistics.median(wc) if wc else float('nan'):.1f}
+- fetch_scale: {f_scale:.4f}
+- write_scale: {w_scale:.4f}
+- fetch_bytes_per_launch: {f_b:.0f}
+- write_bytes_per_launch: {w_b:.0f}
+- traffic_bytes_per_launch: {f_b + w_b:.0f}
+- algorithmic_bytes_per_launch: {nbytes}
+- traffic_over_algorithmic: {(f_b + w_b) / nbytes:.4f}
+"""
+    if a.write_profile:
+        with open(COUNTER_PROFILE, "w") as f:
+            f.write(text)
+    print(text)
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=2000)
+    ap.add_argument("--warmup", type=int, default=100)
+    ap.add_argument("--config", type=int, default=3, choices=sorted(WORKLOADS))
+    ap.add_argument("--tile", type=int, default=-1)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=20.0)
+    ap.add_argument("--sweep", action="store_true")
+    ap.add_argument("--heads", default="")
+    ap.add_argument("--batches", default="")
+    ap.add_argument("--out", default="")
+    ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--summarize-counters", default="")
+    ap.add_argument("--write-profile", action="store_true")
+    ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
+    ap.add_argument("--write-dir-name", default="gpurun_out/pmc_write")
+    a = ap.parse_args()
+    if a.gpus != 1:
+        print("bench.py measures one GPU: selective_state_update has no cross-GPU exchange, and this "
+              "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+    if a.summarize_counters:
+        summarize_counters(a)
+    elif a.counters:
+        run_counters(a)
+    elif a.sweep:
+        run_sweep(a)
+    else:
+        run_bench(a)
+
+
+if __name__ == "__main__":
+    main()

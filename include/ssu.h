@@ -1,0 +1,185 @@
+/*
+ * ssu.h -- libssu: the Mamba2 decode-step selective_state_update on AMD
+ * Instinct MI355X (gfx950), as a C ABI.
+ *
+ * The operation (one decode token for a batch of requests; sglang PR #41223,
+ * "[Perf] Mamba2 selective_state_update up to 2x faster on B200 via 8x1 launch
+ * config for dstate 128", sections "Summary" and "Kernel measurement"): for
+ * every request b and head h, with g = h / (H/G) the head's group,
+ *
+ *     slot    = idx[b]
+ *     delta   = softplus(dt[b,h] + dt_bias[h])        (or dt + dt_bias when
+ *                                                      dt_softplus == 0)
+ *     a       = exp(A[h] * delta)
+ *     S[p,n]  = state[slot,h,p,n] * a + delta * x[b,h,p] * B[b,g,n]
+ *     state[slot,h,p,n] = S[p,n]                       (in place, fp32)
+ *     out[b,h,p] = bf16( sum_n S[p,n] * C[b,g,n] + D[h] * x[b,h,p] )
+ *
+ * The page states the problem this way: an fp32 state pool [pool, H, P, N]
+ * addressed through random state_batch_indices, x/B/C as strided views of one
+ * bf16 tensor, and dt, A, D, dt_bias as stride-0 broadcasts per head. The
+ * arguments below mirror that statement: every operand is a strided view.
+ *
+ * Numerics: fp32 arithmetic throughout; the sum over n is taken in one fixed
+ * order that does not depend on the launch configuration (tile), so every tile
+ * gives bitwise-identical state and out, and repeated runs are bitwise
+ * reproducible. out is rounded to bf16 to nearest, ties to even.
+ *
+ * Ownership and threading: the caller owns every device buffer and the stream.
+ * ssu_update is asynchronous on the stream: buffers must stay alive until the
+ * stream's work completes. The library keeps no pointer after a call returns.
+ * A handle is immutable after ssu_create, so calls on one handle from several
+ * threads or streams are safe. ssu_update allocates nothing, never
+ * synchronises and never reads device memory, so it may be captured into a
+ * HIP graph.
+ *
+ * Errors: every function reports through ssu_status; nothing throws across the
+ * ABI. ssu_last_error() gives a one-line description of the calling thread's
+ * most recent failure.
+ */
+#ifndef SSU_H
+#define SSU_H
+
+#include <stdint.h>
+
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define SSU_ABI_VERSION 1
+
+typedef enum ssu_status {
+    SSU_OK = 0,
+    SSU_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, wrong dtype tag, bad config */
+    SSU_ERR_UNSUPPORTED = 2,      /* shape or layout this build does not run (see ssu_update) */
+    SSU_ERR_MISALIGNED = 3,       /* state or B/C address not aligned for vector access */
+    SSU_ERR_HIP = 4,              /* a HIP runtime call failed (launch, device query, copy) */
+    SSU_ERR_NO_MEMORY = 5,        /* host allocation failed */
+    SSU_ERR_BAD_INDEX = 6         /* ssu_check_indices: duplicate in-range slot ids */
+} ssu_status;
+
+typedef enum ssu_dtype {
+    SSU_F32 = 0,
+    SSU_BF16 = 1,
+    SSU_I32 = 2,
+    SSU_I64 = 3
+} ssu_dtype;
+
+/* Problem shape and options, fixed for the life of a handle. */
+typedef struct ssu_config {
+    int32_t nheads;      /* H >= 1 */
+    int32_t headdim;     /* P: a multiple of 16, 16 <= P <= 256 */
+    int32_t dstate;      /* N: 16, 32, 64, 128 or 256 */
+    int32_t ngroups;     /* G >= 1, divides H; head h uses group h / (H/G) */
+    int32_t dt_softplus; /* 1: delta = softplus(dt + dt_bias); 0: delta = dt + dt_bias */
+    int32_t tile;        /* -1: launch configuration from the built-in table;
+                            >= 0: always use tile #tile (for sweeps; see ssu_tile_info).
+                            The environment variable SSU_TILE, read by ssu_create,
+                            overrides a -1 here the same way. */
+    int32_t device;      /* HIP device ordinal that launches run on; -1: the
+                            device current at the first launch */
+    int32_t reserved;    /* must be 0 */
+} ssu_config;
+
+/* A strided view of device memory. Strides are in elements, outermost first;
+ * unused trailing entries are ignored. */
+typedef struct ssu_view {
+    const void *ptr;
+    int32_t dtype; /* ssu_dtype */
+    int32_t reserved;
+    int64_t stride[4];
+} ssu_view;
+
+/* One call's operands. Shapes are implied by the handle's config and `batch`;
+ * the library cannot see buffer sizes, so the caller guarantees that every
+ * view covers its shape.
+ *
+ *   state   [pool_slots, H, P, N] f32, read and written. stride[3] must be 1;
+ *           the pointer and stride[0..2] must be 16-byte multiples.
+ *   idx     [batch] i32 or i64 (state_batch_indices). stride[0] must be 1.
+ *   x       [batch, H, P] bf16. stride[2] must be 1.
+ *   B, C    [batch, G, N] bf16. stride[2] must be 1; the pointer and
+ *           stride[0..1] must be 8-byte multiples.
+ *   dt      [batch, H, P] bf16, one value per (request, head): stride[2] == 0.
+ *   dt_bias [H, P] f32, stride[1] == 0. ptr may be NULL (no bias).
+ *   A       [H, P, N] f32, stride[1] == stride[2] == 0.
+ *   D       [H, P] f32, stride[1] == 0. ptr may be NULL (no skip term).
+ *   out     [batch, H, P] bf16, written. stride[2] must be 1.
+ *
+ * x, B and C may be views into one packed tensor. out must not overlap any
+ * input, and the state rows of distinct requests must not overlap.
+ */
+typedef struct ssu_args {
+    int32_t batch;      /* >= 0; 0 is a no-op */
+    int32_t reserved;   /* must be 0 */
+    int64_t pool_slots; /* number of slots in the state pool, >= 0 */
+    ssu_view state, idx, x, B, C, dt, dt_bias, A, D, out;
+} ssu_args;
+
+typedef struct ssu_handle ssu_handle;
+
+/* Description of one launch configuration. */
+typedef struct ssu_tile_desc {
+    int32_t dstate;          /* N this tile is compiled for */
+    int32_t rows_per_wave;   /* state rows (p) each wave64 owns */
+    int32_t waves;           /* waves per workgroup */
+    int32_t rows_per_group;  /* rows_per_wave * waves */
+    int32_t nontemporal;     /* 1: state loads/stores carry the non-temporal hint */
+    int32_t xcd_remap;       /* 1: workgroups of neighbouring heads share an XCD */
+    char name[48];
+} ssu_tile_desc;
+
+/* Validate `cfg` and create a handle. Does not touch the GPU.
+ * Errors: SSU_ERR_INVALID_ARGUMENT (null, H/P/N/G out of range, G not dividing
+ * H, tile index out of range), SSU_ERR_UNSUPPORTED (P or N this build does not
+ * compile for), SSU_ERR_NO_MEMORY. */
+ssu_status ssu_create(const ssu_config *cfg, ssu_handle **out);
+
+/* Enqueue one decode step on `stream` (NULL: the null stream).
+ *
+ * Preconditions the library cannot check without reading device memory (see
+ * ssu_check_indices for a debug check): in-range entries of idx are distinct.
+ * Entries outside [0, pool_slots) are padding: that request's state is neither
+ * read nor written and its out rows are left untouched.
+ *
+ * Errors (nothing is launched): SSU_ERR_INVALID_ARGUMENT (null handle/args,
+ * batch < 0, pool_slots < 0, null required pointer, wrong dtype tag, negative
+ * stride, non-zero reserved field), SSU_ERR_UNSUPPORTED (an inner stride that
+ * must be 1 is not, a broadcast stride that must be 0 is not),
+ * SSU_ERR_MISALIGNED (state or B/C alignment), SSU_ERR_HIP (the launch
+ * failed; the stream's state is the runtime's). batch == 0 returns SSU_OK
+ * without launching and without reading any view. */
+ssu_status ssu_update(const ssu_handle *h, const ssu_args *args, hipStream_t stream);
+
+/* Release a handle. NULL is a no-op. */
+void ssu_destroy(ssu_handle *h);
+
+/* Debug check of idx, not for hot paths and not capturable: copies idx to the
+ * host (synchronising `stream`) and returns SSU_ERR_BAD_INDEX if two in-range
+ * entries are equal. Entries outside [0, pool_slots) are padding and allowed. */
+ssu_status ssu_check_indices(const ssu_args *args, hipStream_t stream);
+
+/* The launch configuration ssu_update would use for `batch` requests
+ * (-1 if the handle's shape has none). */
+int32_t ssu_select_tile(const ssu_handle *h, int32_t batch);
+
+/* Number of compiled launch configurations, and their descriptions. */
+int32_t ssu_tile_count(void);
+ssu_status ssu_tile_info(int32_t tile, ssu_tile_desc *out);
+
+/* Static string naming a status code. */
+const char *ssu_status_string(ssu_status s);
+
+/* The calling thread's most recent error description ("" if none). */
+const char *ssu_last_error(void);
+
+/* SSU_ABI_VERSION of the built library. */
+int32_t ssu_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SSU_H */

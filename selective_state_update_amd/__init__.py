@@ -1,0 +1,308 @@
+"""selective_state_update_amd: the Mamba2 decode-step selective_state_update on
+AMD Instinct MI355X (gfx950).
+
+A thin ctypes binding over libssu (include/ssu.h). It checks tensor shapes,
+dtypes and devices, turns torch tensors into (pointer, dtype tag, strides)
+views, and calls ``ssu_update`` on the current HIP stream. All arithmetic runs
+in the library's HIP kernel; nothing here computes, and there is no fallback:
+if libssu.so is missing the import fails.
+
+The operation follows the problem statement of sglang PR #41223 ("[Perf]
+Mamba2 selective_state_update up to 2x faster on B200 via 8x1 launch config for
+dstate 128", section "Kernel measurement"): an fp32 state pool [pool, H, P, N]
+addressed by state_batch_indices, x [bs, H, P] and B/C [bs, G, N] in bf16 (they
+may be strided views of one packed tensor), and dt, A, D, dt_bias broadcast
+per head. Per request b and head h:
+
+    delta = softplus(dt + dt_bias);  a = exp(A * delta)
+    state[idx[b], h] = state[idx[b], h] * a + delta * outer(x[b, h], B[b, g])
+    out[b, h] = state[idx[b], h] @ C[b, g] + D * x[b, h]      (bf16)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import threading
+
+__all__ = [
+    "SSUError",
+    "Handle",
+    "selective_state_update",
+    "tiles",
+    "library_path",
+    "abi_version",
+]
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "libssu.so")
+
+if not os.path.exists(_LIB_PATH):
+    raise ImportError(
+        f"{_LIB_PATH} is not built; run `python -m selective_state_update_amd.build` "
+        "(there is no fallback implementation)"
+    )
+
+_lib = ctypes.CDLL(_LIB_PATH)
+
+_i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p
+
+# ssu_status
+SSU_OK = 0
+STATUS_NAMES = {
+    0: "SSU_OK",
+    1: "SSU_ERR_INVALID_ARGUMENT",
+    2: "SSU_ERR_UNSUPPORTED",
+    3: "SSU_ERR_MISALIGNED",
+    4: "SSU_ERR_HIP",
+    5: "SSU_ERR_NO_MEMORY",
+    6: "SSU_ERR_BAD_INDEX",
+}
+# ssu_dtype
+SSU_F32, SSU_BF16, SSU_I32, SSU_I64 = 0, 1, 2, 3
+
+
+class Config(ctypes.Structure):
+    _fields_ = [("nheads", _i32), ("headdim", _i32), ("dstate", _i32), ("ngroups", _i32),
+                ("dt_softplus", _i32), ("tile", _i32), ("device", _i32), ("reserved", _i32)]
+
+
+class View(ctypes.Structure):
+    _fields_ = [("ptr", _vp), ("dtype", _i32), ("reserved", _i32), ("stride", _i64 * 4)]
+
+
+class Args(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("reserved", _i32), ("pool_slots", _i64),
+                ("state", View), ("idx", View), ("x", View), ("B", View), ("C", View),
+                ("dt", View), ("dt_bias", View), ("A", View), ("D", View), ("out", View)]
+
+
+class TileDesc(ctypes.Structure):
+    _fields_ = [("dstate", _i32), ("rows_per_wave", _i32), ("waves", _i32), ("rows_per_group", _i32),
+                ("nontemporal", _i32), ("xcd_remap", _i32), ("name", ctypes.c_char * 48)]
+
+
+_lib.ssu_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_vp)]
+_lib.ssu_create.restype = _i32
+_lib.ssu_update.argtypes = [_vp, ctypes.POINTER(Args), _vp]
+_lib.ssu_update.restype = _i32
+_lib.ssu_destroy.argtypes = [_vp]
+_lib.ssu_destroy.restype = None
+_lib.ssu_check_indices.argtypes = [ctypes.POINTER(Args), _vp]
+_lib.ssu_check_indices.restype = _i32
+_lib.ssu_select_tile.argtypes = [_vp, _i32]
+_lib.ssu_select_tile.restype = _i32
+_lib.ssu_tile_count.argtypes = []
+_lib.ssu_tile_count.restype = _i32
+_lib.ssu_tile_info.argtypes = [_i32, ctypes.POINTER(TileDesc)]
+_lib.ssu_tile_info.restype = _i32
+_lib.ssu_status_string.argtypes = [_i32]
+_lib.ssu_status_string.restype = ctypes.c_char_p
+_lib.ssu_last_error.argtypes = []
+_lib.ssu_last_error.restype = ctypes.c_char_p
+_lib.ssu_abi_version.argtypes = []
+_lib.ssu_abi_version.restype = _i32
+
+
+class SSUError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        detail = _lib.ssu_last_error().decode(errors="replace")
+        super().__init__(f"{where}: {STATUS_NAMES.get(status, status)}: {detail}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def abi_version() -> int:
+    return int(_lib.ssu_abi_version())
+
+
+def tiles():
+    """All compiled launch configurations, as dicts (index = tile id)."""
+    out = []
+    for i in range(_lib.ssu_tile_count()):
+        d = TileDesc()
+        st = _lib.ssu_tile_info(i, ctypes.byref(d))
+        if st != SSU_OK:
+            raise SSUError(st, "ssu_tile_info")
+        out.append(dict(id=i, dstate=d.dstate, rows_per_wave=d.rows_per_wave, waves=d.waves,
+                        rows_per_group=d.rows_per_group, nontemporal=d.nontemporal,
+                        xcd_remap=d.xcd_remap, name=d.name.decode()))
+    return out
+
+
+def _torch():
+    import torch
+
+    return torch
+
+
+def _dtype_tag(t, allowed, name):
+    torch = _torch()
+    tags = {torch.float32: SSU_F32, torch.bfloat16: SSU_BF16, torch.int32: SSU_I32, torch.int64: SSU_I64}
+    tag = tags.get(t.dtype)
+    if tag not in allowed:
+        raise TypeError(f"{name}: dtype {t.dtype} not supported here")
+    return tag
+
+
+def _view(t, strides, tag) -> View:
+    v = View()
+    v.ptr = t.data_ptr()
+    v.dtype = tag
+    v.reserved = 0
+    for i, s in enumerate(strides):
+        v.stride[i] = int(s)
+    return v
+
+
+def _null_view() -> View:
+    v = View()
+    v.ptr = None
+    return v
+
+
+class Handle:
+    """A libssu handle for one (H, P, N, G, softplus) shape.
+
+    ``tile`` = -1 uses the library's launch table; a tile id forces one launch
+    configuration (see ``tiles()``); the SSU_TILE environment variable does the
+    same for handles created with -1.
+    """
+
+    def __init__(self, nheads: int, headdim: int, dstate: int, ngroups: int = 1,
+                 dt_softplus: bool = True, tile: int = -1, device: int = -1):
+        cfg = Config(nheads, headdim, dstate, ngroups, int(bool(dt_softplus)), tile, device, 0)
+        h = _vp()
+        st = _lib.ssu_create(ctypes.byref(cfg), ctypes.byref(h))
+        if st != SSU_OK:
+            raise SSUError(st, "ssu_create")
+        self._h = h
+        self.nheads, self.headdim, self.dstate, self.ngroups = nheads, headdim, dstate, ngroups
+        self.dt_softplus = bool(dt_softplus)
+        self.tile = tile
+
+    def __del__(self):
+        h = getattr(self, "_h", None)
+        if h is not None and h.value:
+            _lib.ssu_destroy(h)
+            self._h = None
+
+    def selected_tile(self, batch: int) -> int:
+        return int(_lib.ssu_select_tile(self._h, int(batch)))
+
+    # -- argument marshalling -------------------------------------------------
+    def make_args(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None):
+        """Check shapes/devices and build the ssu_args struct (no device work)."""
+        H, P, N, G = self.nheads, self.headdim, self.dstate, self.ngroups
+        if x.dim() != 3 or tuple(x.shape[1:]) != (H, P):
+            raise ValueError(f"x must be [batch, {H}, {P}], got {tuple(x.shape)}")
+        bs = x.shape[0]
+        if state.dim() != 4 or tuple(state.shape[1:]) != (H, P, N):
+            raise ValueError(f"state must be [pool, {H}, {P}, {N}], got {tuple(state.shape)}")
+        for name, t in (("B", B), ("C", C)):
+            if tuple(t.shape) != (bs, G, N):
+                raise ValueError(f"{name} must be [{bs}, {G}, {N}], got {tuple(t.shape)}")
+        if state_batch_indices is None or tuple(state_batch_indices.shape) != (bs,):
+            raise ValueError(f"state_batch_indices must be [{bs}]")
+        if out is None:
+            raise ValueError("out is required")
+        if tuple(out.shape) != (bs, H, P):
+            raise ValueError(f"out must be [{bs}, {H}, {P}], got {tuple(out.shape)}")
+        dev = state.device
+        if dev.type != "cuda":
+            raise ValueError("state must be on a GPU")
+        for name, t in (("state_batch_indices", state_batch_indices), ("x", x), ("B", B), ("C", C),
+                        ("dt", dt), ("A", A), ("D", D), ("dt_bias", dt_bias), ("out", out)):
+            if t is not None and t.device != dev:
+                raise ValueError(f"{name} is on {t.device}, state on {dev}")
+
+        # dt: [bs, H] or [bs, H, P] with stride 0 over P
+        if dt.dim() == 2 and tuple(dt.shape) == (bs, H):
+            dt_s = (dt.stride(0), dt.stride(1), 0)
+        elif dt.dim() == 3 and tuple(dt.shape) == (bs, H, P):
+            dt_s = tuple(dt.stride())
+        else:
+            raise ValueError(f"dt must be [{bs}, {H}] or [{bs}, {H}, {P}], got {tuple(dt.shape)}")
+
+        def per_head(t, name, full):
+            if t is None:
+                return None
+            if t.dim() == 1 and t.shape[0] == H:
+                return (t.stride(0),) + (0,) * (len(full) - 1)
+            if tuple(t.shape) == full:
+                return tuple(t.stride())
+            raise ValueError(f"{name} must be [{H}] or {list(full)}, got {tuple(t.shape)}")
+
+        A_s = per_head(A, "A", (H, P, N))
+        D_s = per_head(D, "D", (H, P))
+        bias_s = per_head(dt_bias, "dt_bias", (H, P))
+
+        a = Args()
+        a.batch = bs
+        a.reserved = 0
+        a.pool_slots = state.shape[0]
+        a.state = _view(state, state.stride(), _dtype_tag(state, (SSU_F32,), "state"))
+        a.idx = _view(state_batch_indices, state_batch_indices.stride(),
+                      _dtype_tag(state_batch_indices, (SSU_I32, SSU_I64), "state_batch_indices"))
+        a.x = _view(x, x.stride(), _dtype_tag(x, (SSU_BF16,), "x"))
+        a.B = _view(B, B.stride(), _dtype_tag(B, (SSU_BF16,), "B"))
+        a.C = _view(C, C.stride(), _dtype_tag(C, (SSU_BF16,), "C"))
+        a.dt = _view(dt, dt_s, _dtype_tag(dt, (SSU_BF16,), "dt"))
+        a.A = _view(A, A_s, _dtype_tag(A, (SSU_F32,), "A"))
+        a.D = _view(D, D_s, _dtype_tag(D, (SSU_F32,), "D")) if D is not None else _null_view()
+        a.dt_bias = (_view(dt_bias, bias_s, _dtype_tag(dt_bias, (SSU_F32,), "dt_bias"))
+                     if dt_bias is not None else _null_view())
+        a.out = _view(out, out.stride(), _dtype_tag(out, (SSU_BF16,), "out"))
+        return a
+
+    def launch(self, args: Args, stream=None):
+        """Enqueue ssu_update with a prepared Args on ``stream`` (torch stream,
+        raw hipStream_t int, or None for torch's current stream)."""
+        if stream is None:
+            stream = _torch().cuda.current_stream().cuda_stream
+        elif hasattr(stream, "cuda_stream"):
+            stream = stream.cuda_stream
+        st = _lib.ssu_update(self._h, ctypes.byref(args), _vp(stream))
+        if st != SSU_OK:
+            raise SSUError(st, "ssu_update")
+
+    def update(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None,
+               stream=None, check_indices=False):
+        """Advance ``state`` in place by one token and return ``out`` (bf16 [bs, H, P])."""
+        if out is None:
+            out = _torch().empty(x.shape, dtype=_torch().bfloat16, device=x.device)
+        args = self.make_args(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)
+        if check_indices:
+            s = _torch().cuda.current_stream().cuda_stream if stream is None else getattr(
+                stream, "cuda_stream", stream)
+            st = _lib.ssu_check_indices(ctypes.byref(args), _vp(s))
+            if st != SSU_OK:
+                raise SSUError(st, "ssu_check_indices")
+        self.launch(args, stream)
+        return out
+
+
+_handles: dict = {}
+_handles_lock = threading.Lock()
+
+
+def selective_state_update(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softplus=True,
+                           state_batch_indices=None, out=None, tile=-1):
+    """Functional form: one decode step on ``state`` (updated in place); returns out.
+
+    state [pool, H, P, N] fp32; x [bs, H, P] bf16; dt [bs, H] (or [bs, H, P] with
+    stride 0 over P) bf16; A [H] (or [H, P, N] stride-0) fp32; B, C [bs, G, N]
+    bf16; D, dt_bias [H] (or [H, P] stride-0) fp32 or None; state_batch_indices
+    [bs] int32/int64.
+    """
+    H, P, N = state.shape[1], state.shape[2], state.shape[3]
+    G = B.shape[1]
+    key = (H, P, N, G, bool(dt_softplus), tile, state.device.index)
+    with _handles_lock:
+        h = _handles.get(key)
+        if h is None:
+            h = Handle(H, P, N, G, dt_softplus, tile, -1 if state.device.index is None else state.device.index)
+            _handles[key] = h
+    return h.update(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)

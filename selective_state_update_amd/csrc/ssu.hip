@@ -1,0 +1,721 @@
+// ssu.hip -- libssu: the Mamba2 decode-step selective_state_update for AMD
+// Instinct MI355X (gfx950), behind the C ABI declared in include/ssu.h.
+//
+// What one call computes (sglang PR #41223, "[Perf] Mamba2
+// selective_state_update up to 2x faster on B200 via 8x1 launch config for
+// dstate 128", sections "Summary" and "Kernel measurement"): for each request
+// b and head h, gather the fp32 state slot idx[b], advance it by one token in
+// place, and emit out[b,h,:] in bf16. The page calls the kernel memory bound:
+// every step reads and writes each request's fp32 state once, and a launch
+// with too few loads in flight per thread leaves HBM bandwidth unused.
+//
+// Kernel design (gfx950, wave64):
+//   * One workgroup owns `rows_per_group` consecutive state rows p of one
+//     (b, h). A row of N fp32 values is split over LPR lanes with one 16-byte
+//     (dwordx4) chunk each (two chunks 512 bytes apart when N = 256), so one
+//     wave instruction moves 64 x 16 B of contiguous state and RPI = 64/LPR
+//     rows at once. Each lane issues all R of its row loads before using any,
+//     so R dwordx4 loads per lane are in flight.
+//   * B and C: the column -> lane map is the same for every row, so each lane
+//     needs only its own 4 (or 8) values of B and C. They are loaded once per
+//     workgroup straight into registers as fp32 and reused for every row; LDS
+//     would only add a round trip.
+//   * dt', dA, D are per-(b,h) scalars computed once per lane at the start.
+//   * out[p] = sum_n S'[p,n] C[n]: each lane sums its own columns in order
+//     (an fma chain), then the LPR lanes of a row combine in a fixed butterfly
+//     (DPP quad permutes, row half-mirror, row mirror, then a swizzle across
+//     the two 16-lane rows). The order depends only on N, never on the tile,
+//     so every tile gives bitwise-identical results, and no atomics are used.
+//   * No MFMA: 2 flops of update and 2 of contraction per 8 bytes of state is
+//     far below the vector-ALU ridge; the bound is HBM bandwidth.
+//   * Optional XCD-aware ordering: workgroups are dispatched round-robin over
+//     the 8 XCDs; remapping gives neighbouring heads of one request (which
+//     share B, C, x and idx cache lines) the same XCD and its L2.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdint>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <new>
+#include <vector>
+
+#include "ssu.h"
+
+namespace ssu {
+
+using f32x4 = float __attribute__((ext_vector_type(4)));
+using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
+
+struct Params {
+    float *state;
+    int64_t s_slot, s_head, s_row;
+    const void *idx;
+    int64_t pool_slots;
+    const uint16_t *x;
+    int64_t x_b, x_h;
+    const uint16_t *B;
+    int64_t B_b, B_g;
+    const uint16_t *C;
+    int64_t C_b, C_g;
+    const uint32_t *dt_words;  // dt's base rounded down to 4 bytes
+    int64_t dt_b, dt_h, dt_off;  // dt_off: 1 if the base was 2 bytes past a word
+    const float *dt_bias;
+    int64_t dtb_h;
+    const float *A;
+    int64_t A_h;
+    const float *D;
+    int64_t D_h;
+    uint16_t *out;
+    int64_t o_b, o_h;
+    int32_t nheads, heads_per_group, ptiles, softplus;
+    int32_t idx64, xcd_remap, total_groups, pad_;
+};
+
+// ---------------------------------------------------------------- device --
+
+// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+__device__ __forceinline__ uint16_t bf16_round(float f)
+{
+    uint32_t u = __float_as_uint(f);
+    if ((u & 0x7fffffffu) > 0x7f800000u)
+        return static_cast<uint16_t>((u >> 16) | 0x40u);
+    u += 0x7fffu + ((u >> 16) & 1u);
+    return static_cast<uint16_t>(u >> 16);
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp(float v)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
+}
+
+// Sum over each aligned group of LPR lanes (LPR in 4..32); every lane of the
+// group receives the same bits. Butterfly order: lane pairs, quads, eights,
+// sixteens, then the two 16-lane rows of a 32-lane half.
+template <int LPR>
+__device__ __forceinline__ float group_sum(float v)
+{
+    static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "LPR");
+    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
+    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
+    if constexpr (LPR >= 8)
+        v += dpp<0x141>(v);  // row_half_mirror: pairs quad 0 with quad 1 of each 8
+    if constexpr (LPR >= 16)
+        v += dpp<0x140>(v);  // row_mirror: pairs the two 8-lane halves of each row
+    if constexpr (LPR >= 32)  // swizzle, bitmask mode: lane ^ 16 within 32
+        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
+    return v;
+}
+
+template <bool NT>
+__device__ __forceinline__ f32x4 load4(const float *p)
+{
+    if constexpr (NT)
+        return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
+    else
+        return *reinterpret_cast<const f32x4 *>(p);
+}
+
+template <bool NT>
+__device__ __forceinline__ void store4(float *p, f32x4 v)
+{
+    if constexpr (NT)
+        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
+    else
+        *reinterpret_cast<f32x4 *>(p) = v;
+}
+
+// Workgroups are dispatched round-robin over 8 XCDs. Map the first
+// floor(total/8)*8 of them so that logical ids [k*q, (k+1)*q) run on XCD k;
+// the tail keeps its order. A bijection on [0, total).
+__device__ __forceinline__ int xcd_order(int g, int total)
+{
+    const int q = total >> 3;
+    if (g >= (q << 3))
+        return g;
+    return (g & 7) * q + (g >> 3);
+}
+
+template <int N, int R, int W, bool NT>
+__global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
+{
+    constexpr int VEC = N > 128 ? N / 128 : 1;  // 16-byte chunks per lane per row
+    constexpr int LPR = N / (4 * VEC);          // lanes per row
+    constexpr int RPI = 64 / LPR;               // rows per wave instruction
+    constexpr int ROWS_WAVE = RPI * R;
+    constexpr int ROWS_GROUP = ROWS_WAVE * W;
+    static_assert(LPR >= 4 && LPR <= 32, "dstate");
+
+    int g = static_cast<int>(blockIdx.x);
+    if (p.xcd_remap)
+        g = xcd_order(g, p.total_groups);
+    const int t = g % p.ptiles;
+    const int bh = g / p.ptiles;
+    const int h = bh % p.nheads;
+    const int b = bh / p.nheads;
+
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    const int c = lane % LPR;    // column chunk
+    const int sub = lane / LPR;  // row within one instruction
+    const int wrow = t * ROWS_GROUP + wave * ROWS_WAVE;  // first row of this wave (uniform)
+    const int p0 = wrow + sub;
+
+    // This lane's columns of B and C: 8-byte vector loads that do not depend
+    // on the slot, issued first (vector-memory counters retire in order, so
+    // anything issued after the state stream could only be used after it).
+    const int grp = h / p.heads_per_group;
+    u32x2 Bw[VEC], Cw[VEC];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + grp * p.B_g + 4 * c + 128 * v);
+        Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + grp * p.C_g + 4 * c + 128 * v);
+    }
+
+    const int64_t slot = p.idx64 ? static_cast<const int64_t *>(p.idx)[b]
+                                 : static_cast<int64_t>(static_cast<const int32_t *>(p.idx)[b]);
+    if (slot < 0 || slot >= p.pool_slots)
+        return;  // padding entry: no state traffic, out rows untouched
+
+    // State loads: R * VEC dwordx4 per lane in flight.
+    float *sp = p.state + slot * p.s_slot + h * p.s_head + static_cast<int64_t>(p0) * p.s_row + 4 * c;
+    const int64_t jstep = static_cast<int64_t>(RPI) * p.s_row;
+    f32x4 s[R][VEC];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            s[j][v] = load4<NT>(sp + j * jstep + 128 * v);
+
+    // Per-(b,h) scalars through the scalar cache, while the state is in
+    // flight; dt is read as the aligned 32-bit word that holds it.
+    const int64_t dte = b * p.dt_b + h * p.dt_h + p.dt_off;
+    const uint32_t dtw = p.dt_words[dte >> 1];
+    const uint32_t dtbits = (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu);
+    const float bias = p.dt_bias ? p.dt_bias[h * p.dtb_h] : 0.0f;
+    const float Ah = p.A[h * p.A_h];
+    const float Dh = p.D ? p.D[h * p.D_h] : 0.0f;
+
+    // x of this lane's rows wrow + sub + j*RPI. With two rows per instruction
+    // the wave's rows are R whole 32-bit words at a uniform address (scalar
+    // load); otherwise each lane reads its own values.
+    uint32_t xbits[R];
+    const uint16_t *xrow = p.x + b * p.x_b + h * p.x_h + wrow;
+    if constexpr (RPI == 2) {
+        const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
+        const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            xbits[j] = (xw[j] << sh) & 0xffff0000u;
+    } else {
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
+    }
+
+    // Per-(b,h) discretisation, while the state is in flight.
+    const float u = __uint_as_float(dtbits << 16) + bias;
+    const float delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
+    const float dA = expf(Ah * delta);
+
+    float Bv[VEC][4], Cv[VEC][4];
+#pragma unroll
+    for (int v = 0; v < VEC; ++v) {
+        Bv[v][0] = __uint_as_float(Bw[v].x << 16);
+        Bv[v][1] = __uint_as_float(Bw[v].x & 0xffff0000u);
+        Bv[v][2] = __uint_as_float(Bw[v].y << 16);
+        Bv[v][3] = __uint_as_float(Bw[v].y & 0xffff0000u);
+        Cv[v][0] = __uint_as_float(Cw[v].x << 16);
+        Cv[v][1] = __uint_as_float(Cw[v].x & 0xffff0000u);
+        Cv[v][2] = __uint_as_float(Cw[v].y << 16);
+        Cv[v][3] = __uint_as_float(Cw[v].y & 0xffff0000u);
+    }
+    float xv[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        xv[j] = __uint_as_float(xbits[j]);
+
+    // Update in registers, write back, and form each lane's partial output.
+    float y[R];
+#pragma unroll
+    for (int j = 0; j < R; ++j) {
+        const float dx = delta * xv[j];
+        float acc = 0.0f;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            f32x4 &q = s[j][v];
+            q.x = fmaf(q.x, dA, dx * Bv[v][0]);
+            q.y = fmaf(q.y, dA, dx * Bv[v][1]);
+            q.z = fmaf(q.z, dA, dx * Bv[v][2]);
+            q.w = fmaf(q.w, dA, dx * Bv[v][3]);
+            acc = (v == 0) ? q.x * Cv[v][0] : fmaf(q.x, Cv[v][0], acc);
+            acc = fmaf(q.y, Cv[v][1], acc);
+            acc = fmaf(q.z, Cv[v][2], acc);
+            acc = fmaf(q.w, Cv[v][3], acc);
+        }
+        y[j] = acc;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v)
+            store4<NT>(sp + j * jstep + 128 * v, s[j][v]);
+    }
+
+#pragma unroll
+    for (int j = 0; j < R; ++j)
+        y[j] = group_sum<LPR>(y[j]);
+
+    // Lane c of each row group writes row (k + c) of its R rows, so one store
+    // instruction covers up to LPR rows per sub-row.
+    uint16_t *op = p.out + b * p.o_b + h * p.o_h + p0;
+#pragma unroll
+    for (int k = 0; k < R; k += LPR) {
+        float yo = y[k], xo = xv[k];
+#pragma unroll
+        for (int j = k + 1; j < R && j < k + LPR; ++j)
+            if (c == j - k) {
+                yo = y[j];
+                xo = xv[j];
+            }
+        if (c < R - k)
+            op[(k + c) * RPI] = bf16_round(fmaf(Dh, xo, yo));
+    }
+}
+
+// ------------------------------------------------------------------ tiles --
+
+using LaunchFn = hipError_t (*)(const Params &, int grid, hipStream_t);
+
+template <int N, int R, int W, bool NT>
+hipError_t launch(const Params &p, int grid, hipStream_t stream)
+{
+    hipLaunchKernelGGL((ssu_decode_kernel<N, R, W, NT>), dim3(grid), dim3(64 * W), 0, stream, p);
+    return hipGetLastError();
+}
+
+struct Tile {
+    ssu_tile_desc d;
+    LaunchFn fn;
+};
+
+template <int N, int R, int W, bool NT>
+void add_tile(std::vector<Tile> &v, int remap)
+{
+    constexpr int VEC = N > 128 ? N / 128 : 1;
+    constexpr int RPI = 64 / (N / (4 * VEC));
+    Tile t{};
+    t.d.dstate = N;
+    t.d.rows_per_wave = RPI * R;
+    t.d.waves = W;
+    t.d.rows_per_group = RPI * R * W;
+    t.d.nontemporal = NT ? 1 : 0;
+    t.d.xcd_remap = remap;
+    std::snprintf(t.d.name, sizeof t.d.name, "n%d_r%d_w%d%s%s", N, RPI * R, W, NT ? "_nt" : "",
+                  remap ? "_xcd" : "");
+    t.fn = &launch<N, R, W, NT>;
+    v.push_back(t);
+}
+
+template <int N, int R, int W, bool NT>
+void add_both(std::vector<Tile> &v)
+{
+    add_tile<N, R, W, NT>(v, 1);
+    add_tile<N, R, W, NT>(v, 0);
+}
+
+template <int N>
+void add_general(std::vector<Tile> &v)
+{
+    add_both<N, 1, 1, false>(v);
+    add_both<N, 1, 2, false>(v);
+    add_both<N, 1, 4, false>(v);
+    add_both<N, 2, 1, false>(v);
+    add_both<N, 2, 2, false>(v);
+    add_both<N, 2, 4, false>(v);
+    add_both<N, 4, 1, false>(v);
+    add_both<N, 4, 2, false>(v);
+    add_both<N, 4, 4, false>(v);
+    add_both<N, 8, 1, false>(v);
+    add_both<N, 8, 2, false>(v);
+    add_both<N, 8, 4, false>(v);
+}
+
+template <bool NT>
+void add_n128(std::vector<Tile> &v)
+{
+    add_both<128, 1, 1, NT>(v);
+    add_both<128, 1, 2, NT>(v);
+    add_both<128, 1, 4, NT>(v);
+    add_both<128, 1, 8, NT>(v);
+    add_both<128, 2, 1, NT>(v);
+    add_both<128, 2, 2, NT>(v);
+    add_both<128, 2, 4, NT>(v);
+    add_both<128, 2, 8, NT>(v);
+    add_both<128, 4, 1, NT>(v);
+    add_both<128, 4, 2, NT>(v);
+    add_both<128, 4, 4, NT>(v);
+    add_both<128, 4, 8, NT>(v);
+    add_both<128, 8, 1, NT>(v);
+    add_both<128, 8, 2, NT>(v);
+    add_both<128, 8, 4, NT>(v);
+    add_both<128, 16, 1, NT>(v);
+    add_both<128, 16, 2, NT>(v);
+}
+
+const std::vector<Tile> &tiles()
+{
+    static const std::vector<Tile> table = [] {
+        std::vector<Tile> v;
+        add_n128<false>(v);
+        add_n128<true>(v);
+        add_general<16>(v);
+        add_general<32>(v);
+        add_general<64>(v);
+        add_general<256>(v);
+        return v;
+    }();
+    return table;
+}
+
+int find_tile(int N, int rows_per_group, int waves, int nt, int remap)
+{
+    const auto &t = tiles();
+    for (size_t i = 0; i < t.size(); ++i)
+        if (t[i].d.dstate == N && t[i].d.rows_per_group == rows_per_group && t[i].d.waves == waves &&
+            t[i].d.nontemporal == nt && t[i].d.xcd_remap == remap)
+            return static_cast<int>(i);
+    return -1;
+}
+
+}  // namespace ssu
+
+// -------------------------------------------------------------- host ABI --
+
+struct ssu_handle {
+    ssu_config cfg;
+    int32_t forced_tile;  // -1: table
+};
+
+namespace {
+
+thread_local char g_err[256] = "";
+
+ssu_status fail(ssu_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
+ssu_status fail(ssu_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
+
+// The launch configuration for `batch` requests: among the compiled tiles for
+// this N whose rows_per_group divides P, prefer ones that keep many dwordx4
+// loads in flight per lane while still giving the chip enough workgroups.
+int select_tile(const ssu_config &c, int32_t batch)
+{
+    using namespace ssu;
+    const int64_t units = static_cast<int64_t>(batch) * c.nheads;  // (b, h) pairs
+    const int P = c.headdim, N = c.dstate;
+    const int rpi = N >= 128 ? 2 : 64 / (N / 4);
+    // Candidate (rows_per_wave, waves) from the most loads in flight downwards.
+    struct Pick {
+        int rows_per_wave, waves;
+    };
+    static const Pick order[] = {{8, 4}, {8, 2}, {4, 4}, {4, 2}, {2, 4}, {2, 2}, {2, 1}, {1, 1}};
+    const int target_groups = 2048;  // 8 per CU on 256 CUs
+    int fallback = -1;
+    for (const Pick &pk : order) {
+        const int rows_wave = rpi * pk.rows_per_wave;
+        const int rows_group = rows_wave * pk.waves;
+        if (rows_group > P || P % rows_group)
+            continue;
+        const int id = find_tile(N, rows_group, pk.waves, 0, 1);
+        if (id < 0)
+            continue;
+        if (fallback < 0)
+            fallback = id;
+        if (units * (P / rows_group) >= target_groups)
+            return id;
+        fallback = id;  // keep shrinking: smaller groups give more of them
+    }
+    return fallback;
+}
+
+ssu_status check_view(const ssu_view &v, const char *name, int32_t dtype, int rank, bool nullable)
+{
+    if (!v.ptr && !nullable)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "%s: null pointer", name);
+    if (!v.ptr)
+        return SSU_OK;
+    if (v.dtype != dtype)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "%s: dtype tag %d, expected %d", name, v.dtype, dtype);
+    if (v.reserved != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "%s: reserved field must be 0", name);
+    for (int i = 0; i < rank; ++i)
+        if (v.stride[i] < 0)
+            return fail(SSU_ERR_INVALID_ARGUMENT, "%s: negative stride[%d]", name, i);
+    return SSU_OK;
+}
+
+#define SSU_TRY(expr)                    \
+    do {                                 \
+        const ssu_status s_ = (expr);    \
+        if (s_ != SSU_OK)                \
+            return s_;                   \
+    } while (0)
+
+}  // namespace
+
+extern "C" {
+
+int32_t ssu_abi_version(void) { return SSU_ABI_VERSION; }
+
+const char *ssu_last_error(void) { return g_err; }
+
+const char *ssu_status_string(ssu_status s)
+{
+    switch (s) {
+    case SSU_OK: return "SSU_OK";
+    case SSU_ERR_INVALID_ARGUMENT: return "SSU_ERR_INVALID_ARGUMENT";
+    case SSU_ERR_UNSUPPORTED: return "SSU_ERR_UNSUPPORTED";
+    case SSU_ERR_MISALIGNED: return "SSU_ERR_MISALIGNED";
+    case SSU_ERR_HIP: return "SSU_ERR_HIP";
+    case SSU_ERR_NO_MEMORY: return "SSU_ERR_NO_MEMORY";
+    case SSU_ERR_BAD_INDEX: return "SSU_ERR_BAD_INDEX";
+    }
+    return "SSU_ERR_UNKNOWN";
+}
+
+int32_t ssu_tile_count(void) { return static_cast<int32_t>(ssu::tiles().size()); }
+
+ssu_status ssu_tile_info(int32_t tile, ssu_tile_desc *out)
+{
+    if (!out)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_tile_info: null output");
+    if (tile < 0 || tile >= ssu_tile_count())
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_tile_info: tile %d out of range", tile);
+    *out = ssu::tiles()[tile].d;
+    return SSU_OK;
+}
+
+ssu_status ssu_create(const ssu_config *cfg, ssu_handle **out)
+{
+    if (!cfg || !out)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: null argument");
+    *out = nullptr;
+    const ssu_config &c = *cfg;
+    if (c.reserved != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: reserved field must be 0");
+    if (c.nheads < 1 || c.ngroups < 1 || c.nheads % c.ngroups != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: need nheads >= 1 and ngroups dividing it (H=%d G=%d)",
+                    c.nheads, c.ngroups);
+    if (c.headdim < 1 || c.dstate < 1)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: headdim and dstate must be positive");
+    if (!valid_dstate(c.dstate))
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_create: dstate %d not compiled (16, 32, 64, 128, 256)", c.dstate);
+    if (c.headdim % 16 != 0 || c.headdim > 256)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_create: headdim %d must be a multiple of 16 in [16, 256]",
+                    c.headdim);
+    if (c.dt_softplus != 0 && c.dt_softplus != 1)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: dt_softplus must be 0 or 1");
+    if (c.device < -1)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: device must be >= -1");
+    int32_t forced = c.tile;
+    if (forced < -1 || forced >= ssu_tile_count())
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: tile %d out of range", forced);
+    if (forced == -1) {
+        if (const char *env = std::getenv("SSU_TILE")) {
+            char *end = nullptr;
+            const long v = std::strtol(env, &end, 10);
+            if (end == env || *end != '\0' || v < -1 || v >= ssu_tile_count())
+                return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: SSU_TILE=%s is not a tile index", env);
+            forced = static_cast<int32_t>(v);
+        }
+    }
+    if (forced >= 0) {
+        const ssu_tile_desc &d = ssu::tiles()[forced].d;
+        if (d.dstate != c.dstate || c.headdim % d.rows_per_group != 0)
+            return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: tile %s does not fit N=%d P=%d", d.name, c.dstate,
+                        c.headdim);
+    }
+    ssu_handle *h = new (std::nothrow) ssu_handle;
+    if (!h)
+        return fail(SSU_ERR_NO_MEMORY, "ssu_create: out of host memory");
+    h->cfg = c;
+    h->forced_tile = forced;
+    *out = h;
+    return SSU_OK;
+}
+
+void ssu_destroy(ssu_handle *h) { delete h; }
+
+int32_t ssu_select_tile(const ssu_handle *h, int32_t batch)
+{
+    if (!h)
+        return -1;
+    if (h->forced_tile >= 0)
+        return h->forced_tile;
+    return select_tile(h->cfg, batch < 1 ? 1 : batch);
+}
+
+ssu_status ssu_update(const ssu_handle *hd, const ssu_args *a, hipStream_t stream)
+{
+    if (!hd || !a)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: null handle or args");
+    const ssu_config &c = hd->cfg;
+    if (a->batch < 0 || a->pool_slots < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: batch %d / pool_slots %lld negative", a->batch,
+                    static_cast<long long>(a->pool_slots));
+    if (a->reserved != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: reserved field must be 0");
+    if (a->batch == 0)
+        return SSU_OK;
+
+    SSU_TRY(check_view(a->state, "state", SSU_F32, 4, false));
+    if (a->idx.ptr && a->idx.dtype == SSU_I64)
+        SSU_TRY(check_view(a->idx, "idx", SSU_I64, 1, false));
+    else
+        SSU_TRY(check_view(a->idx, "idx", SSU_I32, 1, false));
+    SSU_TRY(check_view(a->x, "x", SSU_BF16, 3, false));
+    SSU_TRY(check_view(a->B, "B", SSU_BF16, 3, false));
+    SSU_TRY(check_view(a->C, "C", SSU_BF16, 3, false));
+    SSU_TRY(check_view(a->dt, "dt", SSU_BF16, 3, false));
+    SSU_TRY(check_view(a->dt_bias, "dt_bias", SSU_F32, 2, true));
+    SSU_TRY(check_view(a->A, "A", SSU_F32, 3, false));
+    SSU_TRY(check_view(a->D, "D", SSU_F32, 2, true));
+    SSU_TRY(check_view(a->out, "out", SSU_BF16, 3, false));
+
+    if (a->state.stride[3] != 1)
+        return fail(SSU_ERR_UNSUPPORTED, "state: dstate stride must be 1");
+    if (a->idx.stride[0] != 1)
+        return fail(SSU_ERR_UNSUPPORTED, "idx: stride must be 1");
+    if (a->x.stride[2] != 1 || a->out.stride[2] != 1)
+        return fail(SSU_ERR_UNSUPPORTED, "x/out: headdim stride must be 1");
+    if (a->B.stride[2] != 1 || a->C.stride[2] != 1)
+        return fail(SSU_ERR_UNSUPPORTED, "B/C: dstate stride must be 1");
+    if (a->dt.stride[2] != 0)
+        return fail(SSU_ERR_UNSUPPORTED, "dt: must be one value per (request, head) (headdim stride 0)");
+    if (a->dt_bias.ptr && a->dt_bias.stride[1] != 0)
+        return fail(SSU_ERR_UNSUPPORTED, "dt_bias: headdim stride must be 0");
+    if (a->A.stride[1] != 0 || a->A.stride[2] != 0)
+        return fail(SSU_ERR_UNSUPPORTED, "A: must be one value per head (headdim, dstate strides 0)");
+    if (a->D.ptr && a->D.stride[1] != 0)
+        return fail(SSU_ERR_UNSUPPORTED, "D: headdim stride must be 0");
+
+    const uintptr_t sp = reinterpret_cast<uintptr_t>(a->state.ptr);
+    if (sp % 16 || a->state.stride[0] % 4 || a->state.stride[1] % 4 || a->state.stride[2] % 4)
+        return fail(SSU_ERR_MISALIGNED, "state: pointer and slot/head/row strides must be 16-byte multiples");
+    const uintptr_t xp = reinterpret_cast<uintptr_t>(a->x.ptr);
+    if (xp % 4 || a->x.stride[0] % 2 || a->x.stride[1] % 2)
+        return fail(SSU_ERR_MISALIGNED, "x: pointer and request/head strides must be 4-byte multiples");
+    for (const ssu_view *v : {&a->B, &a->C}) {
+        const uintptr_t bp = reinterpret_cast<uintptr_t>(v->ptr);
+        if (bp % 8 || v->stride[0] % 4 || v->stride[1] % 4)
+            return fail(SSU_ERR_MISALIGNED, "B/C: pointer and request/group strides must be 8-byte multiples");
+    }
+
+    const int32_t tile = hd->forced_tile >= 0 ? hd->forced_tile : select_tile(c, a->batch);
+    if (tile < 0)
+        return fail(SSU_ERR_UNSUPPORTED, "no launch configuration for N=%d P=%d", c.dstate, c.headdim);
+    const ssu::Tile &T = ssu::tiles()[tile];
+    const int ptiles = c.headdim / T.d.rows_per_group;
+    const int64_t groups = static_cast<int64_t>(a->batch) * c.nheads * ptiles;
+    if (groups > 0x7fffffff)
+        return fail(SSU_ERR_UNSUPPORTED, "batch * heads too large for one launch");
+
+    ssu::Params p{};
+    p.state = static_cast<float *>(const_cast<void *>(a->state.ptr));
+    p.s_slot = a->state.stride[0];
+    p.s_head = a->state.stride[1];
+    p.s_row = a->state.stride[2];
+    p.idx = a->idx.ptr;
+    p.idx64 = a->idx.dtype == SSU_I64;
+    p.pool_slots = a->pool_slots;
+    p.x = static_cast<const uint16_t *>(a->x.ptr);
+    p.x_b = a->x.stride[0];
+    p.x_h = a->x.stride[1];
+    p.B = static_cast<const uint16_t *>(a->B.ptr);
+    p.B_b = a->B.stride[0];
+    p.B_g = a->B.stride[1];
+    p.C = static_cast<const uint16_t *>(a->C.ptr);
+    p.C_b = a->C.stride[0];
+    p.C_g = a->C.stride[1];
+    const uintptr_t dtp = reinterpret_cast<uintptr_t>(a->dt.ptr);
+    if (dtp % 2)
+        return fail(SSU_ERR_MISALIGNED, "dt: pointer must be 2-byte aligned");
+    p.dt_words = reinterpret_cast<const uint32_t *>(dtp & ~uintptr_t(3));
+    p.dt_off = (dtp & 2) ? 1 : 0;
+    p.dt_b = a->dt.stride[0];
+    p.dt_h = a->dt.stride[1];
+    p.dt_bias = static_cast<const float *>(a->dt_bias.ptr);
+    p.dtb_h = a->dt_bias.stride[0];
+    p.A = static_cast<const float *>(a->A.ptr);
+    p.A_h = a->A.stride[0];
+    p.D = static_cast<const float *>(a->D.ptr);
+    p.D_h = a->D.stride[0];
+    p.out = static_cast<uint16_t *>(const_cast<void *>(a->out.ptr));
+    p.o_b = a->out.stride[0];
+    p.o_h = a->out.stride[1];
+    p.nheads = c.nheads;
+    p.heads_per_group = c.nheads / c.ngroups;
+    p.ptiles = ptiles;
+    p.softplus = c.dt_softplus;
+    p.xcd_remap = T.d.xcd_remap;
+    p.total_groups = static_cast<int32_t>(groups);
+
+    int prev = -1;
+    if (c.device >= 0) {
+        if (hipGetDevice(&prev) != hipSuccess)
+            return fail(SSU_ERR_HIP, "hipGetDevice failed");
+        if (prev != c.device && hipSetDevice(c.device) != hipSuccess)
+            return fail(SSU_ERR_HIP, "hipSetDevice(%d) failed", c.device);
+    }
+    const hipError_t e = T.fn(p, static_cast<int>(groups), stream);
+    if (c.device >= 0 && prev != c.device)
+        (void)hipSetDevice(prev);
+    if (e != hipSuccess)
+        return fail(SSU_ERR_HIP, "launch of %s failed: %s", T.d.name, hipGetErrorString(e));
+    return SSU_OK;
+}
+
+ssu_status ssu_check_indices(const ssu_args *a, hipStream_t stream)
+{
+    if (!a)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_check_indices: null args");
+    if (a->batch < 0 || a->pool_slots < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_check_indices: negative size");
+    if (a->batch == 0)
+        return SSU_OK;
+    const bool i64 = a->idx.dtype == SSU_I64;
+    if (!a->idx.ptr || (!i64 && a->idx.dtype != SSU_I32) || a->idx.stride[0] != 1)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_check_indices: idx must be a contiguous i32/i64 view");
+    const size_t esz = i64 ? 8 : 4;
+    std::vector<unsigned char> host(esz * static_cast<size_t>(a->batch));
+    if (hipMemcpyAsync(host.data(), a->idx.ptr, host.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
+        hipStreamSynchronize(stream) != hipSuccess)
+        return fail(SSU_ERR_HIP, "ssu_check_indices: copy of idx failed");
+    std::vector<unsigned char> seen(static_cast<size_t>(a->pool_slots), 0);
+    for (int32_t b = 0; b < a->batch; ++b) {
+        int64_t s;
+        if (i64) {
+            std::memcpy(&s, host.data() + 8 * b, 8);
+        } else {
+            int32_t s32;
+            std::memcpy(&s32, host.data() + 4 * b, 4);
+            s = s32;
+        }
+        if (s < 0 || s >= a->pool_slots)
+            continue;
+        if (seen[s])
+            return fail(SSU_ERR_BAD_INDEX, "idx[%d] = %lld repeats an earlier entry", b, static_cast<long long>(s));
+        seen[s] = 1;
+    }
+    return SSU_OK;
+}
+
+}  // extern "C"

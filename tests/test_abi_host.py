@@ -1,0 +1,273 @@
+"""libssu's C ABI on the host: it loads, exports what include/ssu.h declares,
+and rejects bad arguments before touching the GPU.
+
+No test here launches a kernel: every ssu_update call below carries at least
+one invalid field (or batch 0), so the library returns before any HIP call.
+The pointer values are never dereferenced on the host.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "ssu.h")
+
+
+@pytest.fixture(scope="module")
+def ssu():
+    import selective_state_update_amd as m
+
+    return m
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(ssu_[a-z_0-9]+)\s*\(", text)))
+
+
+def test_header_declares_the_entry_points():
+    names = declared_functions()
+    for n in ("ssu_create", "ssu_update", "ssu_destroy", "ssu_status_string", "ssu_check_indices"):
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(ssu):
+    lib = ctypes.CDLL(ssu.library_path())
+    missing = [n for n in declared_functions() if not hasattr(lib, n)]
+    assert not missing, missing
+    out = subprocess.run(["nm", "-D", "--defined-only", ssu.library_path()], capture_output=True, text=True)
+    if out.returncode == 0:
+        exported = set(re.findall(r"\bT (ssu_[a-z_0-9]+)$", out.stdout, flags=re.M))
+        assert set(declared_functions()) <= exported
+
+
+def test_abi_version(ssu):
+    text = open(HEADER).read()
+    want = int(re.search(r"#define SSU_ABI_VERSION (\d+)", text).group(1))
+    assert ssu.abi_version() == want
+
+
+def test_status_strings(ssu):
+    for code, name in ssu.STATUS_NAMES.items():
+        assert ssu._lib.ssu_status_string(code).decode() == name
+    assert ssu._lib.ssu_status_string(99).decode() == "SSU_ERR_UNKNOWN"
+
+
+def test_struct_layout_matches_header(ssu):
+    # ssu_view: pointer, two int32, four int64
+    assert ctypes.sizeof(ssu.View) == 8 + 4 + 4 + 32
+    assert ctypes.sizeof(ssu.Config) == 8 * 4
+    assert ctypes.sizeof(ssu.Args) == 16 + 10 * ctypes.sizeof(ssu.View)
+    assert ctypes.sizeof(ssu.TileDesc) == 6 * 4 + 48
+
+
+def _create(ssu, **kw):
+    cfg = dict(nheads=16, headdim=64, dstate=128, ngroups=1, dt_softplus=1, tile=-1, device=-1, reserved=0)
+    cfg.update(kw)
+    c = ssu.Config(**cfg)
+    h = ctypes.c_void_p()
+    st = ssu._lib.ssu_create(ctypes.byref(c), ctypes.byref(h))
+    return st, h
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(nheads=0), 1),
+    (dict(ngroups=3), 1),
+    (dict(ngroups=0), 1),
+    (dict(headdim=0), 1),
+    (dict(dstate=100), 2),
+    (dict(dstate=512), 2),
+    (dict(headdim=24), 2),
+    (dict(headdim=512), 2),
+    (dict(dt_softplus=2), 1),
+    (dict(tile=100000), 1),
+    (dict(tile=-2), 1),
+    (dict(device=-5), 1),
+    (dict(reserved=1), 1),
+])
+def test_create_rejects(ssu, kw, code):
+    st, h = _create(ssu, **kw)
+    assert st == code, ssu._lib.ssu_last_error()
+    assert not h.value
+    assert ssu._lib.ssu_last_error().decode()
+
+
+def test_create_rejects_tile_for_other_dstate(ssu):
+    t = ssu.tiles()
+    wrong = next(x["id"] for x in t if x["dstate"] != 128)
+    st, h = _create(ssu, tile=wrong)
+    assert st == 1 and not h.value
+
+
+def test_create_env_override(ssu, monkeypatch):
+    monkeypatch.setenv("SSU_TILE", "not-a-number")
+    st, _ = _create(ssu)
+    assert st == 1
+    t = next(x["id"] for x in ssu.tiles() if x["dstate"] == 128)
+    monkeypatch.setenv("SSU_TILE", str(t))
+    st, h = _create(ssu)
+    assert st == 0
+    assert ssu._lib.ssu_select_tile(h, 512) == t
+    ssu._lib.ssu_destroy(h)
+
+
+def test_destroy_null_is_noop(ssu):
+    ssu._lib.ssu_destroy(None)
+
+
+def test_tiles_are_described(ssu):
+    t = ssu.tiles()
+    assert len(t) == ssu._lib.ssu_tile_count() > 0
+    names = [x["name"] for x in t]
+    assert len(set(names)) == len(names)
+    for x in t:
+        assert x["rows_per_group"] == x["rows_per_wave"] * x["waves"]
+        assert x["dstate"] in (16, 32, 64, 128, 256)
+    d = ssu.TileDesc()
+    assert ssu._lib.ssu_tile_info(len(t), ctypes.byref(d)) == 1
+    assert ssu._lib.ssu_tile_info(0, None) == 1
+
+
+@pytest.mark.parametrize("N", [16, 32, 64, 128, 256])
+@pytest.mark.parametrize("P", [16, 64, 80, 256])
+def test_select_tile_fits_shape(ssu, N, P):
+    st, h = _create(ssu, dstate=N, headdim=P)
+    assert st == 0
+    t = ssu.tiles()
+    for bs in (1, 8, 128, 512, 1024):
+        i = ssu._lib.ssu_select_tile(h, bs)
+        assert i >= 0
+        assert t[i]["dstate"] == N and P % t[i]["rows_per_group"] == 0
+    ssu._lib.ssu_destroy(h)
+
+
+# ---------------------------------------------------------------- ssu_update --
+FAKE = 0x7F0000000000  # 256-byte aligned fake device address, never dereferenced
+
+
+def _good_args(ssu, bs=4, H=16, P=64, N=128, G=1):
+    a = ssu.Args()
+    a.batch, a.reserved, a.pool_slots = bs, 0, 8
+
+    def v(off, dtype, strides):
+        x = ssu.View()
+        x.ptr = FAKE + off
+        x.dtype = dtype
+        x.reserved = 0
+        for i, s in enumerate(strides):
+            x.stride[i] = s
+        return x
+
+    row = H * P + 2 * G * N
+    a.state = v(0, ssu.SSU_F32, (H * P * N, P * N, N, 1))
+    a.idx = v(0x1000, ssu.SSU_I32, (1,))
+    a.x = v(0x2000, ssu.SSU_BF16, (row, P, 1))
+    a.B = v(0x2000 + 2 * H * P, ssu.SSU_BF16, (row, N, 1))
+    a.C = v(0x2000 + 2 * (H * P + G * N), ssu.SSU_BF16, (row, N, 1))
+    a.dt = v(0x3000, ssu.SSU_BF16, (H, 1, 0))
+    a.dt_bias = v(0x4000, ssu.SSU_F32, (1, 0))
+    a.A = v(0x5000, ssu.SSU_F32, (1, 0, 0))
+    a.D = v(0x6000, ssu.SSU_F32, (1, 0))
+    a.out = v(0x7000, ssu.SSU_BF16, (H * P, P, 1))
+    return a
+
+
+def _break(a, field, what, value):
+    v = getattr(a, field)
+    if what == "ptr":
+        v.ptr = value
+    elif what == "dtype":
+        v.dtype = value
+    elif what == "reserved":
+        v.reserved = value
+    else:
+        v.stride[int(what)] = value
+    setattr(a, field, v)
+
+
+BAD = [
+    ("state", "ptr", None, 1), ("idx", "ptr", None, 1), ("x", "ptr", None, 1), ("B", "ptr", None, 1),
+    ("C", "ptr", None, 1), ("dt", "ptr", None, 1), ("A", "ptr", None, 1), ("out", "ptr", None, 1),
+    ("state", "dtype", 1, 1), ("idx", "dtype", 0, 1), ("x", "dtype", 0, 1), ("B", "dtype", 2, 1),
+    ("dt", "dtype", 0, 1), ("A", "dtype", 1, 1), ("D", "dtype", 1, 1), ("dt_bias", "dtype", 1, 1),
+    ("out", "dtype", 0, 1), ("x", "reserved", 7, 1),
+    ("state", "3", 2, 2), ("idx", "0", 2, 2), ("x", "2", 2, 2), ("out", "2", 2, 2), ("B", "2", 2, 2),
+    ("C", "2", 3, 2), ("dt", "2", 1, 2), ("dt_bias", "1", 1, 2), ("A", "1", 1, 2), ("A", "2", 1, 2),
+    ("D", "1", 1, 2), ("x", "0", -1280, 1),
+    ("state", "ptr", FAKE + 8, 3), ("state", "0", 131070, 3), ("state", "2", 130, 3),
+    ("B", "ptr", FAKE + 0x2000 + 2050, 3), ("C", "0", 1282, 3), ("x", "ptr", FAKE + 0x2002, 3),
+    ("x", "1", 63, 3), ("dt", "ptr", FAKE + 0x3001, 3),
+]
+
+
+@pytest.mark.parametrize("field,what,value,code", BAD, ids=[f"{b[0]}.{b[1]}={b[2]}" for b in BAD])
+def test_update_rejects_before_launch(ssu, field, what, value, code):
+    st, h = _create(ssu)
+    assert st == 0
+    a = _good_args(ssu)
+    _break(a, field, what, value)
+    got = ssu._lib.ssu_update(h, ctypes.byref(a), None)
+    assert got == code, (got, ssu._lib.ssu_last_error())
+    ssu._lib.ssu_destroy(h)
+
+
+def test_update_size_errors(ssu):
+    st, h = _create(ssu)
+    a = _good_args(ssu)
+    a.batch = -1
+    assert ssu._lib.ssu_update(h, ctypes.byref(a), None) == 1
+    a = _good_args(ssu)
+    a.pool_slots = -1
+    assert ssu._lib.ssu_update(h, ctypes.byref(a), None) == 1
+    a = _good_args(ssu)
+    a.reserved = 3
+    assert ssu._lib.ssu_update(h, ctypes.byref(a), None) == 1
+    assert ssu._lib.ssu_update(None, ctypes.byref(a), None) == 1
+    assert ssu._lib.ssu_update(h, None, None) == 1
+    ssu._lib.ssu_destroy(h)
+
+
+def test_batch_zero_is_a_noop(ssu):
+    st, h = _create(ssu)
+    a = ssu.Args()  # all pointers NULL: nothing may be read
+    a.batch = 0
+    assert ssu._lib.ssu_update(h, ctypes.byref(a), None) == 0
+    assert ssu._lib.ssu_check_indices(ctypes.byref(a), None) == 0
+    ssu._lib.ssu_destroy(h)
+
+
+def test_check_indices_rejects_bad_views(ssu):
+    a = _good_args(ssu)
+    a.idx.ptr = None
+    assert ssu._lib.ssu_check_indices(ctypes.byref(a), None) == 1
+    a = _good_args(ssu)
+    a.idx.dtype = ssu.SSU_F32
+    assert ssu._lib.ssu_check_indices(ctypes.byref(a), None) == 1
+    a = _good_args(ssu)
+    a.batch = -2
+    assert ssu._lib.ssu_check_indices(ctypes.byref(a), None) == 1
+
+
+def test_python_binding_validates_shapes(ssu):
+    import torch
+
+    h = ssu.Handle(2, 64, 128)
+    st = torch.zeros(4, 2, 64, 128)
+    x = torch.zeros(3, 2, 64, dtype=torch.bfloat16)
+    B = torch.zeros(3, 1, 128, dtype=torch.bfloat16)
+    idx = torch.zeros(3, dtype=torch.int32)
+    dt = torch.zeros(3, 2, dtype=torch.bfloat16)
+    A = torch.zeros(2)
+    out = torch.empty(3, 2, 64, dtype=torch.bfloat16)
+    with pytest.raises(ValueError):
+        h.make_args(st, idx, x[:, :1], B, B, dt, A, out=out)
+    with pytest.raises(ValueError):
+        h.make_args(st, idx, x, B[:, :, :64], B, dt, A, out=out)
+    with pytest.raises(ValueError, match="GPU"):
+        h.make_args(st, idx, x, B, B, dt, A, out=out)
+    with pytest.raises(ssu.SSUError):
+        ssu.Handle(2, 64, 100)

@@ -1,0 +1,71 @@
+"""Host-side checks of the benchmark's measurement arithmetic."""
+import os
+import subprocess
+import sys
+
+import numpy as np
+
+import bench
+import ssu_inputs as si
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "p1_b200_kernel_timings.txt")
+
+
+def _golden():
+    rows, tbps = [], None
+    for line in open(GOLDEN):
+        line = line.strip()
+        if not line or line.startswith("#"):
+            continue
+        f = line.split()
+        if f[0] == "tbps":
+            tbps = (int(f[1]), float(f[2]), float(f[3]))
+        else:
+            rows.append((int(f[0]), float(f[1]), float(f[2])))
+    return rows, tbps
+
+
+def test_byte_formula_reproduces_the_pages_bandwidth():
+    """The page prints about 3.1 -> 6.3 TB/s at batch 512 for 173.5 -> 85.7 us;
+    the state bytes of a call (fp32, read + written) over those times must give
+    the same figures to the printed digit, and so must the full algorithmic
+    byte count (the small operands add under 0.5%)."""
+    rows, (bs, tb_base, tb_pr) = _golden()
+    us = {r[0]: (r[1], r[2]) for r in rows}
+    base_us, pr_us = us[bs]
+    for nbytes in (bench.state_bytes(16, 64, 128, bs), bench.algorithmic_bytes(16, 64, 128, 1, bs)):
+        assert round(nbytes / (base_us * 1e-6) / 1e12, 1) == tb_base
+        assert round(nbytes / (pr_us * 1e-6) / 1e12, 1) == tb_pr
+    assert bench.algorithmic_bytes(16, 64, 128, 1, bs) / bench.state_bytes(16, 64, 128, bs) < 1.005
+
+
+def test_byte_formula_terms():
+    H, P, N, G, bs = 3, 16, 32, 1, 5
+    got = bench.algorithmic_bytes(H, P, N, G, bs)
+    parts = dict(state=8 * bs * H * P * N, x=2 * bs * H * P, BC=2 * 2 * bs * G * N, dt=2 * bs * H,
+                 idx=4 * bs, params=3 * 4 * H, out=2 * bs * H * P)
+    assert got == sum(parts.values())
+
+
+def test_rotation_sets_are_disjoint_and_cold():
+    per_call = 512 * 16 * 64 * 128 * 4
+    K, sets = si.rotation_sets(per_call, 512, bench.ROTATION_BYTES, seed=3)
+    assert K * per_call >= 3 * 256 * 1024 * 1024
+    flat = sets.ravel()
+    assert len(np.unique(flat)) == flat.size == K * 512
+    assert flat.min() == 0 and flat.max() == K * 512 - 1
+    K8, _ = si.rotation_sets(8 * 16 * 64 * 128 * 4, 8, bench.ROTATION_BYTES, seed=1)
+    assert K8 == 192
+
+
+def test_sweep_grid_is_920_points():
+    pts = si.sweep_points()
+    assert len(pts) == 920
+    assert {h for h, _ in pts} == {8, 16, 32, 64, 128}
+    bss = sorted({b for _, b in pts})
+    assert bss[:64] == list(range(1, 65)) and bss[64:] == list(range(72, 1025, 8))
+
+
+def test_multi_gpu_request_exits_with_message():
+    r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
+    assert r.returncode == 2 and "one GPU" in r.stderr

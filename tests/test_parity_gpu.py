@@ -1,0 +1,325 @@
+"""libssu on the GPU against the CPU oracle, element by element.
+
+Every test calls the HIP kernel through the C ABI (the Python binding only
+marshals arguments) and compares with oracle/ on the same seeded inputs:
+state within 1e-5 * (1 + |ref|), out within 2 bf16 ulp of bf16(fp32(y)) (with
+the cancellation floor of tests/tolerance.py), untouched slots bitwise
+unchanged, reruns and launch configurations bitwise identical.
+"""
+import numpy as np
+import pytest
+
+import ssu_inputs as si
+
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _problem(cfg_id, pool_slots=None):
+    c = dict(si.CONFIGS[cfg_id])
+    c.pop("name")
+    if pool_slots is not None:
+        c["pool_slots"] = pool_slots
+    elif "pool_slots" not in c:
+        c["pool_slots"] = 2 * c["batch"]
+    return si.make_problem(**c)
+
+
+@pytest.mark.parametrize("cfg", [0, 1, 2, 3])
+def test_config_parity_and_rerun(ref, cfg):
+    torch = gu.torch_mod()
+    p = _problem(cfg)
+    print(f"config {cfg}: {si.CONFIGS[cfg]['name']}", flush=True)
+    dp = gu.DeviceProblem(p)
+    pool0 = p.pool.copy()
+    backup = dp.pool.clone()
+    h = dp.handle()
+    out = dp.run(h)
+    torch.cuda.synchronize()
+    _, pool_gpu, out_bits, floor = gu.compare_full(ref, dp, pool0, out, f"config {cfg}")
+    print(f"config {cfg}: tile {h.selected_tile(p.batch)}, floor passes {floor}", flush=True)
+    # rerun from the restored pool: bitwise equal
+    dp.pool.copy_(backup)
+    out2 = dp.run(h, out=torch.empty_like(out))
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(out2), out_bits)
+    assert np.array_equal(dp.pool.cpu().numpy().view(np.uint32), pool_gpu.view(np.uint32))
+
+
+@pytest.mark.parametrize("N,P", [(128, 64), (16, 64), (32, 64), (64, 64), (256, 64), (128, 32)])
+def test_every_tile_bitwise_identical(ref, N, P):
+    """All launch configurations give the same bits (fixed reduction order)."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=P, N=N, G=1, batch=6, pool_slots=13, seed=500 + N + P)
+    dp = gu.DeviceProblem(p)
+    backup = dp.pool.clone()
+    base_out = dp.run(tile=-1).clone()
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), base_out, f"N{N} P{P} auto")
+    base_pool = dp.pool.clone()
+    ids = [t["id"] for t in ssu.tiles() if t["dstate"] == N and P % t["rows_per_group"] == 0]
+    assert ids
+    for tid in ids:
+        dp.pool.copy_(backup)
+        o = dp.run(tile=tid, out=torch.empty_like(base_out))
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), base_out.view(torch.int16)), f"tile {tid} out differs"
+        assert torch.equal(dp.pool.view(torch.int32), base_pool.view(torch.int32)), f"tile {tid} state differs"
+
+
+@pytest.mark.parametrize("N,P,H,G,bs", [
+    (16, 64, 4, 1, 5), (32, 32, 4, 2, 7), (64, 64, 8, 4, 3), (256, 64, 4, 1, 9), (128, 16, 6, 3, 4),
+    (128, 128, 4, 1, 6), (128, 256, 2, 2, 3), (64, 80, 4, 1, 5), (128, 64, 8, 8, 4), (256, 256, 2, 1, 3),
+])
+def test_shapes_groups_parity(ref, N, P, H, G, bs):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=H, P=P, N=N, G=G, batch=bs, pool_slots=2 * bs + 1, seed=600 + N + P + H + G)
+    dp = gu.DeviceProblem(p)
+    out = dp.run()
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, f"N{N} P{P} H{H} G{G} bs{bs}")
+
+
+@pytest.mark.parametrize("softplus,use_bias,use_D", [(False, True, True), (True, False, True),
+                                                     (True, True, False), (False, False, False)])
+def test_options_parity(ref, softplus, use_bias, use_D):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=8, pool_slots=17, seed=700, dt_softplus=softplus)
+    dp = gu.DeviceProblem(p)
+    out = dp.run(use_bias=use_bias, use_D=use_D)
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, f"softplus={softplus} bias={use_bias} D={use_D}",
+                    use_bias=use_bias, use_D=use_D)
+
+
+def test_padding_and_int64_indices(ref):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=10, seed=800)
+    idx = p.idx.copy()
+    idx[1] = -1
+    idx[4] = p.pool_slots  # one past the end: padding too
+    p.idx = idx
+    dp = gu.DeviceProblem(p)
+    sentinel = torch.full((6, 4, 64), 0.5, dtype=torch.bfloat16, device="cuda")
+    out = dp.run(out=sentinel)
+    torch.cuda.synchronize()
+    r, pool_gpu, out_bits, _ = gu.compare_full(ref, dp, p.pool.copy(), out, "padding")
+    half = gu.bits(torch.tensor([0.5], dtype=torch.bfloat16))[0]
+    assert np.all(out_bits[[1, 4]] == half), "padding rows written"
+    # int64 indices: bitwise the same as int32
+    dp2 = gu.DeviceProblem(p)
+    o64 = dp2.run(idx=dp2.idx.to(torch.int64), out=torch.full_like(sentinel, 0.5))
+    torch.cuda.synchronize()
+    assert np.array_equal(gu.bits(o64), out_bits)
+    assert np.array_equal(dp2.pool.cpu().numpy().view(np.uint32), pool_gpu.view(np.uint32))
+
+
+def test_dt_zero_leaves_state_unchanged(ref):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=5, pool_slots=9, seed=900, dt_softplus=False)
+    p.dt[:] = 0
+    dp = gu.DeviceProblem(p)
+    before = dp.pool.clone()
+    out = dp.run(use_bias=False)
+    torch.cuda.synchronize()
+    assert torch.equal(dp.pool.view(torch.int32), before.view(torch.int32))
+    gu.compare_full(ref, dp, p.pool.copy(), out, "dt=0", use_bias=False)
+
+
+def test_C_zero_gives_D_x_exactly(ref):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=5, pool_slots=9, seed=901)
+    o = p.nheads * p.headdim + p.ngroups * p.dstate
+    p.xbc[:, o:] = 0
+    dp = gu.DeviceProblem(p)
+    out = dp.run()
+    torch.cuda.synchronize()
+    want = (dp.D[None, :, None].double() * dp.x.double()).float().to(torch.bfloat16)
+    assert torch.equal(out.view(torch.int16), want.view(torch.int16))
+    gu.compare_full(ref, dp, p.pool.copy(), out, "C=0")
+
+
+def test_very_negative_A_collapses_state(ref):
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=5, pool_slots=9, seed=902)
+    p.dt[:] = 0
+    p.A[:] = -1e9
+    dp = gu.DeviceProblem(p)
+    out = dp.run()
+    torch.cuda.synchronize()
+    r, pool_gpu, _, _ = gu.compare_full(ref, dp, p.pool.copy(), out, "A=-1e9")
+    # closed form: S' = delta * x[p] * B[n]
+    delta = np.logaddexp(0.0, p.dt_bias.astype(np.float64))
+    xs = si.bf16_values(p.x).astype(np.float64)
+    Bs = si.bf16_values(p.B[:, 0]).astype(np.float64)
+    want = delta[None, :, None, None] * xs[:, :, :, None] * Bs[:, None, None, :]
+    gu.assert_state(pool_gpu[p.idx], want, "closed form")
+
+
+@pytest.mark.parametrize("K", [2, 7, 32])
+def test_k_successive_steps_match_scan(ref, K):
+    """K decode calls equal the oracle's sequential length-K scan."""
+    torch = gu.torch_mod()
+    base = si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=11, seed=1000 + K)
+    steps = [si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=11, seed=2000 + 10 * K + t, idx=base.idx)
+             for t in range(K)]
+    dev = gu.DeviceProblem(base)
+    h = dev.handle()
+    outs = []
+    for s in steps:
+        d = gu.DeviceProblem(s, pool=dev.pool)
+        outs.append(d.run(h).clone())
+    torch.cuda.synchronize()
+    x = np.stack([s.x for s in steps])
+    B = np.stack([s.B for s in steps])
+    C = np.stack([s.C for s in steps])
+    dt = np.stack([s.dt for s in steps])
+    pool_ref = base.pool.copy()
+    r = ref.run(pool_ref, base.idx, x, B, C, dt, base.A, base.dt_bias, base.D)
+    gpu = dev.pool.cpu().numpy()
+    gu.assert_state(gpu[base.idx], r["state"], f"K={K} state")
+    for t in (0, K - 1):
+        gu.assert_out(gu.bits(outs[t]), {k: r[k][t] for k in ("out", "y", "tau")}, f"K={K} out[{t}]")
+
+
+def test_hip_graph_replays_match_eager(ref):
+    """Three updates captured in one HIP graph, replayed three times with eager
+    work in between; every replay equals the eager run from the same state."""
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=24, seed=1100)
+    sets = [np.arange(6, dtype=np.int32) + 6 * k for k in range(3)]
+    dp = gu.DeviceProblem(p)
+    h = dp.handle()
+    idxs = [torch.from_numpy(s).cuda() for s in sets]
+    outs = [torch.empty_like(dp.out) for _ in sets]
+
+    def calls():
+        for i, o in zip(idxs, outs):
+            h.update(dp.pool, i, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, o)
+
+    start = dp.pool.clone()
+    # eager reference of three successive rounds
+    eager = []
+    for _ in range(3):
+        calls()
+        torch.cuda.synchronize()
+        eager.append((dp.pool.clone(), [o.clone() for o in outs]))
+    dp.pool.copy_(start)
+    s = torch.cuda.Stream()
+    s.wait_stream(torch.cuda.current_stream())
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s):
+        calls()  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(s)
+    torch.cuda.synchronize()
+    dp.pool.copy_(start)
+    torch.cuda.synchronize()
+    with torch.cuda.graph(g):
+        calls()
+    dp.pool.copy_(start)  # capture does not run the work
+    torch.cuda.synchronize()
+    for k in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (dp.pool[:1].sum() + 1).item()  # eager work between replays
+        want_pool, want_outs = eager[k]
+        assert torch.equal(dp.pool.view(torch.int32), want_pool.view(torch.int32)), f"replay {k} state"
+        for o, w in zip(outs, want_outs):
+            assert torch.equal(o.view(torch.int16), w.view(torch.int16)), f"replay {k} out"
+    # and the first round is right against the oracle
+    pool_ref = p.pool.copy()
+    for s_ in sets:
+        r = ref.run(pool_ref, s_, p.x, p.B, p.C, p.dt, p.A, p.dt_bias, p.D)
+    gu.assert_state(eager[0][0].cpu().numpy()[sets[2]], r["state"], "graph round 0, set 2")
+
+
+def test_batch_zero_and_functional_api(ref):
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    p = si.make_problem(H=2, P=64, N=128, batch=4, pool_slots=8, seed=0)
+    dp = gu.DeviceProblem(p)
+    before = dp.pool.clone()
+    empty = torch.empty(0, 2, 64, dtype=torch.bfloat16, device="cuda")
+    eB = torch.empty(0, 1, 128, dtype=torch.bfloat16, device="cuda")
+    o = ssu.selective_state_update(dp.pool, empty, torch.empty(0, 2, dtype=torch.bfloat16, device="cuda"),
+                                   dp.A, eB, eB, dp.D, dp.dt_bias, True,
+                                   torch.empty(0, dtype=torch.int32, device="cuda"))
+    torch.cuda.synchronize()
+    assert o.shape == (0, 2, 64) and torch.equal(dp.pool, before)
+    out = ssu.selective_state_update(dp.pool, dp.x, dp.dt, dp.A, dp.B, dp.C, dp.D, dp.dt_bias, True, dp.idx)
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, "functional")
+
+
+def test_check_indices_detects_duplicates():
+    import selective_state_update_amd as ssu
+
+    p = si.make_problem(H=2, P=64, N=128, batch=4, pool_slots=8, seed=3)
+    dp = gu.DeviceProblem(p)
+    h = dp.handle()
+    h.update(dp.pool, dp.idx, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out, check_indices=True)
+    dup = dp.idx.clone()
+    dup[3] = dup[0]
+    with pytest.raises(ssu.SSUError, match="BAD_INDEX"):
+        h.update(dp.pool, dup, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out, check_indices=True)
+
+
+def test_strided_pool_view(ref):
+    """The pool may be one layer's view of a larger cache (slot stride larger
+    than H*P*N); the state of other layers must stay untouched."""
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=5, pool_slots=9, seed=1200)
+    big = torch.randn(9, 3, 4, 64, 128, device="cuda")
+    big[:, 1] = torch.from_numpy(p.pool).cuda()
+    other = big[:, [0, 2]].clone()
+    pool_view = big[:, 1]
+    dp = gu.DeviceProblem(p, pool=pool_view)
+    out = dp.run()
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, "strided pool")
+    assert torch.equal(big[:, [0, 2]], other)
+
+
+def test_largest_sweep_point_sampled(ref):
+    """H=128, batch 1024 (4 GiB of state per call) in the launch configuration
+    the library picks: sampled requests against the oracle, untouched slots
+    bitwise, rerun bitwise."""
+    torch = gu.torch_mod()
+    H, bs = 128, 1024
+    p = si.make_problem(H=H, P=64, N=128, batch=bs, pool_slots=bs + 64, seed=si.sweep_seed(H, bs),
+                        host_pool=False)
+    pool = torch.empty((bs + 64, H, 64, 128), device="cuda")
+    si.draw_pool_on_device(pool, p.seed)
+    dp = gu.DeviceProblem(p, pool=pool)
+    backup = pool.clone()
+    out = dp.run()
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(7))
+    sample = np.sort(rng.choice(bs, size=6, replace=False))
+    sl = torch.from_numpy(p.idx[sample].astype(np.int64)).cuda()
+    before = backup[sl].cpu().numpy()
+    after = pool[sl].cpu().numpy()
+    sub_pool = before.copy()
+    sub_idx = np.arange(len(sample), dtype=np.int32)
+    r = ref.run(sub_pool, sub_idx, p.x[sample], p.B[sample], p.C[sample], p.dt[sample], p.A, p.dt_bias, p.D)
+    gu.assert_state(after, r["state"], "H128 bs1024 sampled")
+    gu.assert_out(gu.bits(out)[sample], r, "H128 bs1024 sampled")
+    mask = torch.ones(bs + 64, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(p.idx.astype(np.int64)).cuda()] = False
+    assert torch.equal(pool[mask].view(torch.int32), backup[mask].view(torch.int32))
+    o1 = out.clone()
+    s1 = pool[sl].clone()
+    pool.copy_(backup)
+    dp.run(out=out)
+    torch.cuda.synchronize()
+    assert torch.equal(out.view(torch.int16), o1.view(torch.int16))
+    assert torch.equal(pool[sl].view(torch.int32), s1.view(torch.int32))
