@@ -328,6 +328,75 @@ def run_sweep(a):
             torch.cuda.empty_cache()
 
 
+def run_tile_sweep(a):
+    """µs/call and GB/s of every compiled launch configuration for this N and
+    P on the chosen workload (same rotation and graph method), one line each."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    w = WORKLOADS[a.config]
+    H, P, N, G, bs = w["H"], w["P"], w["N"], w["G"], w["batch"]
+    nbytes = algorithmic_bytes(H, P, N, G, bs)
+    rot = Rotation(H, P, N, G, bs, seed=a.config)
+    auto = ssu.Handle(H, P, N, G, True, -1).selected_tile(bs)
+    out = open(a.out, "w") if a.out else sys.stdout
+    print(f"# H{H} P{P} N{N} bs{bs}: {nbytes} B/call; auto tile {ssu.tiles()[auto]['name']}", file=out)
+    print("tile name rows_per_group waves us_per_call GBps pct_peak", file=out, flush=True)
+    for t in ssu.tiles():
+        if t["dstate"] != N or P % t["rows_per_group"]:
+            continue
+        h = ssu.Handle(H, P, N, G, True, t["id"])
+        args = rot.args(h)
+        calls = max(20, rot.K)
+        g = capture(h, args, 0, calls)
+        g.replay()
+        torch.cuda.synchronize()
+        reps = [time_graph(g, 10) / (10 * calls) for _ in range(5)]
+        us = statistics.median(reps) * 1e6
+        gbs = nbytes / (us * 1e-6) / 1e9
+        print(f"{t['id']} {t['name']} {t['rows_per_group']} {t['waves']} {us:.3f} {gbs:.1f} "
+              f"{100 * gbs / HBM_PEAK_GBS:.2f}", file=out, flush=True)
+        del g
+
+
+def run_copy_ceiling(a):
+    """Attainable read+write HBM bandwidth on this machine: plain device copies of
+    the headline call's state volume (256 MiB read + 256 MiB written), rotated
+    over buffers totalling >= 3x the last-level cache, timed like the decode
+    kernel (HIP graph of 20 calls, median of 5 x 20 replays)."""
+    import torch
+
+    nelem = 64 * 1024 * 1024  # 256 MiB of fp32
+    nbuf = 4
+    src = [torch.empty(nelem, device="cuda").normal_() for _ in range(nbuf)]
+    dst = [torch.empty(nelem, device="cuda") for _ in range(nbuf)]
+    ops = {
+        "copy_(hipMemcpy)": lambda i: dst[i].copy_(src[i]),
+        "mul(elementwise)": lambda i: torch.mul(src[i], 2.0, out=dst[i]),
+        "read-only(sum)": lambda i: src[i].sum(),
+    }
+    for name, op in ops.items():
+        for i in range(nbuf):
+            op(i)
+        torch.cuda.synchronize()
+        g = torch.cuda.CUDAGraph()
+        try:
+            with torch.cuda.graph(g):
+                for i in range(20):
+                    op(i % nbuf)
+        except Exception as e:  # noqa: BLE001 - report and go on
+            print(f"{name}: capture failed: {e}", flush=True)
+            continue
+        g.replay()
+        torch.cuda.synchronize()
+        reps = [time_graph(g, 20) / (20 * 20) for _ in range(5)]
+        us = statistics.median(reps) * 1e6
+        moved = nelem * 4 * (1 if name.startswith("read-only") else 2)
+        print(f"ceiling {name}: {us:.2f} us per {moved >> 20} MiB moved -> {moved / us / 1e3:.1f} GB/s "
+              f"({100 * moved / us / 1e3 / HBM_PEAK_GBS:.1f}% of 8 TB/s)", flush=True)
+
+
 def run_counters(a):
     """Eager calls for a rocprofv3 --pmc pass: `a.steps` headline calls rotating
     over the slot sets, then a plain device copy of a known size (256 MiB read
@@ -395,9 +464,9 @@ def summarize_counters(a):
 
 Commands (run from the repository root on one MI355X):
 
-    rocprofv3 --pmc FETCH_SIZE -d {a.fetch_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
-    rocprofv3 --pmc WRITE_SIZE -d {a.write_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
-    python3 bench.py --summarize-counters <fetch_dir>,<write_dir> --write-profile
+    rocprofv3 --pmc FETCH_SIZE -f csv -d {a.fetch_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
+    rocprofv3 --pmc WRITE_SIZE -f csv -d {a.write_dir_name} -o run -- python3 bench.py --counters --steps {a.steps}
+    python3 bench.py --summarize-counters {a.fetch_dir_name},{a.write_dir_name} --steps {a.steps} --write-profile
 
 Counters are KiB per dispatch. Each is scaled by the ratio (known bytes / counter)
 measured on a plain device copy of 268435456 bytes read + 268435456 written in the
@@ -437,6 +506,8 @@ def main():
     ap.add_argument("--batches", default="")
     ap.add_argument("--out", default="")
     ap.add_argument("--counters", action="store_true")
+    ap.add_argument("--tile-sweep", action="store_true")
+    ap.add_argument("--copy-ceiling", action="store_true")
     ap.add_argument("--summarize-counters", default="")
     ap.add_argument("--write-profile", action="store_true")
     ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
@@ -450,6 +521,10 @@ def main():
         summarize_counters(a)
     elif a.counters:
         run_counters(a)
+    elif a.tile_sweep:
+        run_tile_sweep(a)
+    elif a.copy_ceiling:
+        run_copy_ceiling(a)
     elif a.sweep:
         run_sweep(a)
     else:

@@ -324,21 +324,23 @@ void add_both(std::vector<Tile> &v)
     add_tile<N, R, W, NT>(v, 0);
 }
 
+// Tiles for the other dstate values: non-temporal only (the measured winner
+// for the state stream at N = 128), both workgroup orders.
 template <int N>
 void add_general(std::vector<Tile> &v)
 {
-    add_both<N, 1, 1, false>(v);
-    add_both<N, 1, 2, false>(v);
-    add_both<N, 1, 4, false>(v);
-    add_both<N, 2, 1, false>(v);
-    add_both<N, 2, 2, false>(v);
-    add_both<N, 2, 4, false>(v);
-    add_both<N, 4, 1, false>(v);
-    add_both<N, 4, 2, false>(v);
-    add_both<N, 4, 4, false>(v);
-    add_both<N, 8, 1, false>(v);
-    add_both<N, 8, 2, false>(v);
-    add_both<N, 8, 4, false>(v);
+    add_both<N, 1, 1, true>(v);
+    add_both<N, 1, 2, true>(v);
+    add_both<N, 1, 4, true>(v);
+    add_both<N, 2, 1, true>(v);
+    add_both<N, 2, 2, true>(v);
+    add_both<N, 2, 4, true>(v);
+    add_both<N, 4, 1, true>(v);
+    add_both<N, 4, 2, true>(v);
+    add_both<N, 4, 4, true>(v);
+    add_both<N, 8, 1, true>(v);
+    add_both<N, 8, 2, true>(v);
+    add_both<N, 8, 4, true>(v);
 }
 
 template <bool NT>
@@ -413,35 +415,38 @@ ssu_status fail(ssu_status s, const char *fmt, ...)
 
 bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
-// The launch configuration for `batch` requests: among the compiled tiles for
-// this N whose rows_per_group divides P, prefer ones that keep many dwordx4
-// loads in flight per lane while still giving the chip enough workgroups.
+// The launch configuration for `batch` requests. Measured on MI355X (tile
+// sweep over every compiled configuration at H16 P64 N128, batches 8, 128 and
+// 512, cold state): non-temporal state access plus XCD-ordered workgroups win
+// at every batch, and two dwordx4 state loads per lane with four waves per
+// workgroup is best or within 0.5% of best (512: 88.6 us; 128: 24.9 us; 8:
+// 3.19 us). More loads per lane lowers occupancy and loses; one load per lane
+// loses more. So: two loads per lane (R = 2 / VEC), the most waves (4, 2, 1)
+// that still give the chip `target_groups` workgroups, else the smallest
+// groups that fit P.
 int select_tile(const ssu_config &c, int32_t batch)
 {
     using namespace ssu;
     const int64_t units = static_cast<int64_t>(batch) * c.nheads;  // (b, h) pairs
     const int P = c.headdim, N = c.dstate;
-    const int rpi = N >= 128 ? 2 : 64 / (N / 4);
-    // Candidate (rows_per_wave, waves) from the most loads in flight downwards.
-    struct Pick {
-        int rows_per_wave, waves;
-    };
-    static const Pick order[] = {{8, 4}, {8, 2}, {4, 4}, {4, 2}, {2, 4}, {2, 2}, {2, 1}, {1, 1}};
-    const int target_groups = 2048;  // 8 per CU on 256 CUs
+    const int vec = N > 128 ? N / 128 : 1;
+    const int rpi = 64 / (N / (4 * vec));
+    const int64_t target_groups = 1024;
     int fallback = -1;
-    for (const Pick &pk : order) {
-        const int rows_wave = rpi * pk.rows_per_wave;
-        const int rows_group = rows_wave * pk.waves;
-        if (rows_group > P || P % rows_group)
-            continue;
-        const int id = find_tile(N, rows_group, pk.waves, 0, 1);
-        if (id < 0)
-            continue;
-        if (fallback < 0)
-            fallback = id;
-        if (units * (P / rows_group) >= target_groups)
-            return id;
-        fallback = id;  // keep shrinking: smaller groups give more of them
+    for (int R : {2 / vec > 0 ? 2 / vec : 1, 1}) {
+        for (int W : {4, 2, 1}) {
+            const int rows_group = rpi * R * W;
+            if (rows_group > P || P % rows_group)
+                continue;
+            const int id = find_tile(N, rows_group, W, 1, 1);
+            if (id < 0)
+                continue;
+            if (units * (P / rows_group) >= target_groups)
+                return id;
+            fallback = id;  // keep shrinking: smaller groups give more of them
+        }
+        if (fallback >= 0)
+            return fallback;
     }
     return fallback;
 }

@@ -171,6 +171,8 @@ def test_k_successive_steps_match_scan(ref, K):
     base = si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=11, seed=1000 + K)
     steps = [si.make_problem(H=4, P=64, N=128, batch=6, pool_slots=11, seed=2000 + 10 * K + t, idx=base.idx)
              for t in range(K)]
+    for s in steps:  # the per-head parameters are the layer's weights: the same for every token
+        s.A, s.D, s.dt_bias = base.A, base.D, base.dt_bias
     dev = gu.DeviceProblem(base)
     h = dev.handle()
     outs = []
