@@ -69,8 +69,15 @@ def algorithmic_bytes(H, P, N, G, batch):
 
 
 def source_digest() -> str:
-    with open(KERNEL_SRC, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """Hash of the kernel source's code: comments and whitespace are removed
+    first, so only a change to the code itself invalidates counter data."""
+    import re
+
+    text = open(KERNEL_SRC).read()
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    text = " ".join(text.split())
+    return hashlib.sha256(text.encode()).hexdigest()[:16]
 
 
 # --------------------------------------------------------------------------- #
@@ -196,7 +203,7 @@ def counter_traffic():
         if ":" in line and line.startswith("- "):
             k, v = line[2:].split(":", 1)
             fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256_16") != source_digest():
+    if fields.get("kernel_code_digest") != source_digest():
         return None
     try:
         return int(float(fields["traffic_bytes_per_launch"]))
@@ -341,6 +348,11 @@ def run_tile_sweep(a):
     rot = Rotation(H, P, N, G, bs, seed=a.config)
     auto = ssu.Handle(H, P, N, G, True, -1).selected_tile(bs)
     out = open(a.out, "w") if a.out else sys.stdout
+    prop = torch.cuda.get_device_properties(0)
+    info = {k: getattr(prop, k) for k in ("name", "multi_processor_count", "shared_memory_per_multiprocessor",
+                                          "shared_memory_per_block", "max_threads_per_multi_processor",
+                                          "L2_cache_size") if hasattr(prop, k)}
+    print(f"# device {info}", file=out)
     print(f"# H{H} P{P} N{N} bs{bs}: {nbytes} B/call; auto tile {ssu.tiles()[auto]['name']}", file=out)
     print("tile name rows_per_group waves us_per_call GBps pct_peak", file=out, flush=True)
     for t in ssu.tiles():
@@ -472,7 +484,7 @@ Counters are KiB per dispatch. Each is scaled by the ratio (known bytes / counte
 measured on a plain device copy of 268435456 bytes read + 268435456 written in the
 same run.
 
-- kernel_source_sha256_16: `{source_digest()}`
+- kernel_code_digest: `{source_digest()}`
 - ssu_dispatches: {len(fs)}
 - fetch_kib_median: {statistics.median(fs):.1f}
 - write_kib_median: {statistics.median(ws):.1f}

@@ -16,8 +16,9 @@
  *     out[b,h,p] = bf16( sum_n S[p,n] * C[b,g,n] + D[h] * x[b,h,p] )
  *
  * The page states the problem this way: an fp32 state pool [pool, H, P, N]
- * addressed through random state_batch_indices, x/B/C as strided views of one
- * bf16 tensor, and dt, A, D, dt_bias as stride-0 broadcasts per head. The
+ * addressed through random state_batch_indices, x/B/C as views into one packed
+ * bf16 tensor, and dt, A, D, dt_bias holding one value per head (zero strides
+ * over the other axes). The
  * arguments below mirror that statement: every operand is a strided view.
  *
  * Numerics: fp32 arithmetic throughout; the sum over n is taken in one fixed
@@ -108,8 +109,10 @@ typedef struct ssu_view {
  *   D       [H, P] f32, stride[1] == 0. ptr may be NULL (no skip term).
  *   out     [batch, H, P] bf16, written. stride[2] must be 1.
  *
- * x, B and C may be views into one packed tensor. out must not overlap any
- * input, and the state rows of distinct requests must not overlap.
+ * x, B and C may be views into one packed tensor. Neither out nor the state
+ * pool may overlap any input (the kernel reads inputs through the read-only
+ * scalar cache), out must not overlap the state, and the state rows of
+ * distinct requests must not overlap.
  */
 typedef struct ssu_args {
     int32_t batch;      /* >= 0; 0 is a no-op */
@@ -128,6 +131,8 @@ typedef struct ssu_tile_desc {
     int32_t rows_per_group;  /* rows_per_wave * waves */
     int32_t nontemporal;     /* 1: state loads/stores carry the non-temporal hint */
     int32_t xcd_remap;       /* 1: workgroups of neighbouring heads share an XCD */
+    int32_t groups_per_cu;   /* residency cap: at most this many workgroups per CU
+                                (enforced by reserving unused LDS); 0 = none */
     char name[48];
 } ssu_tile_desc;
 

@@ -11,7 +11,7 @@ The operation follows the problem statement of sglang PR #41223 ("[Perf]
 Mamba2 selective_state_update up to 2x faster on B200 via 8x1 launch config for
 dstate 128", section "Kernel measurement"): an fp32 state pool [pool, H, P, N]
 addressed by state_batch_indices, x [bs, H, P] and B/C [bs, G, N] in bf16 (they
-may be strided views of one packed tensor), and dt, A, D, dt_bias broadcast
+may be views into one packed tensor), and dt, A, D, dt_bias broadcast
 per head. Per request b and head h:
 
     delta = softplus(dt + dt_bias);  a = exp(A * delta)
@@ -78,7 +78,7 @@ class Args(ctypes.Structure):
 
 class TileDesc(ctypes.Structure):
     _fields_ = [("dstate", _i32), ("rows_per_wave", _i32), ("waves", _i32), ("rows_per_group", _i32),
-                ("nontemporal", _i32), ("xcd_remap", _i32), ("name", ctypes.c_char * 48)]
+                ("nontemporal", _i32), ("xcd_remap", _i32), ("groups_per_cu", _i32), ("name", ctypes.c_char * 48)]
 
 
 _lib.ssu_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_vp)]
@@ -128,7 +128,7 @@ def tiles():
             raise SSUError(st, "ssu_tile_info")
         out.append(dict(id=i, dstate=d.dstate, rows_per_wave=d.rows_per_wave, waves=d.waves,
                         rows_per_group=d.rows_per_group, nontemporal=d.nontemporal,
-                        xcd_remap=d.xcd_remap, name=d.name.decode()))
+                        xcd_remap=d.xcd_remap, groups_per_cu=d.groups_per_cu, name=d.name.decode()))
     return out
 
 

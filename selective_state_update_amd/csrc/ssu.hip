@@ -7,7 +7,7 @@
 // b and head h, gather the fp32 state slot idx[b], advance it by one token in
 // place, and emit out[b,h,:] in bf16. The page calls the kernel memory bound:
 // every step reads and writes each request's fp32 state once, and a launch
-// with too few loads in flight per thread leaves HBM bandwidth unused.
+// that gives each thread little state to move cannot keep HBM busy.
 //
 // Kernel design (gfx950, wave64):
 //   * One workgroup owns `rows_per_group` consecutive state rows p of one
@@ -34,7 +34,9 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cstdarg>
+#include <initializer_list>
 #include <cstdint>
 #include <cstdio>
 #include <cstdlib>
@@ -84,6 +86,17 @@ __device__ __forceinline__ uint16_t bf16_round(float f)
         return static_cast<uint16_t>((u >> 16) | 0x40u);
     u += 0x7fffu + ((u >> 16) & 1u);
     return static_cast<uint16_t>(u >> 16);
+}
+
+// Read-only operands (slot ids, dt, dt_bias, A, D, x) are never written while
+// the kernel runs (the ABI forbids aliasing them with the state or out), so
+// they are read through the constant address space: at a uniform address the
+// compiler can then always use the scalar cache, even after the loop's state
+// stores, and waiting for them never waits on the vector-memory counter.
+template <typename T>
+__device__ __forceinline__ T load_ro(const T *ptr)
+{
+    return *(const __attribute__((address_space(4))) T *)(ptr);
 }
 
 template <int CTRL>
@@ -139,158 +152,187 @@ __device__ __forceinline__ int xcd_order(int g, int total)
     return (g & 7) * q + (g >> 3);
 }
 
+// One lane's share of one tile: `rows_per_group` consecutive state rows of one
+// (request, head), split over the workgroup's waves (R row groups of RPI rows
+// per wave). fetch() requests every operand the lane needs; finish() waits for
+// them, updates the state in registers, writes it back and emits out.
+template <int N, int R, bool NT>
+struct Work {
+    static constexpr int VEC = N > 128 ? N / 128 : 1;  // 16-byte chunks per lane per row
+    static constexpr int LPR = N / (4 * VEC);          // lanes per row
+    static constexpr int RPI = 64 / LPR;               // rows per wave instruction
+    static constexpr int ROWS_WAVE = RPI * R;
+    static_assert(LPR >= 4 && LPR <= 32, "dstate");
+
+    bool live;
+    int b, h, c, sub, p0;
+    float *sp;
+    int64_t jstep;
+    u32x2 Bw[VEC], Cw[VEC];
+    f32x4 s[R][VEC];
+    uint32_t dtbits;
+    float bias, Ah, Dh;
+    uint32_t xbits[R];
+
+    // graw: workgroup-order tile id (>= total_groups: nothing to do).
+    __device__ __forceinline__ void fetch(const Params &p, int graw, int rows_group, int wave, int lane)
+    {
+        if (graw >= p.total_groups) {
+            live = false;
+            return;
+        }
+        const int g = p.xcd_remap ? xcd_order(graw, p.total_groups) : graw;
+        const int t = g % p.ptiles;
+        const int bh = g / p.ptiles;
+        h = bh % p.nheads;
+        b = bh / p.nheads;
+        c = lane % LPR;    // column chunk
+        sub = lane / LPR;  // row within one instruction
+        const int wrow = t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
+        p0 = wrow + sub;
+
+        // This lane's columns of B and C: 8-byte vector loads that do not
+        // depend on the slot, issued first (vector-memory counters retire in
+        // order, so anything issued after the state stream could only be used
+        // after it).
+        const int grp = h / p.heads_per_group;
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + grp * p.B_g + 4 * c + 128 * v);
+            Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + grp * p.C_g + 4 * c + 128 * v);
+        }
+
+        const int64_t slot = p.idx64 ? load_ro(static_cast<const int64_t *>(p.idx) + b)
+                                     : static_cast<int64_t>(load_ro(static_cast<const int32_t *>(p.idx) + b));
+        live = slot >= 0 && slot < p.pool_slots;
+        if (!live)
+            return;  // padding entry: no state traffic, out rows untouched
+
+        // State loads: all R * VEC dwordx4 of this lane are requested up front.
+        sp = p.state + slot * p.s_slot + h * p.s_head + static_cast<int64_t>(p0) * p.s_row + 4 * c;
+        jstep = static_cast<int64_t>(RPI) * p.s_row;
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+                s[j][v] = load4<NT>(sp + j * jstep + 128 * v);
+
+        // Per-(b,h) scalars through the scalar cache, while the state is in
+        // flight; dt is read as the aligned 32-bit word that holds it.
+        const int64_t dte = b * p.dt_b + h * p.dt_h + p.dt_off;
+        const uint32_t dtw = load_ro(p.dt_words + (dte >> 1));
+        dtbits = (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu);
+        bias = p.dt_bias ? load_ro(p.dt_bias + h * p.dtb_h) : 0.0f;
+        Ah = load_ro(p.A + h * p.A_h);
+        Dh = p.D ? load_ro(p.D + h * p.D_h) : 0.0f;
+
+        // x of this lane's rows wrow + sub + j*RPI. With two rows per
+        // instruction the wave's rows are R whole 32-bit words at a uniform
+        // address (scalar load); otherwise each lane reads its own values.
+        const uint16_t *xrow = p.x + b * p.x_b + h * p.x_h + wrow;
+        if constexpr (RPI == 2) {
+            const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
+            const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                xbits[j] = (load_ro(xw + j) << sh) & 0xffff0000u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
+        }
+    }
+
+    __device__ __forceinline__ void finish(const Params &p)
+    {
+        // Per-(b,h) discretisation.
+        const float u = __uint_as_float(dtbits << 16) + bias;
+        const float delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
+        const float dA = expf(Ah * delta);
+
+        float Bv[VEC][4], Cv[VEC][4];
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            Bv[v][0] = __uint_as_float(Bw[v].x << 16);
+            Bv[v][1] = __uint_as_float(Bw[v].x & 0xffff0000u);
+            Bv[v][2] = __uint_as_float(Bw[v].y << 16);
+            Bv[v][3] = __uint_as_float(Bw[v].y & 0xffff0000u);
+            Cv[v][0] = __uint_as_float(Cw[v].x << 16);
+            Cv[v][1] = __uint_as_float(Cw[v].x & 0xffff0000u);
+            Cv[v][2] = __uint_as_float(Cw[v].y << 16);
+            Cv[v][3] = __uint_as_float(Cw[v].y & 0xffff0000u);
+        }
+        float xv[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            xv[j] = __uint_as_float(xbits[j]);
+
+        // Update in registers, write back, and form each lane's partial output.
+        float y[R];
+#pragma unroll
+        for (int j = 0; j < R; ++j) {
+            const float dx = delta * xv[j];
+            float acc = 0.0f;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v) {
+                f32x4 &q = s[j][v];
+                q.x = fmaf(q.x, dA, dx * Bv[v][0]);
+                q.y = fmaf(q.y, dA, dx * Bv[v][1]);
+                q.z = fmaf(q.z, dA, dx * Bv[v][2]);
+                q.w = fmaf(q.w, dA, dx * Bv[v][3]);
+                acc = (v == 0) ? q.x * Cv[v][0] : fmaf(q.x, Cv[v][0], acc);
+                acc = fmaf(q.y, Cv[v][1], acc);
+                acc = fmaf(q.z, Cv[v][2], acc);
+                acc = fmaf(q.w, Cv[v][3], acc);
+            }
+            y[j] = acc;
+#pragma unroll
+            for (int v = 0; v < VEC; ++v)
+                store4<NT>(sp + j * jstep + 128 * v, s[j][v]);
+        }
+
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            y[j] = group_sum<LPR>(y[j]);
+
+        // Lane c of each row group writes row (k + c) of its R rows, so one
+        // store instruction covers up to LPR rows per sub-row.
+        uint16_t *op = p.out + b * p.o_b + h * p.o_h + p0;
+#pragma unroll
+        for (int k = 0; k < R; k += LPR) {
+            float yo = y[k], xo = xv[k];
+#pragma unroll
+            for (int j = k + 1; j < R && j < k + LPR; ++j)
+                if (c == j - k) {
+                    yo = y[j];
+                    xo = xv[j];
+                }
+            if (c < R - k)
+                op[(k + c) * RPI] = bf16_round(fmaf(Dh, xo, yo));
+        }
+    }
+};
+
+// One workgroup per tile.
 template <int N, int R, int W, bool NT>
 __global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
 {
-    constexpr int VEC = N > 128 ? N / 128 : 1;  // 16-byte chunks per lane per row
-    constexpr int LPR = N / (4 * VEC);          // lanes per row
-    constexpr int RPI = 64 / LPR;               // rows per wave instruction
-    constexpr int ROWS_WAVE = RPI * R;
-    constexpr int ROWS_GROUP = ROWS_WAVE * W;
-    static_assert(LPR >= 4 && LPR <= 32, "dstate");
-
-    int g = static_cast<int>(blockIdx.x);
-    if (p.xcd_remap)
-        g = xcd_order(g, p.total_groups);
-    const int t = g % p.ptiles;
-    const int bh = g / p.ptiles;
-    const int h = bh % p.nheads;
-    const int b = bh / p.nheads;
-
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
-    const int c = lane % LPR;    // column chunk
-    const int sub = lane / LPR;  // row within one instruction
-    const int wrow = t * ROWS_GROUP + wave * ROWS_WAVE;  // first row of this wave (uniform)
-    const int p0 = wrow + sub;
-
-    // This lane's columns of B and C: 8-byte vector loads that do not depend
-    // on the slot, issued first (vector-memory counters retire in order, so
-    // anything issued after the state stream could only be used after it).
-    const int grp = h / p.heads_per_group;
-    u32x2 Bw[VEC], Cw[VEC];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + grp * p.B_g + 4 * c + 128 * v);
-        Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + grp * p.C_g + 4 * c + 128 * v);
-    }
-
-    const int64_t slot = p.idx64 ? static_cast<const int64_t *>(p.idx)[b]
-                                 : static_cast<int64_t>(static_cast<const int32_t *>(p.idx)[b]);
-    if (slot < 0 || slot >= p.pool_slots)
-        return;  // padding entry: no state traffic, out rows untouched
-
-    // State loads: R * VEC dwordx4 per lane in flight.
-    float *sp = p.state + slot * p.s_slot + h * p.s_head + static_cast<int64_t>(p0) * p.s_row + 4 * c;
-    const int64_t jstep = static_cast<int64_t>(RPI) * p.s_row;
-    f32x4 s[R][VEC];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-#pragma unroll
-        for (int v = 0; v < VEC; ++v)
-            s[j][v] = load4<NT>(sp + j * jstep + 128 * v);
-
-    // Per-(b,h) scalars through the scalar cache, while the state is in
-    // flight; dt is read as the aligned 32-bit word that holds it.
-    const int64_t dte = b * p.dt_b + h * p.dt_h + p.dt_off;
-    const uint32_t dtw = p.dt_words[dte >> 1];
-    const uint32_t dtbits = (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu);
-    const float bias = p.dt_bias ? p.dt_bias[h * p.dtb_h] : 0.0f;
-    const float Ah = p.A[h * p.A_h];
-    const float Dh = p.D ? p.D[h * p.D_h] : 0.0f;
-
-    // x of this lane's rows wrow + sub + j*RPI. With two rows per instruction
-    // the wave's rows are R whole 32-bit words at a uniform address (scalar
-    // load); otherwise each lane reads its own values.
-    uint32_t xbits[R];
-    const uint16_t *xrow = p.x + b * p.x_b + h * p.x_h + wrow;
-    if constexpr (RPI == 2) {
-        const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
-        const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            xbits[j] = (xw[j] << sh) & 0xffff0000u;
-    } else {
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
-    }
-
-    // Per-(b,h) discretisation, while the state is in flight.
-    const float u = __uint_as_float(dtbits << 16) + bias;
-    const float delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
-    const float dA = expf(Ah * delta);
-
-    float Bv[VEC][4], Cv[VEC][4];
-#pragma unroll
-    for (int v = 0; v < VEC; ++v) {
-        Bv[v][0] = __uint_as_float(Bw[v].x << 16);
-        Bv[v][1] = __uint_as_float(Bw[v].x & 0xffff0000u);
-        Bv[v][2] = __uint_as_float(Bw[v].y << 16);
-        Bv[v][3] = __uint_as_float(Bw[v].y & 0xffff0000u);
-        Cv[v][0] = __uint_as_float(Cw[v].x << 16);
-        Cv[v][1] = __uint_as_float(Cw[v].x & 0xffff0000u);
-        Cv[v][2] = __uint_as_float(Cw[v].y << 16);
-        Cv[v][3] = __uint_as_float(Cw[v].y & 0xffff0000u);
-    }
-    float xv[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-        xv[j] = __uint_as_float(xbits[j]);
-
-    // Update in registers, write back, and form each lane's partial output.
-    float y[R];
-#pragma unroll
-    for (int j = 0; j < R; ++j) {
-        const float dx = delta * xv[j];
-        float acc = 0.0f;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            f32x4 &q = s[j][v];
-            q.x = fmaf(q.x, dA, dx * Bv[v][0]);
-            q.y = fmaf(q.y, dA, dx * Bv[v][1]);
-            q.z = fmaf(q.z, dA, dx * Bv[v][2]);
-            q.w = fmaf(q.w, dA, dx * Bv[v][3]);
-            acc = (v == 0) ? q.x * Cv[v][0] : fmaf(q.x, Cv[v][0], acc);
-            acc = fmaf(q.y, Cv[v][1], acc);
-            acc = fmaf(q.z, Cv[v][2], acc);
-            acc = fmaf(q.w, Cv[v][3], acc);
-        }
-        y[j] = acc;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v)
-            store4<NT>(sp + j * jstep + 128 * v, s[j][v]);
-    }
-
-#pragma unroll
-    for (int j = 0; j < R; ++j)
-        y[j] = group_sum<LPR>(y[j]);
-
-    // Lane c of each row group writes row (k + c) of its R rows, so one store
-    // instruction covers up to LPR rows per sub-row.
-    uint16_t *op = p.out + b * p.o_b + h * p.o_h + p0;
-#pragma unroll
-    for (int k = 0; k < R; k += LPR) {
-        float yo = y[k], xo = xv[k];
-#pragma unroll
-        for (int j = k + 1; j < R && j < k + LPR; ++j)
-            if (c == j - k) {
-                yo = y[j];
-                xo = xv[j];
-            }
-        if (c < R - k)
-            op[(k + c) * RPI] = bf16_round(fmaf(Dh, xo, yo));
-    }
+    Work<N, R, NT> w;
+    w.fetch(p, static_cast<int>(blockIdx.x), Work<N, R, NT>::ROWS_WAVE * W, wave, lane);
+    if (w.live)
+        w.finish(p);
 }
 
 // ------------------------------------------------------------------ tiles --
 
-using LaunchFn = hipError_t (*)(const Params &, int grid, hipStream_t);
+using LaunchFn = hipError_t (*)(const Params &, int grid, size_t lds_bytes, hipStream_t);
 
 template <int N, int R, int W, bool NT>
-hipError_t launch(const Params &p, int grid, hipStream_t stream)
+hipError_t launch(const Params &p, int grid, size_t lds_bytes, hipStream_t stream)
 {
-    hipLaunchKernelGGL((ssu_decode_kernel<N, R, W, NT>), dim3(grid), dim3(64 * W), 0, stream, p);
+    hipLaunchKernelGGL((ssu_decode_kernel<N, R, W, NT>), dim3(grid), dim3(64 * W), lds_bytes, stream, p);
     return hipGetLastError();
 }
 
@@ -300,7 +342,7 @@ struct Tile {
 };
 
 template <int N, int R, int W, bool NT>
-void add_tile(std::vector<Tile> &v, int remap)
+void add_tile(std::vector<Tile> &v, int remap, int cap)
 {
     constexpr int VEC = N > 128 ? N / 128 : 1;
     constexpr int RPI = 64 / (N / (4 * VEC));
@@ -311,58 +353,69 @@ void add_tile(std::vector<Tile> &v, int remap)
     t.d.rows_per_group = RPI * R * W;
     t.d.nontemporal = NT ? 1 : 0;
     t.d.xcd_remap = remap;
-    std::snprintf(t.d.name, sizeof t.d.name, "n%d_r%d_w%d%s%s", N, RPI * R, W, NT ? "_nt" : "",
-                  remap ? "_xcd" : "");
+    t.d.groups_per_cu = cap;
+    char capname[16] = "";
+    if (cap > 0)
+        std::snprintf(capname, sizeof capname, "_g%d", cap);
+    std::snprintf(t.d.name, sizeof t.d.name, "n%d_r%d_w%d%s%s%s", N, RPI * R, W, NT ? "_nt" : "",
+                  remap ? "_xcd" : "", capname);
     t.fn = &launch<N, R, W, NT>;
     v.push_back(t);
 }
 
+// Every kernel in both workgroup orders, uncapped; non-temporal kernels also
+// XCD-ordered with each residency cap in `caps` (workgroups per CU).
 template <int N, int R, int W, bool NT>
-void add_both(std::vector<Tile> &v)
+void add_kernel(std::vector<Tile> &v, std::initializer_list<int> caps)
 {
-    add_tile<N, R, W, NT>(v, 1);
-    add_tile<N, R, W, NT>(v, 0);
-}
-
-// Tiles for the other dstate values: non-temporal only (the measured winner
-// for the state stream at N = 128), both workgroup orders.
-template <int N>
-void add_general(std::vector<Tile> &v)
-{
-    add_both<N, 1, 1, true>(v);
-    add_both<N, 1, 2, true>(v);
-    add_both<N, 1, 4, true>(v);
-    add_both<N, 2, 1, true>(v);
-    add_both<N, 2, 2, true>(v);
-    add_both<N, 2, 4, true>(v);
-    add_both<N, 4, 1, true>(v);
-    add_both<N, 4, 2, true>(v);
-    add_both<N, 4, 4, true>(v);
-    add_both<N, 8, 1, true>(v);
-    add_both<N, 8, 2, true>(v);
-    add_both<N, 8, 4, true>(v);
+    add_tile<N, R, W, NT>(v, 1, 0);
+    add_tile<N, R, W, NT>(v, 0, 0);
+    if (NT)
+        for (int cap : caps)
+            add_tile<N, R, W, NT>(v, 1, cap);
 }
 
 template <bool NT>
 void add_n128(std::vector<Tile> &v)
 {
-    add_both<128, 1, 1, NT>(v);
-    add_both<128, 1, 2, NT>(v);
-    add_both<128, 1, 4, NT>(v);
-    add_both<128, 1, 8, NT>(v);
-    add_both<128, 2, 1, NT>(v);
-    add_both<128, 2, 2, NT>(v);
-    add_both<128, 2, 4, NT>(v);
-    add_both<128, 2, 8, NT>(v);
-    add_both<128, 4, 1, NT>(v);
-    add_both<128, 4, 2, NT>(v);
-    add_both<128, 4, 4, NT>(v);
-    add_both<128, 4, 8, NT>(v);
-    add_both<128, 8, 1, NT>(v);
-    add_both<128, 8, 2, NT>(v);
-    add_both<128, 8, 4, NT>(v);
-    add_both<128, 16, 1, NT>(v);
-    add_both<128, 16, 2, NT>(v);
+    const std::initializer_list<int> caps = {2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
+    add_kernel<128, 1, 1, NT>(v, caps);
+    add_kernel<128, 1, 2, NT>(v, caps);
+    add_kernel<128, 1, 4, NT>(v, caps);
+    add_kernel<128, 1, 8, NT>(v, caps);
+    add_kernel<128, 2, 1, NT>(v, caps);
+    add_kernel<128, 2, 2, NT>(v, caps);
+    add_kernel<128, 2, 4, NT>(v, caps);
+    add_kernel<128, 2, 8, NT>(v, caps);
+    add_kernel<128, 4, 1, NT>(v, caps);
+    add_kernel<128, 4, 2, NT>(v, caps);
+    add_kernel<128, 4, 4, NT>(v, caps);
+    add_kernel<128, 4, 8, NT>(v, caps);
+    add_kernel<128, 8, 1, NT>(v, caps);
+    add_kernel<128, 8, 2, NT>(v, caps);
+    add_kernel<128, 8, 4, NT>(v, caps);
+    add_kernel<128, 16, 1, NT>(v, caps);
+    add_kernel<128, 16, 2, NT>(v, caps);
+}
+
+// Tiles for the other dstate values: non-temporal only (the measured winner
+// for the state stream at N = 128).
+template <int N>
+void add_general(std::vector<Tile> &v)
+{
+    const std::initializer_list<int> caps = {6, 12};
+    add_kernel<N, 1, 1, true>(v, caps);
+    add_kernel<N, 1, 2, true>(v, caps);
+    add_kernel<N, 1, 4, true>(v, caps);
+    add_kernel<N, 2, 1, true>(v, caps);
+    add_kernel<N, 2, 2, true>(v, caps);
+    add_kernel<N, 2, 4, true>(v, caps);
+    add_kernel<N, 4, 1, true>(v, caps);
+    add_kernel<N, 4, 2, true>(v, caps);
+    add_kernel<N, 4, 4, true>(v, caps);
+    add_kernel<N, 8, 1, true>(v, caps);
+    add_kernel<N, 8, 2, true>(v, caps);
+    add_kernel<N, 8, 4, true>(v, caps);
 }
 
 const std::vector<Tile> &tiles()
@@ -380,12 +433,26 @@ const std::vector<Tile> &tiles()
     return table;
 }
 
-int find_tile(int N, int rows_per_group, int waves, int nt, int remap)
+// Dynamic LDS that caps residency at `cap` workgroups per CU: the largest
+// 512-byte multiple (the LDS allocation granule) not above lds_cu / cap and the
+// per-workgroup limit. The kernel never touches this LDS; it only keeps more
+// workgroups from fitting on a CU.
+size_t lds_for_cap(int cap, int lds_cu, int lds_block)
+{
+    if (cap <= 0 || lds_cu <= 0)
+        return 0;
+    size_t b = (static_cast<size_t>(lds_cu) / cap) & ~static_cast<size_t>(511);
+    if (lds_block > 0 && b > static_cast<size_t>(lds_block))
+        b = static_cast<size_t>(lds_block) & ~static_cast<size_t>(511);
+    return b;
+}
+
+int find_tile(int N, int rows_per_group, int waves, int nt, int remap, int cap)
 {
     const auto &t = tiles();
     for (size_t i = 0; i < t.size(); ++i)
         if (t[i].d.dstate == N && t[i].d.rows_per_group == rows_per_group && t[i].d.waves == waves &&
-            t[i].d.nontemporal == nt && t[i].d.xcd_remap == remap)
+            t[i].d.nontemporal == nt && t[i].d.xcd_remap == remap && t[i].d.groups_per_cu == cap)
             return static_cast<int>(i);
     return -1;
 }
@@ -403,6 +470,34 @@ namespace {
 
 thread_local char g_err[256] = "";
 
+// Per-device LDS sizes, queried once per device (host attribute queries only).
+struct DeviceLimits {
+    int lds_cu, lds_block, cus;
+};
+
+DeviceLimits device_limits(int dev)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> lds_cu[kMaxDevices];
+    static std::atomic<int> lds_block[kMaxDevices];
+    static std::atomic<int> cu_count[kMaxDevices];
+    if (dev < 0 || dev >= kMaxDevices)
+        return {0, 0, 0};
+    int cu = lds_cu[dev].load(std::memory_order_acquire);
+    int blk = lds_block[dev].load(std::memory_order_acquire);
+    int n = cu_count[dev].load(std::memory_order_acquire);
+    if (cu <= 0 || blk <= 0 || n <= 0) {
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+            return {0, 0, 0};
+        lds_cu[dev].store(cu, std::memory_order_release);
+        lds_block[dev].store(blk, std::memory_order_release);
+        cu_count[dev].store(n, std::memory_order_release);
+    }
+    return {cu, blk, n};
+}
+
 ssu_status fail(ssu_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
 ssu_status fail(ssu_status s, const char *fmt, ...)
 {
@@ -415,15 +510,17 @@ ssu_status fail(ssu_status s, const char *fmt, ...)
 
 bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
-// The launch configuration for `batch` requests. Measured on MI355X (tile
-// sweep over every compiled configuration at H16 P64 N128, batches 8, 128 and
-// 512, cold state): non-temporal state access plus XCD-ordered workgroups win
-// at every batch, and two dwordx4 state loads per lane with four waves per
-// workgroup is best or within 0.5% of best (512: 88.6 us; 128: 24.9 us; 8:
-// 3.19 us). More loads per lane lowers occupancy and loses; one load per lane
-// loses more. So: two loads per lane (R = 2 / VEC), the most waves (4, 2, 1)
-// that still give the chip `target_groups` workgroups, else the smallest
-// groups that fit P.
+// The launch configuration for `batch` requests, from tile sweeps on MI355X
+// (every compiled configuration, H16 P64 N128, batches 8 to 512, cold state).
+// Non-temporal access and XCD-ordered workgroups win everywhere. What matters
+// next is how much state is in flight per CU: about 40-48 KiB is best; a full
+// CU (32 waves x 2 KiB) congests the memory system, and fewer bytes leave it
+// idle. So, by state bytes per call:
+//   >= 32 MiB: one-wave groups, four dwordx4 loads per lane, at most 12
+//              groups per CU (batch 512: 85.6 us against 88.5 us uncapped;
+//              best or within 0.6% of best from batch 64 up);
+//   smaller:   two loads per lane, the most waves (4, 2, 1) that still give
+//              the chip 1024 workgroups, uncapped (batch 8: 3.18 us).
 int select_tile(const ssu_config &c, int32_t batch)
 {
     using namespace ssu;
@@ -431,16 +528,27 @@ int select_tile(const ssu_config &c, int32_t batch)
     const int P = c.headdim, N = c.dstate;
     const int vec = N > 128 ? N / 128 : 1;
     const int rpi = 64 / (N / (4 * vec));
+    const int64_t state_bytes = units * P * N * 4;
+    auto pick = [&](int loads_per_lane, int W, int cap) -> int {
+        const int R = loads_per_lane / vec > 0 ? loads_per_lane / vec : 1;
+        const int rows_group = rpi * R * W;
+        if (rows_group > P || P % rows_group)
+            return -1;
+        return find_tile(N, rows_group, W, 1, 1, cap);
+    };
+    if (state_bytes >= (int64_t(32) << 20)) {
+        const int id = pick(4, 1, 12);
+        if (id >= 0)
+            return id;
+    }
     const int64_t target_groups = 1024;
     int fallback = -1;
-    for (int R : {2 / vec > 0 ? 2 / vec : 1, 1}) {
+    for (int loads : {2, 1}) {
         for (int W : {4, 2, 1}) {
-            const int rows_group = rpi * R * W;
-            if (rows_group > P || P % rows_group)
-                continue;
-            const int id = find_tile(N, rows_group, W, 1, 1);
+            const int id = pick(loads, W, 0);
             if (id < 0)
                 continue;
+            const int rows_group = ssu::tiles()[id].d.rows_per_group;
             if (units * (P / rows_group) >= target_groups)
                 return id;
             fallback = id;  // keep shrinking: smaller groups give more of them
@@ -680,7 +788,18 @@ ssu_status ssu_update(const ssu_handle *hd, const ssu_args *a, hipStream_t strea
         if (prev != c.device && hipSetDevice(c.device) != hipSuccess)
             return fail(SSU_ERR_HIP, "hipSetDevice(%d) failed", c.device);
     }
-    const hipError_t e = T.fn(p, static_cast<int>(groups), stream);
+    size_t lds = 0;
+    const int64_t grid = groups;
+    if (T.d.groups_per_cu > 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess)
+            return fail(SSU_ERR_HIP, "hipGetDevice failed");
+        const DeviceLimits lim = device_limits(dev);
+        if (lim.lds_cu <= 0)
+            return fail(SSU_ERR_HIP, "cannot query the LDS size of device %d", dev);
+        lds = ssu::lds_for_cap(T.d.groups_per_cu, lim.lds_cu, lim.lds_block);
+    }
+    const hipError_t e = T.fn(p, static_cast<int>(grid), lds, stream);
     if (c.device >= 0 && prev != c.device)
         (void)hipSetDevice(prev);
     if (e != hipSuccess)

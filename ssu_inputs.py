@@ -10,7 +10,7 @@ The shapes and distributions follow the kernel workload of sglang PR #41223
 ("[Perf] Mamba2 selective_state_update up to 2x faster on B200 via 8x1 launch
 config for dstate 128"), section "Kernel measurement": a state pool
 [pool, H, 64, 128] fp32 addressed through random state_batch_indices, x
-[bs, H, 64] and B/C [bs, 1, 128] as strided views of one bf16 tensor, and
+[bs, H, 64] and B/C [bs, 1, 128] as views into one packed bf16 tensor, and
 dt/A/D/dt_bias broadcast per head. Section "Model" of the same page gives the
 per-rank shape (16 heads, headdim 64, dstate 128, fp32 SSM cache).
 

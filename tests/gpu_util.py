@@ -39,7 +39,7 @@ def bits(t) -> np.ndarray:
 
 class DeviceProblem:
     """Device copies of a Problem's operands, laid out as the kernel workload
-    describes them: x/B/C as strided views of one packed bf16 tensor, per-head
+    describes them: x/B/C as views into one packed bf16 tensor, per-head
     parameters as [H] tensors (broadcast with stride 0 by the binding)."""
 
     def __init__(self, p: si.Problem, device="cuda", pool=None):

@@ -62,7 +62,7 @@ def test_struct_layout_matches_header(ssu):
     assert ctypes.sizeof(ssu.View) == 8 + 4 + 4 + 32
     assert ctypes.sizeof(ssu.Config) == 8 * 4
     assert ctypes.sizeof(ssu.Args) == 16 + 10 * ctypes.sizeof(ssu.View)
-    assert ctypes.sizeof(ssu.TileDesc) == 6 * 4 + 48
+    assert ctypes.sizeof(ssu.TileDesc) == 7 * 4 + 48
 
 
 def _create(ssu, **kw):
@@ -126,6 +126,7 @@ def test_tiles_are_described(ssu):
     assert len(set(names)) == len(names)
     for x in t:
         assert x["rows_per_group"] == x["rows_per_wave"] * x["waves"]
+        assert x["groups_per_cu"] == 0 or (x["nontemporal"] and x["xcd_remap"])
         assert x["dstate"] in (16, 32, 64, 128, 256)
     d = ssu.TileDesc()
     assert ssu._lib.ssu_tile_info(len(t), ctypes.byref(d)) == 1
