@@ -409,6 +409,56 @@ def run_copy_ceiling(a):
               f"({100 * moved / us / 1e3 / HBM_PEAK_GBS:.1f}% of 8 TB/s)", flush=True)
 
 
+def tokens_bytes(H, P, N, G, batch, K):
+    """Bytes of one K-token call: the state read and written once, then K
+    tokens' x, B, C, dt and out, plus idx and the per-head parameters."""
+    per_token = 2 * batch * H * P + 4 * batch * G * N + 2 * batch * H + 2 * batch * H * P
+    return 8 * batch * H * P * N + K * per_token + 4 * batch + 12 * H
+
+
+def run_tokens(a):
+    """K decode tokens per request in one launch (ssu_update_tokens) at the
+    chosen workload, same rotation method; one line per K."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    w = WORKLOADS[a.config]
+    H, P, N, G, bs = w["H"], w["P"], w["N"], w["G"], w["batch"]
+    out = open(a.out, "w") if a.out else sys.stdout
+    print("tokens us_per_call us_per_token GBps pct_peak tokens_per_s", file=out, flush=True)
+    for K in [int(k) for k in a.tokens.split(",")]:
+        rot = Rotation(H, P, N, G, bs, seed=a.config)
+        h = ssu.Handle(H, P, N, G, True, a.tile)
+        args = []
+        for s in rot.sets:
+            p = s["problem"]
+            rng = np.random.Generator(np.random.PCG64([a.config, K]))
+            xbc = torch.from_numpy(si.bf16_bits(rng.standard_normal((bs, K, p.xbc.shape[1]), dtype=np.float32))
+                                   .view(np.int16)).view(torch.bfloat16).cuda()
+            row = xbc.shape[2]
+            dt = torch.from_numpy(si.bf16_bits(rng.standard_normal((bs, K, H), dtype=np.float32))
+                                  .view(np.int16)).view(torch.bfloat16).cuda()
+            o = torch.empty((bs, K, H, P), dtype=torch.bfloat16, device="cuda")
+            s["tok"] = (xbc, dt, o)
+            args.append(h.make_tokens_args(
+                rot.pool, s["idx"], xbc.as_strided((bs, K, H, P), (K * row, row, P, 1), 0),
+                xbc.as_strided((bs, K, G, N), (K * row, row, N, 1), H * P),
+                xbc.as_strided((bs, K, G, N), (K * row, row, N, 1), H * P + G * N), dt, rot.A, rot.D,
+                rot.dt_bias, o))
+        calls = max(20, rot.K)
+        g = capture(h, args, 0, calls)
+        g.replay()
+        torch.cuda.synchronize()
+        us = statistics.median([time_graph(g, 10) / (10 * calls) for _ in range(5)]) * 1e6
+        nb = tokens_bytes(H, P, N, G, bs, K)
+        gbs = nb / (us * 1e-6) / 1e9
+        print(f"{K} {us:.3f} {us / K:.3f} {gbs:.1f} {100 * gbs / HBM_PEAK_GBS:.2f} {bs * K / (us * 1e-6):.4g}",
+              file=out, flush=True)
+        del g, rot, args
+        torch.cuda.empty_cache()
+
+
 def run_counters(a):
     """Eager calls for a rocprofv3 --pmc pass: `a.steps` headline calls rotating
     over the slot sets, then a plain device copy of a known size (256 MiB read
@@ -520,6 +570,7 @@ def main():
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--tile-sweep", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true")
+    ap.add_argument("--tokens", default="", help="comma list of tokens per call (ssu_update_tokens)")
     ap.add_argument("--summarize-counters", default="")
     ap.add_argument("--write-profile", action="store_true")
     ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
@@ -537,6 +588,8 @@ def main():
         run_tile_sweep(a)
     elif a.copy_ceiling:
         run_copy_ceiling(a)
+    elif a.tokens:
+        run_tokens(a)
     elif a.sweep:
         run_sweep(a)
     else:

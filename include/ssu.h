@@ -121,6 +121,26 @@ typedef struct ssu_args {
     ssu_view state, idx, x, B, C, dt, dt_bias, A, D, out;
 } ssu_args;
 
+/* Operands of a call that advances each request by `ntokens` tokens at once
+ * (for example the draft tokens of speculative or multi-token-prediction
+ * decoding). As ssu_args, but x, B, C, dt and out carry a token axis:
+ *
+ *   x    [batch, ntokens, H, P] bf16, stride[3] == 1
+ *   B, C [batch, ntokens, G, N] bf16, stride[3] == 1
+ *   dt   [batch, ntokens, H, P] bf16, stride[3] == 0
+ *   out  [batch, ntokens, H, P] bf16, stride[3] == 1
+ *
+ * state, idx, dt_bias, A and D are as in ssu_args. Alignment rules extend to
+ * the token stride (x: 4-byte multiples; B, C: 8-byte multiples). */
+#define SSU_MAX_TOKENS 1024
+
+typedef struct ssu_tokens_args {
+    int32_t batch;      /* >= 0; 0 is a no-op */
+    int32_t ntokens;    /* 1 .. SSU_MAX_TOKENS */
+    int64_t pool_slots; /* number of slots in the state pool, >= 0 */
+    ssu_view state, idx, x, B, C, dt, dt_bias, A, D, out;
+} ssu_tokens_args;
+
 typedef struct ssu_handle ssu_handle;
 
 /* Description of one launch configuration. */
@@ -158,6 +178,15 @@ ssu_status ssu_create(const ssu_config *cfg, ssu_handle **out);
  * without launching and without reading any view. */
 ssu_status ssu_update(const ssu_handle *h, const ssu_args *args, hipStream_t stream);
 
+/* Enqueue `ntokens` decode steps per request in one launch: each request's
+ * state is read once, advanced token by token (token t uses x, B, C, dt of
+ * token t; out[:, t] is the output after token t) and written once. The
+ * result is bitwise identical to `ntokens` successive ssu_update calls with
+ * the per-token operands, at 1/ntokens of their state traffic. Same
+ * preconditions, padding rule and errors as ssu_update, plus
+ * SSU_ERR_INVALID_ARGUMENT for ntokens outside [1, SSU_MAX_TOKENS]. */
+ssu_status ssu_update_tokens(const ssu_handle *h, const ssu_tokens_args *args, hipStream_t stream);
+
 /* Release a handle. NULL is a no-op. */
 void ssu_destroy(ssu_handle *h);
 
@@ -169,6 +198,10 @@ ssu_status ssu_check_indices(const ssu_args *args, hipStream_t stream);
 /* The launch configuration ssu_update would use for `batch` requests
  * (-1 if the handle's shape has none). */
 int32_t ssu_select_tile(const ssu_handle *h, int32_t batch);
+
+/* The launch configuration ssu_update_tokens would use for `batch` requests
+ * of `ntokens` tokens (-1 if none). */
+int32_t ssu_select_tile_tokens(const ssu_handle *h, int32_t batch, int32_t ntokens);
 
 /* Number of compiled launch configurations, and their descriptions. */
 int32_t ssu_tile_count(void);

@@ -28,6 +28,7 @@ __all__ = [
     "SSUError",
     "Handle",
     "selective_state_update",
+    "TokensArgs",
     "tiles",
     "library_path",
     "abi_version",
@@ -38,7 +39,7 @@ _LIB_PATH = os.path.join(_HERE, "libssu.so")
 
 if not os.path.exists(_LIB_PATH):
     raise ImportError(
-        f"{_LIB_PATH} is not built; run `python -m selective_state_update_amd.build` "
+        f"{_LIB_PATH} is not built; run `python selective_state_update_amd/build.py` "
         "(there is no fallback implementation)"
     )
 
@@ -76,6 +77,12 @@ class Args(ctypes.Structure):
                 ("dt", View), ("dt_bias", View), ("A", View), ("D", View), ("out", View)]
 
 
+class TokensArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("ntokens", _i32), ("pool_slots", _i64),
+                ("state", View), ("idx", View), ("x", View), ("B", View), ("C", View),
+                ("dt", View), ("dt_bias", View), ("A", View), ("D", View), ("out", View)]
+
+
 class TileDesc(ctypes.Structure):
     _fields_ = [("dstate", _i32), ("rows_per_wave", _i32), ("waves", _i32), ("rows_per_group", _i32),
                 ("nontemporal", _i32), ("xcd_remap", _i32), ("groups_per_cu", _i32), ("name", ctypes.c_char * 48)]
@@ -85,12 +92,16 @@ _lib.ssu_create.argtypes = [ctypes.POINTER(Config), ctypes.POINTER(_vp)]
 _lib.ssu_create.restype = _i32
 _lib.ssu_update.argtypes = [_vp, ctypes.POINTER(Args), _vp]
 _lib.ssu_update.restype = _i32
+_lib.ssu_update_tokens.argtypes = [_vp, ctypes.POINTER(TokensArgs), _vp]
+_lib.ssu_update_tokens.restype = _i32
 _lib.ssu_destroy.argtypes = [_vp]
 _lib.ssu_destroy.restype = None
 _lib.ssu_check_indices.argtypes = [ctypes.POINTER(Args), _vp]
 _lib.ssu_check_indices.restype = _i32
 _lib.ssu_select_tile.argtypes = [_vp, _i32]
 _lib.ssu_select_tile.restype = _i32
+_lib.ssu_select_tile_tokens.argtypes = [_vp, _i32, _i32]
+_lib.ssu_select_tile_tokens.restype = _i32
 _lib.ssu_tile_count.argtypes = []
 _lib.ssu_tile_count.restype = _i32
 _lib.ssu_tile_info.argtypes = [_i32, ctypes.POINTER(TileDesc)]
@@ -189,7 +200,9 @@ class Handle:
             _lib.ssu_destroy(h)
             self._h = None
 
-    def selected_tile(self, batch: int) -> int:
+    def selected_tile(self, batch: int, ntokens: int = 1) -> int:
+        if ntokens > 1:
+            return int(_lib.ssu_select_tile_tokens(self._h, int(batch), int(ntokens)))
         return int(_lib.ssu_select_tile(self._h, int(batch)))
 
     # -- argument marshalling -------------------------------------------------
@@ -257,16 +270,66 @@ class Handle:
         a.out = _view(out, out.stride(), _dtype_tag(out, (SSU_BF16,), "out"))
         return a
 
-    def launch(self, args: Args, stream=None):
-        """Enqueue ssu_update with a prepared Args on ``stream`` (torch stream,
-        raw hipStream_t int, or None for torch's current stream)."""
+    def make_tokens_args(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None):
+        """As make_args, for several tokens per request: x [bs, T, H, P],
+        B/C [bs, T, G, N], dt [bs, T, H] (or [bs, T, H, P] with stride 0 over P),
+        out [bs, T, H, P]."""
+        H, P, N, G = self.nheads, self.headdim, self.dstate, self.ngroups
+        if x.dim() != 4 or tuple(x.shape[2:]) != (H, P):
+            raise ValueError(f"x must be [batch, tokens, {H}, {P}], got {tuple(x.shape)}")
+        bs, T = x.shape[0], x.shape[1]
+        if T < 1:
+            raise ValueError("need at least one token")
+        for name, t in (("B", B), ("C", C)):
+            if tuple(t.shape) != (bs, T, G, N):
+                raise ValueError(f"{name} must be [{bs}, {T}, {G}, {N}], got {tuple(t.shape)}")
+        if out is None or tuple(out.shape) != (bs, T, H, P):
+            raise ValueError(f"out must be [{bs}, {T}, {H}, {P}]")
+        if dt.dim() == 3 and tuple(dt.shape) == (bs, T, H):
+            dt_s = (dt.stride(0), dt.stride(1), dt.stride(2), 0)
+        elif dt.dim() == 4 and tuple(dt.shape) == (bs, T, H, P):
+            dt_s = tuple(dt.stride())
+        else:
+            raise ValueError(f"dt must be [{bs}, {T}, {H}] or [{bs}, {T}, {H}, {P}], got {tuple(dt.shape)}")
+        # token 0's views go through the one-token checks (shapes, devices, dtypes)
+        one = self.make_args(state, state_batch_indices, x[:, 0], B[:, 0], C[:, 0], dt[:, 0], A, D, dt_bias,
+                             out[:, 0])
+        a = TokensArgs()
+        a.batch, a.ntokens, a.pool_slots = bs, T, one.pool_slots
+        a.state, a.idx, a.A, a.D, a.dt_bias = one.state, one.idx, one.A, one.D, one.dt_bias
+        a.x = _view(x, x.stride(), SSU_BF16)
+        a.B = _view(B, B.stride(), SSU_BF16)
+        a.C = _view(C, C.stride(), SSU_BF16)
+        a.dt = _view(dt, dt_s, SSU_BF16)
+        a.out = _view(out, out.stride(), SSU_BF16)
+        return a
+
+    def launch(self, args, stream=None):
+        """Enqueue ssu_update (Args) or ssu_update_tokens (TokensArgs) with
+        prepared arguments on ``stream`` (torch stream, raw hipStream_t int, or
+        None for torch's current stream)."""
         if stream is None:
             stream = _torch().cuda.current_stream().cuda_stream
         elif hasattr(stream, "cuda_stream"):
             stream = stream.cuda_stream
-        st = _lib.ssu_update(self._h, ctypes.byref(args), _vp(stream))
+        if isinstance(args, TokensArgs):
+            st = _lib.ssu_update_tokens(self._h, ctypes.byref(args), _vp(stream))
+            where = "ssu_update_tokens"
+        else:
+            st = _lib.ssu_update(self._h, ctypes.byref(args), _vp(stream))
+            where = "ssu_update"
         if st != SSU_OK:
-            raise SSUError(st, "ssu_update")
+            raise SSUError(st, where)
+
+    def update_tokens(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None,
+                      stream=None):
+        """Advance ``state`` in place by x.shape[1] tokens per request in one
+        launch; returns out [bs, T, H, P] (bf16), out[:, t] after token t."""
+        if out is None:
+            out = _torch().empty(x.shape, dtype=_torch().bfloat16, device=x.device)
+        args = self.make_tokens_args(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)
+        self.launch(args, stream)
+        return out
 
     def update(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None,
                stream=None, check_indices=False):

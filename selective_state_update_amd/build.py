@@ -1,6 +1,6 @@
 """Build libssu.so (HIP, gfx950) in-tree with hipcc.
 
-    python -m selective_state_update_amd.build
+    python selective_state_update_amd/build.py
 
 The library lands next to this file, where the Python binding loads it.
 Flags: gfx950 code only; -O3; no floating-point contraction beyond the

@@ -56,14 +56,16 @@ struct Params {
     int64_t s_slot, s_head, s_row;
     const void *idx;
     int64_t pool_slots;
+    // per-token operands: strides over (request, token, head|group); the token
+    // stride is 0 for one-token calls
     const uint16_t *x;
-    int64_t x_b, x_h;
+    int64_t x_b, x_t, x_h;
     const uint16_t *B;
-    int64_t B_b, B_g;
+    int64_t B_b, B_t, B_g;
     const uint16_t *C;
-    int64_t C_b, C_g;
+    int64_t C_b, C_t, C_g;
     const uint32_t *dt_words;  // dt's base rounded down to 4 bytes
-    int64_t dt_b, dt_h, dt_off;  // dt_off: 1 if the base was 2 bytes past a word
+    int64_t dt_b, dt_t, dt_h, dt_off;  // dt_off: 1 if the base was 2 bytes past a word
     const float *dt_bias;
     int64_t dtb_h;
     const float *A;
@@ -71,9 +73,9 @@ struct Params {
     const float *D;
     int64_t D_h;
     uint16_t *out;
-    int64_t o_b, o_h;
+    int64_t o_b, o_t, o_h;
     int32_t nheads, heads_per_group, ptiles, softplus;
-    int32_t idx64, xcd_remap, total_groups, pad_;
+    int32_t idx64, xcd_remap, total_groups, ntokens;
 };
 
 // ---------------------------------------------------------------- device --
@@ -154,8 +156,10 @@ __device__ __forceinline__ int xcd_order(int g, int total)
 
 // One lane's share of one tile: `rows_per_group` consecutive state rows of one
 // (request, head), split over the workgroup's waves (R row groups of RPI rows
-// per wave). fetch() requests every operand the lane needs; finish() waits for
-// them, updates the state in registers, writes it back and emits out.
+// per wave). fetch() requests every operand the lane needs for token 0;
+// step() waits for them, advances the state in registers by one token and
+// emits that token's out; the state goes back to memory after the last token.
+// finish() is the one-token case.
 template <int N, int R, bool NT>
 struct Work {
     static constexpr int VEC = N > 128 ? N / 128 : 1;  // 16-byte chunks per lane per row
@@ -165,7 +169,7 @@ struct Work {
     static_assert(LPR >= 4 && LPR <= 32, "dstate");
 
     bool live;
-    int b, h, c, sub, p0;
+    int b, h, grp, c, sub, wrow, p0;
     float *sp;
     int64_t jstep;
     u32x2 Bw[VEC], Cw[VEC];
@@ -173,6 +177,52 @@ struct Work {
     uint32_t dtbits;
     float bias, Ah, Dh;
     uint32_t xbits[R];
+
+    // This lane's columns of B and C for token t (8-byte vector loads).
+    __device__ __forceinline__ void load_bc(const Params &p, int t)
+    {
+#pragma unroll
+        for (int v = 0; v < VEC; ++v) {
+            Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + t * p.B_t + grp * p.B_g + 4 * c + 128 * v);
+            Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + t * p.C_t + grp * p.C_g + 4 * c + 128 * v);
+        }
+    }
+
+    // dt of token t: the aligned 32-bit word that holds it.
+    __device__ __forceinline__ void load_dt(const Params &p, int t)
+    {
+        const int64_t dte = b * p.dt_b + t * p.dt_t + h * p.dt_h + p.dt_off;
+        const uint32_t dtw = load_ro(p.dt_words + (dte >> 1));
+        dtbits = (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu);
+    }
+
+    // x of this lane's rows wrow + sub + j*RPI for token t. With two rows per
+    // instruction the wave's rows are R whole 32-bit words at a uniform
+    // address (scalar loads); otherwise each lane reads its own values.
+    __device__ __forceinline__ void load_x(const Params &p, int t)
+    {
+        const uint16_t *xrow = p.x + b * p.x_b + t * p.x_t + h * p.x_h + wrow;
+        if constexpr (RPI == 2) {
+            const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
+            const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                xbits[j] = (load_ro(xw + j) << sh) & 0xffff0000u;
+        } else {
+#pragma unroll
+            for (int j = 0; j < R; ++j)
+                xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
+        }
+    }
+
+    // delta = softplus(dt + dt_bias) (or dt + dt_bias) and the decay
+    // exp(A * delta) from a bf16 dt bit pattern.
+    __device__ __forceinline__ void discretize(const Params &p, uint32_t bits, float &delta, float &dA) const
+    {
+        const float u = __uint_as_float(bits << 16) + bias;
+        delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
+        dA = expf(Ah * delta);
+    }
 
     // graw: workgroup-order tile id (>= total_groups: nothing to do).
     __device__ __forceinline__ void fetch(const Params &p, int graw, int rows_group, int wave, int lane)
@@ -186,21 +236,16 @@ struct Work {
         const int bh = g / p.ptiles;
         h = bh % p.nheads;
         b = bh / p.nheads;
+        grp = h / p.heads_per_group;
         c = lane % LPR;    // column chunk
         sub = lane / LPR;  // row within one instruction
-        const int wrow = t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
+        wrow = t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
         p0 = wrow + sub;
 
-        // This lane's columns of B and C: 8-byte vector loads that do not
-        // depend on the slot, issued first (vector-memory counters retire in
-        // order, so anything issued after the state stream could only be used
-        // after it).
-        const int grp = h / p.heads_per_group;
-#pragma unroll
-        for (int v = 0; v < VEC; ++v) {
-            Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + grp * p.B_g + 4 * c + 128 * v);
-            Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + grp * p.C_g + 4 * c + 128 * v);
-        }
+        // B and C do not depend on the slot: requested first (vector-memory
+        // counters retire in order, so anything issued after the state stream
+        // could only be used after it).
+        load_bc(p, 0);
 
         const int64_t slot = p.idx64 ? load_ro(static_cast<const int64_t *>(p.idx) + b)
                                      : static_cast<int64_t>(load_ro(static_cast<const int32_t *>(p.idx) + b));
@@ -217,39 +262,20 @@ struct Work {
             for (int v = 0; v < VEC; ++v)
                 s[j][v] = load4<NT>(sp + j * jstep + 128 * v);
 
-        // Per-(b,h) scalars through the scalar cache, while the state is in
-        // flight; dt is read as the aligned 32-bit word that holds it.
-        const int64_t dte = b * p.dt_b + h * p.dt_h + p.dt_off;
-        const uint32_t dtw = load_ro(p.dt_words + (dte >> 1));
-        dtbits = (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu);
+        // Per-head parameters and token 0's dt and x through the scalar cache,
+        // while the state is in flight.
         bias = p.dt_bias ? load_ro(p.dt_bias + h * p.dtb_h) : 0.0f;
         Ah = load_ro(p.A + h * p.A_h);
         Dh = p.D ? load_ro(p.D + h * p.D_h) : 0.0f;
-
-        // x of this lane's rows wrow + sub + j*RPI. With two rows per
-        // instruction the wave's rows are R whole 32-bit words at a uniform
-        // address (scalar load); otherwise each lane reads its own values.
-        const uint16_t *xrow = p.x + b * p.x_b + h * p.x_h + wrow;
-        if constexpr (RPI == 2) {
-            const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
-            const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
-#pragma unroll
-            for (int j = 0; j < R; ++j)
-                xbits[j] = (load_ro(xw + j) << sh) & 0xffff0000u;
-        } else {
-#pragma unroll
-            for (int j = 0; j < R; ++j)
-                xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
-        }
+        load_dt(p, 0);
+        load_x(p, 0);
     }
 
-    __device__ __forceinline__ void finish(const Params &p)
+    // Advance the state by token t with its discretisation (delta, dA);
+    // write the state back when LAST.
+    template <bool LAST>
+    __device__ __forceinline__ void step(const Params &p, int t, float delta, float dA)
     {
-        // Per-(b,h) discretisation.
-        const float u = __uint_as_float(dtbits << 16) + bias;
-        const float delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
-        const float dA = expf(Ah * delta);
-
         float Bv[VEC][4], Cv[VEC][4];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
@@ -267,7 +293,8 @@ struct Work {
         for (int j = 0; j < R; ++j)
             xv[j] = __uint_as_float(xbits[j]);
 
-        // Update in registers, write back, and form each lane's partial output.
+        // Update in registers (write back after the last token) and form each
+        // lane's partial output.
         float y[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) {
@@ -286,9 +313,11 @@ struct Work {
                 acc = fmaf(q.w, Cv[v][3], acc);
             }
             y[j] = acc;
+            if constexpr (LAST) {
 #pragma unroll
-            for (int v = 0; v < VEC; ++v)
-                store4<NT>(sp + j * jstep + 128 * v, s[j][v]);
+                for (int v = 0; v < VEC; ++v)
+                    store4<NT>(sp + j * jstep + 128 * v, s[j][v]);
+            }
         }
 
 #pragma unroll
@@ -297,7 +326,7 @@ struct Work {
 
         // Lane c of each row group writes row (k + c) of its R rows, so one
         // store instruction covers up to LPR rows per sub-row.
-        uint16_t *op = p.out + b * p.o_b + h * p.o_h + p0;
+        uint16_t *op = p.out + b * p.o_b + t * p.o_t + h * p.o_h + p0;
 #pragma unroll
         for (int k = 0; k < R; k += LPR) {
             float yo = y[k], xo = xv[k];
@@ -311,9 +340,16 @@ struct Work {
                 op[(k + c) * RPI] = bf16_round(fmaf(Dh, xo, yo));
         }
     }
+
+    __device__ __forceinline__ void finish(const Params &p)
+    {
+        float delta, dA;
+        discretize(p, dtbits, delta, dA);
+        step<true>(p, 0, delta, dA);
+    }
 };
 
-// One workgroup per tile.
+// One workgroup per tile, one token.
 template <int N, int R, int W, bool NT>
 __global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
 {
@@ -323,6 +359,53 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
     w.fetch(p, static_cast<int>(blockIdx.x), Work<N, R, NT>::ROWS_WAVE * W, wave, lane);
     if (w.live)
         w.finish(p);
+}
+
+// One workgroup per tile, p.ntokens tokens: the state is read once, advanced
+// token by token in registers with the same arithmetic as the one-token
+// kernel, and written once; each token's out is written as it is formed. The
+// operands of token t+1 are requested before token t is computed, and the
+// per-token discretisation is done 64 tokens at a time, one token per lane
+// (the same fp32 operations as the one-token kernel, so the same bits), then
+// read back with a uniform lane read.
+template <int N, int R, int W, bool NT>
+__global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params p)
+{
+    using WK = Work<N, R, NT>;
+    const int lane = static_cast<int>(threadIdx.x) & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
+    WK w;
+    w.fetch(p, static_cast<int>(blockIdx.x), WK::ROWS_WAVE * W, wave, lane);
+    if (!w.live)
+        return;
+    const int K = p.ntokens;
+    float lane_delta = 0.0f, lane_dA = 1.0f;
+    for (int t = 0; t < K; ++t) {
+        const int tl = t & 63;
+        if (tl == 0 && t + lane < K) {  // discretise tokens t .. t+63, one per lane
+            const int64_t dte = w.b * p.dt_b + (t + lane) * p.dt_t + w.h * p.dt_h + p.dt_off;
+            const uint32_t dtw = p.dt_words[dte >> 1];
+            w.discretize(p, (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu), lane_delta, lane_dA);
+        }
+        const float delta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_delta), tl));
+        const float dA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_dA), tl));
+        if (t + 1 == K) {
+            w.template step<true>(p, t, delta, dA);
+            break;
+        }
+        WK next = w;  // same tile; only the token operands are replaced below
+        next.load_bc(p, t + 1);
+        next.load_x(p, t + 1);
+        w.template step<false>(p, t, delta, dA);
+#pragma unroll
+        for (int v = 0; v < WK::VEC; ++v) {
+            w.Bw[v] = next.Bw[v];
+            w.Cw[v] = next.Cw[v];
+        }
+#pragma unroll
+        for (int j = 0; j < R; ++j)
+            w.xbits[j] = next.xbits[j];
+    }
 }
 
 // ------------------------------------------------------------------ tiles --
@@ -336,9 +419,17 @@ hipError_t launch(const Params &p, int grid, size_t lds_bytes, hipStream_t strea
     return hipGetLastError();
 }
 
+template <int N, int R, int W, bool NT>
+hipError_t launch_tokens(const Params &p, int grid, size_t lds_bytes, hipStream_t stream)
+{
+    hipLaunchKernelGGL((ssu_decode_tokens_kernel<N, R, W, NT>), dim3(grid), dim3(64 * W), lds_bytes, stream, p);
+    return hipGetLastError();
+}
+
 struct Tile {
     ssu_tile_desc d;
-    LaunchFn fn;
+    LaunchFn fn;         // one token
+    LaunchFn fn_tokens;  // several tokens
 };
 
 template <int N, int R, int W, bool NT>
@@ -360,6 +451,7 @@ void add_tile(std::vector<Tile> &v, int remap, int cap)
     std::snprintf(t.d.name, sizeof t.d.name, "n%d_r%d_w%d%s%s%s", N, RPI * R, W, NT ? "_nt" : "",
                   remap ? "_xcd" : "", capname);
     t.fn = &launch<N, R, W, NT>;
+    t.fn_tokens = &launch_tokens<N, R, W, NT>;
     v.push_back(t);
 }
 
@@ -521,7 +613,7 @@ bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n
 //              best or within 0.6% of best from batch 64 up);
 //   smaller:   two loads per lane, the most waves (4, 2, 1) that still give
 //              the chip 1024 workgroups, uncapped (batch 8: 3.18 us).
-int select_tile(const ssu_config &c, int32_t batch)
+int select_tile(const ssu_config &c, int32_t batch, int32_t ntokens)
 {
     using namespace ssu;
     const int64_t units = static_cast<int64_t>(batch) * c.nheads;  // (b, h) pairs
@@ -537,7 +629,13 @@ int select_tile(const ssu_config &c, int32_t batch)
         return find_tile(N, rows_group, W, 1, 1, cap);
     };
     if (state_bytes >= (int64_t(32) << 20)) {
-        const int id = pick(4, 1, 12);
+        // Several tokens per call make each workgroup's work longer and
+        // ALU-heavier: full occupancy hides that better than the cap, and
+        // from 4 tokens on, eight loads per lane (fewer waves repeating the
+        // per-token work) win (batch 512, 8 tokens: 129 us against 139 us
+        // with four loads uncapped and 202 us capped).
+        const int loads = ntokens >= 4 ? 8 : 4;
+        const int id = pick(loads, 1, ntokens > 1 ? 0 : 12);
         if (id >= 0)
             return id;
     }
@@ -673,123 +771,170 @@ int32_t ssu_select_tile(const ssu_handle *h, int32_t batch)
         return -1;
     if (h->forced_tile >= 0)
         return h->forced_tile;
-    return select_tile(h->cfg, batch < 1 ? 1 : batch);
+    return select_tile(h->cfg, batch < 1 ? 1 : batch, 1);
 }
 
-ssu_status ssu_update(const ssu_handle *hd, const ssu_args *a, hipStream_t stream)
+int32_t ssu_select_tile_tokens(const ssu_handle *h, int32_t batch, int32_t ntokens)
 {
-    if (!hd || !a)
-        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: null handle or args");
-    const ssu_config &c = hd->cfg;
-    if (a->batch < 0 || a->pool_slots < 0)
-        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: batch %d / pool_slots %lld negative", a->batch,
-                    static_cast<long long>(a->pool_slots));
-    if (a->reserved != 0)
-        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: reserved field must be 0");
-    if (a->batch == 0)
+    if (!h)
+        return -1;
+    if (h->forced_tile >= 0)
+        return h->forced_tile;
+    return select_tile(h->cfg, batch < 1 ? 1 : batch, ntokens < 1 ? 1 : ntokens);
+}
+
+}  // extern "C"
+
+namespace {
+
+// One call's operands in a single form: the per-token views (x, B, C, dt,
+// out) carry four strides (request, token, head or group, innermost); a
+// one-token call has token stride 0.
+struct Operands {
+    int32_t batch, ntokens;
+    int64_t pool_slots;
+    ssu_view state, idx, dt_bias, A, D;
+    ssu_view x, B, C, dt, out;
+};
+
+// [request, head|group, inner] -> [request, token (stride 0), head|group, inner]
+ssu_view with_token_axis(const ssu_view &v)
+{
+    ssu_view w = v;
+    w.stride[3] = v.stride[2];
+    w.stride[2] = v.stride[1];
+    w.stride[1] = 0;
+    return w;
+}
+
+// Restores the caller's current device on every return path.
+struct DeviceGuard {
+    int prev = -1;
+    bool switched = false;
+    ssu_status enter(int device)
+    {
+        if (device < 0)
+            return SSU_OK;
+        if (hipGetDevice(&prev) != hipSuccess)
+            return fail(SSU_ERR_HIP, "hipGetDevice failed");
+        if (prev != device) {
+            if (hipSetDevice(device) != hipSuccess)
+                return fail(SSU_ERR_HIP, "hipSetDevice(%d) failed", device);
+            switched = true;
+        }
         return SSU_OK;
+    }
+    ~DeviceGuard()
+    {
+        if (switched)
+            (void)hipSetDevice(prev);
+    }
+};
 
-    SSU_TRY(check_view(a->state, "state", SSU_F32, 4, false));
-    if (a->idx.ptr && a->idx.dtype == SSU_I64)
-        SSU_TRY(check_view(a->idx, "idx", SSU_I64, 1, false));
+ssu_status run(const ssu_handle *hd, const Operands &a, hipStream_t stream)
+{
+    const ssu_config &c = hd->cfg;
+    SSU_TRY(check_view(a.state, "state", SSU_F32, 4, false));
+    if (a.idx.ptr && a.idx.dtype == SSU_I64)
+        SSU_TRY(check_view(a.idx, "idx", SSU_I64, 1, false));
     else
-        SSU_TRY(check_view(a->idx, "idx", SSU_I32, 1, false));
-    SSU_TRY(check_view(a->x, "x", SSU_BF16, 3, false));
-    SSU_TRY(check_view(a->B, "B", SSU_BF16, 3, false));
-    SSU_TRY(check_view(a->C, "C", SSU_BF16, 3, false));
-    SSU_TRY(check_view(a->dt, "dt", SSU_BF16, 3, false));
-    SSU_TRY(check_view(a->dt_bias, "dt_bias", SSU_F32, 2, true));
-    SSU_TRY(check_view(a->A, "A", SSU_F32, 3, false));
-    SSU_TRY(check_view(a->D, "D", SSU_F32, 2, true));
-    SSU_TRY(check_view(a->out, "out", SSU_BF16, 3, false));
+        SSU_TRY(check_view(a.idx, "idx", SSU_I32, 1, false));
+    SSU_TRY(check_view(a.x, "x", SSU_BF16, 4, false));
+    SSU_TRY(check_view(a.B, "B", SSU_BF16, 4, false));
+    SSU_TRY(check_view(a.C, "C", SSU_BF16, 4, false));
+    SSU_TRY(check_view(a.dt, "dt", SSU_BF16, 4, false));
+    SSU_TRY(check_view(a.dt_bias, "dt_bias", SSU_F32, 2, true));
+    SSU_TRY(check_view(a.A, "A", SSU_F32, 3, false));
+    SSU_TRY(check_view(a.D, "D", SSU_F32, 2, true));
+    SSU_TRY(check_view(a.out, "out", SSU_BF16, 4, false));
 
-    if (a->state.stride[3] != 1)
+    if (a.state.stride[3] != 1)
         return fail(SSU_ERR_UNSUPPORTED, "state: dstate stride must be 1");
-    if (a->idx.stride[0] != 1)
+    if (a.idx.stride[0] != 1)
         return fail(SSU_ERR_UNSUPPORTED, "idx: stride must be 1");
-    if (a->x.stride[2] != 1 || a->out.stride[2] != 1)
+    if (a.x.stride[3] != 1 || a.out.stride[3] != 1)
         return fail(SSU_ERR_UNSUPPORTED, "x/out: headdim stride must be 1");
-    if (a->B.stride[2] != 1 || a->C.stride[2] != 1)
+    if (a.B.stride[3] != 1 || a.C.stride[3] != 1)
         return fail(SSU_ERR_UNSUPPORTED, "B/C: dstate stride must be 1");
-    if (a->dt.stride[2] != 0)
+    if (a.dt.stride[3] != 0)
         return fail(SSU_ERR_UNSUPPORTED, "dt: must be one value per (request, head) (headdim stride 0)");
-    if (a->dt_bias.ptr && a->dt_bias.stride[1] != 0)
+    if (a.dt_bias.ptr && a.dt_bias.stride[1] != 0)
         return fail(SSU_ERR_UNSUPPORTED, "dt_bias: headdim stride must be 0");
-    if (a->A.stride[1] != 0 || a->A.stride[2] != 0)
+    if (a.A.stride[1] != 0 || a.A.stride[2] != 0)
         return fail(SSU_ERR_UNSUPPORTED, "A: must be one value per head (headdim, dstate strides 0)");
-    if (a->D.ptr && a->D.stride[1] != 0)
+    if (a.D.ptr && a.D.stride[1] != 0)
         return fail(SSU_ERR_UNSUPPORTED, "D: headdim stride must be 0");
 
-    const uintptr_t sp = reinterpret_cast<uintptr_t>(a->state.ptr);
-    if (sp % 16 || a->state.stride[0] % 4 || a->state.stride[1] % 4 || a->state.stride[2] % 4)
+    const uintptr_t sp = reinterpret_cast<uintptr_t>(a.state.ptr);
+    if (sp % 16 || a.state.stride[0] % 4 || a.state.stride[1] % 4 || a.state.stride[2] % 4)
         return fail(SSU_ERR_MISALIGNED, "state: pointer and slot/head/row strides must be 16-byte multiples");
-    const uintptr_t xp = reinterpret_cast<uintptr_t>(a->x.ptr);
-    if (xp % 4 || a->x.stride[0] % 2 || a->x.stride[1] % 2)
-        return fail(SSU_ERR_MISALIGNED, "x: pointer and request/head strides must be 4-byte multiples");
-    for (const ssu_view *v : {&a->B, &a->C}) {
+    const uintptr_t xp = reinterpret_cast<uintptr_t>(a.x.ptr);
+    if (xp % 4 || a.x.stride[0] % 2 || a.x.stride[1] % 2 || a.x.stride[2] % 2)
+        return fail(SSU_ERR_MISALIGNED, "x: pointer and request/token/head strides must be 4-byte multiples");
+    for (const ssu_view *v : {&a.B, &a.C}) {
         const uintptr_t bp = reinterpret_cast<uintptr_t>(v->ptr);
-        if (bp % 8 || v->stride[0] % 4 || v->stride[1] % 4)
-            return fail(SSU_ERR_MISALIGNED, "B/C: pointer and request/group strides must be 8-byte multiples");
+        if (bp % 8 || v->stride[0] % 4 || v->stride[1] % 4 || v->stride[2] % 4)
+            return fail(SSU_ERR_MISALIGNED, "B/C: pointer and request/token/group strides must be 8-byte multiples");
     }
+    const uintptr_t dtp = reinterpret_cast<uintptr_t>(a.dt.ptr);
+    if (dtp % 2)
+        return fail(SSU_ERR_MISALIGNED, "dt: pointer must be 2-byte aligned");
 
-    const int32_t tile = hd->forced_tile >= 0 ? hd->forced_tile : select_tile(c, a->batch);
+    const int32_t tile = hd->forced_tile >= 0 ? hd->forced_tile : select_tile(c, a.batch, a.ntokens);
     if (tile < 0)
         return fail(SSU_ERR_UNSUPPORTED, "no launch configuration for N=%d P=%d", c.dstate, c.headdim);
     const ssu::Tile &T = ssu::tiles()[tile];
     const int ptiles = c.headdim / T.d.rows_per_group;
-    const int64_t groups = static_cast<int64_t>(a->batch) * c.nheads * ptiles;
+    const int64_t groups = static_cast<int64_t>(a.batch) * c.nheads * ptiles;
     if (groups > 0x7fffffff)
         return fail(SSU_ERR_UNSUPPORTED, "batch * heads too large for one launch");
 
     ssu::Params p{};
-    p.state = static_cast<float *>(const_cast<void *>(a->state.ptr));
-    p.s_slot = a->state.stride[0];
-    p.s_head = a->state.stride[1];
-    p.s_row = a->state.stride[2];
-    p.idx = a->idx.ptr;
-    p.idx64 = a->idx.dtype == SSU_I64;
-    p.pool_slots = a->pool_slots;
-    p.x = static_cast<const uint16_t *>(a->x.ptr);
-    p.x_b = a->x.stride[0];
-    p.x_h = a->x.stride[1];
-    p.B = static_cast<const uint16_t *>(a->B.ptr);
-    p.B_b = a->B.stride[0];
-    p.B_g = a->B.stride[1];
-    p.C = static_cast<const uint16_t *>(a->C.ptr);
-    p.C_b = a->C.stride[0];
-    p.C_g = a->C.stride[1];
-    const uintptr_t dtp = reinterpret_cast<uintptr_t>(a->dt.ptr);
-    if (dtp % 2)
-        return fail(SSU_ERR_MISALIGNED, "dt: pointer must be 2-byte aligned");
+    p.state = static_cast<float *>(const_cast<void *>(a.state.ptr));
+    p.s_slot = a.state.stride[0];
+    p.s_head = a.state.stride[1];
+    p.s_row = a.state.stride[2];
+    p.idx = a.idx.ptr;
+    p.idx64 = a.idx.dtype == SSU_I64;
+    p.pool_slots = a.pool_slots;
+    p.x = static_cast<const uint16_t *>(a.x.ptr);
+    p.x_b = a.x.stride[0];
+    p.x_t = a.x.stride[1];
+    p.x_h = a.x.stride[2];
+    p.B = static_cast<const uint16_t *>(a.B.ptr);
+    p.B_b = a.B.stride[0];
+    p.B_t = a.B.stride[1];
+    p.B_g = a.B.stride[2];
+    p.C = static_cast<const uint16_t *>(a.C.ptr);
+    p.C_b = a.C.stride[0];
+    p.C_t = a.C.stride[1];
+    p.C_g = a.C.stride[2];
     p.dt_words = reinterpret_cast<const uint32_t *>(dtp & ~uintptr_t(3));
     p.dt_off = (dtp & 2) ? 1 : 0;
-    p.dt_b = a->dt.stride[0];
-    p.dt_h = a->dt.stride[1];
-    p.dt_bias = static_cast<const float *>(a->dt_bias.ptr);
-    p.dtb_h = a->dt_bias.stride[0];
-    p.A = static_cast<const float *>(a->A.ptr);
-    p.A_h = a->A.stride[0];
-    p.D = static_cast<const float *>(a->D.ptr);
-    p.D_h = a->D.stride[0];
-    p.out = static_cast<uint16_t *>(const_cast<void *>(a->out.ptr));
-    p.o_b = a->out.stride[0];
-    p.o_h = a->out.stride[1];
+    p.dt_b = a.dt.stride[0];
+    p.dt_t = a.dt.stride[1];
+    p.dt_h = a.dt.stride[2];
+    p.dt_bias = static_cast<const float *>(a.dt_bias.ptr);
+    p.dtb_h = a.dt_bias.stride[0];
+    p.A = static_cast<const float *>(a.A.ptr);
+    p.A_h = a.A.stride[0];
+    p.D = static_cast<const float *>(a.D.ptr);
+    p.D_h = a.D.stride[0];
+    p.out = static_cast<uint16_t *>(const_cast<void *>(a.out.ptr));
+    p.o_b = a.out.stride[0];
+    p.o_t = a.out.stride[1];
+    p.o_h = a.out.stride[2];
     p.nheads = c.nheads;
     p.heads_per_group = c.nheads / c.ngroups;
     p.ptiles = ptiles;
     p.softplus = c.dt_softplus;
     p.xcd_remap = T.d.xcd_remap;
     p.total_groups = static_cast<int32_t>(groups);
+    p.ntokens = a.ntokens;
 
-    int prev = -1;
-    if (c.device >= 0) {
-        if (hipGetDevice(&prev) != hipSuccess)
-            return fail(SSU_ERR_HIP, "hipGetDevice failed");
-        if (prev != c.device && hipSetDevice(c.device) != hipSuccess)
-            return fail(SSU_ERR_HIP, "hipSetDevice(%d) failed", c.device);
-    }
+    DeviceGuard guard;
+    SSU_TRY(guard.enter(c.device));
     size_t lds = 0;
-    const int64_t grid = groups;
     if (T.d.groups_per_cu > 0) {
         int dev = 0;
         if (hipGetDevice(&dev) != hipSuccess)
@@ -799,12 +944,72 @@ ssu_status ssu_update(const ssu_handle *hd, const ssu_args *a, hipStream_t strea
             return fail(SSU_ERR_HIP, "cannot query the LDS size of device %d", dev);
         lds = ssu::lds_for_cap(T.d.groups_per_cu, lim.lds_cu, lim.lds_block);
     }
-    const hipError_t e = T.fn(p, static_cast<int>(grid), lds, stream);
-    if (c.device >= 0 && prev != c.device)
-        (void)hipSetDevice(prev);
+    const ssu::LaunchFn fn = a.ntokens > 1 ? T.fn_tokens : T.fn;
+    const hipError_t e = fn(p, static_cast<int>(groups), lds, stream);
     if (e != hipSuccess)
         return fail(SSU_ERR_HIP, "launch of %s failed: %s", T.d.name, hipGetErrorString(e));
     return SSU_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+ssu_status ssu_update(const ssu_handle *hd, const ssu_args *a, hipStream_t stream)
+{
+    if (!hd || !a)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: null handle or args");
+    if (a->batch < 0 || a->pool_slots < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: batch %d / pool_slots %lld negative", a->batch,
+                    static_cast<long long>(a->pool_slots));
+    if (a->reserved != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update: reserved field must be 0");
+    if (a->batch == 0)
+        return SSU_OK;
+    Operands o{};
+    o.batch = a->batch;
+    o.ntokens = 1;
+    o.pool_slots = a->pool_slots;
+    o.state = a->state;
+    o.idx = a->idx;
+    o.dt_bias = a->dt_bias;
+    o.A = a->A;
+    o.D = a->D;
+    o.x = with_token_axis(a->x);
+    o.B = with_token_axis(a->B);
+    o.C = with_token_axis(a->C);
+    o.dt = with_token_axis(a->dt);
+    o.out = with_token_axis(a->out);
+    return run(hd, o, stream);
+}
+
+ssu_status ssu_update_tokens(const ssu_handle *hd, const ssu_tokens_args *a, hipStream_t stream)
+{
+    if (!hd || !a)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update_tokens: null handle or args");
+    if (a->batch < 0 || a->pool_slots < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update_tokens: batch %d / pool_slots %lld negative", a->batch,
+                    static_cast<long long>(a->pool_slots));
+    if (a->ntokens < 1 || a->ntokens > SSU_MAX_TOKENS)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_update_tokens: ntokens %d outside [1, %d]", a->ntokens,
+                    SSU_MAX_TOKENS);
+    if (a->batch == 0)
+        return SSU_OK;
+    Operands o{};
+    o.batch = a->batch;
+    o.ntokens = a->ntokens;
+    o.pool_slots = a->pool_slots;
+    o.state = a->state;
+    o.idx = a->idx;
+    o.dt_bias = a->dt_bias;
+    o.A = a->A;
+    o.D = a->D;
+    o.x = a->x;
+    o.B = a->B;
+    o.C = a->C;
+    o.dt = a->dt;
+    o.out = a->out;
+    return run(hd, o, stream);
 }
 
 ssu_status ssu_check_indices(const ssu_args *a, hipStream_t stream)

@@ -272,3 +272,77 @@ def test_python_binding_validates_shapes(ssu):
         h.make_args(st, idx, x, B, B, dt, A, out=out)
     with pytest.raises(ssu.SSUError):
         ssu.Handle(2, 64, 100)
+
+
+# ---------------------------------------------------------- ssu_update_tokens --
+def _good_tokens_args(ssu, bs=4, T=3, H=16, P=64, N=128, G=1):
+    a = ssu.TokensArgs()
+    a.batch, a.ntokens, a.pool_slots = bs, T, 8
+
+    def v(off, dtype, strides):
+        x = ssu.View()
+        x.ptr = FAKE + off
+        x.dtype = dtype
+        x.reserved = 0
+        for i, s in enumerate(strides):
+            x.stride[i] = s
+        return x
+
+    row = H * P + 2 * G * N
+    a.state = v(0, ssu.SSU_F32, (H * P * N, P * N, N, 1))
+    a.idx = v(0x1000, ssu.SSU_I32, (1,))
+    a.x = v(0x2000, ssu.SSU_BF16, (T * row, row, P, 1))
+    a.B = v(0x2000 + 2 * H * P, ssu.SSU_BF16, (T * row, row, N, 1))
+    a.C = v(0x2000 + 2 * (H * P + G * N), ssu.SSU_BF16, (T * row, row, N, 1))
+    a.dt = v(0x3000, ssu.SSU_BF16, (T * H, H, 1, 0))
+    a.dt_bias = v(0x4000, ssu.SSU_F32, (1, 0))
+    a.A = v(0x5000, ssu.SSU_F32, (1, 0, 0))
+    a.D = v(0x6000, ssu.SSU_F32, (1, 0))
+    a.out = v(0x7000, ssu.SSU_BF16, (T * H * P, H * P, P, 1))
+    return a
+
+
+TOKENS_BAD = [
+    ("ntokens", 0, 1), ("ntokens", -3, 1), ("ntokens", 1025, 1),
+    ("x.stride1", 1281, 3), ("B.stride1", 1282, 3), ("dt.stride3", 1, 2), ("x.stride3", 2, 2),
+    ("out.stride3", 0, 2), ("C.stride3", 2, 2), ("x.ptr", None, 1), ("out.dtype", 0, 1),
+]
+
+
+@pytest.mark.parametrize("what,value,code", TOKENS_BAD, ids=[f"{b[0]}={b[1]}" for b in TOKENS_BAD])
+def test_update_tokens_rejects_before_launch(ssu, what, value, code):
+    st, h = _create(ssu)
+    a = _good_tokens_args(ssu)
+    if what == "ntokens":
+        a.ntokens = value
+    else:
+        field, attr = what.split(".")
+        v = getattr(a, field)
+        if attr == "ptr":
+            v.ptr = value
+        elif attr == "dtype":
+            v.dtype = value
+        else:
+            v.stride[int(attr[-1])] = value
+        setattr(a, field, v)
+    got = ssu._lib.ssu_update_tokens(h, ctypes.byref(a), None)
+    assert got == code, (got, ssu._lib.ssu_last_error())
+    ssu._lib.ssu_destroy(h)
+
+
+def test_update_tokens_batch_zero_and_nulls(ssu):
+    st, h = _create(ssu)
+    a = ssu.TokensArgs()
+    a.batch, a.ntokens = 0, 4
+    assert ssu._lib.ssu_update_tokens(h, ctypes.byref(a), None) == 0
+    assert ssu._lib.ssu_update_tokens(None, ctypes.byref(a), None) == 1
+    assert ssu._lib.ssu_update_tokens(h, None, None) == 1
+    a.batch = -1
+    assert ssu._lib.ssu_update_tokens(h, ctypes.byref(a), None) == 1
+    ssu._lib.ssu_destroy(h)
+
+
+def test_tokens_struct_layout(ssu):
+    assert ctypes.sizeof(ssu.TokensArgs) == 16 + 10 * ctypes.sizeof(ssu.View)
+    text = open(HEADER).read()
+    assert int(re.search(r"#define SSU_MAX_TOKENS (\d+)", text).group(1)) == 1024

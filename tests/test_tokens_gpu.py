@@ -1,0 +1,162 @@
+"""Several decode tokens per request in one launch (ssu_update_tokens).
+
+The fused call must be bitwise identical to the same tokens applied by
+successive one-token ssu_update calls (the per-token arithmetic is the same
+and the state stays fp32 between tokens), in every launch configuration, and
+within tolerance of the oracle's fp64 length-K scan.
+"""
+import numpy as np
+import pytest
+
+import ssu_inputs as si
+
+from . import gpu_util as gu
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+class TokenProblem:
+    """K tokens for `batch` requests: per-token xBC rows packed as
+    [batch, K, row] (x, B, C are views with a token axis), dt [batch, K, H];
+    per-head parameters and slots shared by all tokens."""
+
+    def __init__(self, H, P, N, G, batch, slots, K, seed, softplus=True, host_pool=True):
+        self.base = si.make_problem(H, P, N, G, batch, slots, seed, dt_softplus=softplus, host_pool=host_pool)
+        self.steps = []
+        for t in range(K):
+            s = si.make_problem(H, P, N, G, batch, slots, seed * 100 + t + 1, dt_softplus=softplus,
+                                host_pool=False, idx=self.base.idx)
+            s.A, s.D, s.dt_bias = self.base.A, self.base.D, self.base.dt_bias
+            self.steps.append(s)
+        self.H, self.P, self.N, self.G, self.bs, self.K = H, P, N, G, batch, K
+        self.xbc = np.stack([s.xbc for s in self.steps], axis=1)  # [bs, K, row]
+        self.dt = np.stack([s.dt for s in self.steps], axis=1)    # [bs, K, H]
+
+    def device(self, pool):
+        torch = gu.torch_mod()
+        H, P, N, G, bs, K = self.H, self.P, self.N, self.G, self.bs, self.K
+        xbc = gu.bf16_tensor(self.xbc, "cuda")
+        row = xbc.shape[2]
+        d = dict(
+            pool=pool, xbc=xbc,
+            x=xbc.as_strided((bs, K, H, P), (K * row, row, P, 1), 0),
+            B=xbc.as_strided((bs, K, G, N), (K * row, row, N, 1), H * P),
+            C=xbc.as_strided((bs, K, G, N), (K * row, row, N, 1), H * P + G * N),
+            dt=gu.bf16_tensor(self.dt, "cuda"),
+            A=torch.from_numpy(self.base.A).cuda(), D=torch.from_numpy(self.base.D).cuda(),
+            dt_bias=torch.from_numpy(self.base.dt_bias).cuda(), idx=torch.from_numpy(self.base.idx).cuda())
+        return d
+
+    def oracle(self, ref, pool_np, sample=None):
+        b = slice(None) if sample is None else sample
+        x = np.stack([s.x[b] for s in self.steps])
+        B = np.stack([s.B[b] for s in self.steps])
+        C = np.stack([s.C[b] for s in self.steps])
+        dt = np.stack([s.dt[b] for s in self.steps])
+        idx = self.base.idx if sample is None else np.arange(len(sample), dtype=np.int32)
+        return ref.run(pool_np, idx, x, B, C, dt, self.base.A, self.base.dt_bias, self.base.D,
+                       self.base.dt_softplus)
+
+
+def _fused_and_sequential(tp, h):
+    torch = gu.torch_mod()
+    pool0 = torch.from_numpy(tp.base.pool).cuda()
+    d = tp.device(pool0.clone())
+    out_f = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
+    pool_seq = pool0.clone()
+    outs = []
+    for t in range(tp.K):
+        outs.append(h.update(pool_seq, d["idx"], d["x"][:, t], d["B"][:, t], d["C"][:, t], d["dt"][:, t],
+                             d["A"], d["D"], d["dt_bias"]))
+    torch.cuda.synchronize()
+    return d["pool"], out_f, pool_seq, torch.stack(outs, dim=1)
+
+
+@pytest.mark.parametrize("N,P,H,G,bs,K", [
+    (128, 64, 4, 1, 6, 1), (128, 64, 4, 1, 6, 2), (128, 64, 4, 1, 6, 3), (128, 64, 4, 1, 5, 8),
+    (64, 32, 4, 2, 5, 3), (256, 64, 2, 1, 4, 4), (16, 64, 4, 1, 3, 5), (32, 128, 2, 2, 3, 2),
+])
+def test_tokens_match_sequential_bitwise_and_oracle(ref, N, P, H, G, bs, K):
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    tp = TokenProblem(H, P, N, G, bs, 2 * bs + 1, K, seed=3000 + N + P + K)
+    h = ssu.Handle(H, P, N, G, True)
+    pool_f, out_f, pool_s, out_s = _fused_and_sequential(tp, h)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "out differs from sequential"
+    assert torch.equal(pool_f.view(torch.int32), pool_s.view(torch.int32)), "state differs from sequential"
+    pool_ref = tp.base.pool.copy()
+    r = tp.oracle(ref, pool_ref)
+    gpu = pool_f.cpu().numpy()
+    gu.assert_state(gpu[tp.base.idx], r["state"], f"K={K} state")
+    ob = gu.bits(out_f)  # [bs, K, H, P]
+    for t in range(K):
+        gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"K={K} token {t}")
+    untouched = np.setdiff1d(np.arange(tp.base.pool_slots), tp.base.idx)
+    assert np.array_equal(gpu[untouched].view(np.uint32), tp.base.pool[untouched].view(np.uint32))
+
+
+def test_tokens_every_tile_bitwise():
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    tp = TokenProblem(4, 64, 128, 1, 6, 13, 3, seed=3100)
+    base = None
+    for t in [x for x in ssu.tiles() if x["dstate"] == 128]:
+        h = ssu.Handle(4, 64, 128, 1, True, t["id"])
+        pool = torch.from_numpy(tp.base.pool).cuda()
+        d = tp.device(pool)
+        o = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
+        torch.cuda.synchronize()
+        if base is None:
+            base = (o.clone(), pool.clone())
+        else:
+            assert torch.equal(o.view(torch.int16), base[0].view(torch.int16)), t["name"]
+            assert torch.equal(pool.view(torch.int32), base[1].view(torch.int32)), t["name"]
+
+
+def test_tokens_padding():
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    tp = TokenProblem(4, 64, 128, 1, 5, 11, 4, seed=3200)
+    tp.base.idx[2] = -1
+    h = ssu.Handle(4, 64, 128, 1, True)
+    pool = torch.from_numpy(tp.base.pool).cuda()
+    d = tp.device(pool)
+    out = torch.full((5, 4, 4, 64), 0.25, dtype=torch.bfloat16, device="cuda")
+    h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"], out)
+    torch.cuda.synchronize()
+    assert torch.all(out[2] == 0.25)
+    live = tp.base.idx[tp.base.idx >= 0]
+    untouched = np.setdiff1d(np.arange(11), live)
+    assert np.array_equal(pool.cpu().numpy()[untouched], tp.base.pool[untouched])
+
+
+def test_tokens_headline_shape_sampled(ref):
+    """H16 P64 N128, batch 512, 4 tokens (the state read and written once):
+    sampled requests against the oracle's scan."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    bs, K = 512, 4
+    tp = TokenProblem(16, 64, 128, 1, bs, bs, K, seed=3300, host_pool=False)
+    pool = torch.empty((bs, 16, 64, 128), device="cuda")
+    si.draw_pool_on_device(pool, 3300)
+    before = pool.clone()
+    h = ssu.Handle(16, 64, 128, 1, True)
+    d = tp.device(pool)
+    out = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
+    torch.cuda.synchronize()
+    sample = np.array([0, 77, 300, 511])
+    sl = torch.from_numpy(tp.base.idx[sample].astype(np.int64)).cuda()
+    r = tp.oracle(ref, before[sl].cpu().numpy(), sample=sample)
+    gu.assert_state(pool[sl].cpu().numpy(), r["state"], "tokens headline")
+    ob = gu.bits(out)[sample]
+    for t in range(K):
+        gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"tokens headline t{t}")
