@@ -55,6 +55,10 @@ def _ptr(a):
     return None if a is None else a.ctypes.data
 
 
+class RefBlockTensor(ctypes.Structure):
+    _fields_ = [("base", _vp), ("block_stride", _i64), ("block_bytes", _i64), ("nblocks", _i64)]
+
+
 class Oracle:
     """Handle on one build of the oracle library (the default build, or any other
     path, which the tests use to load deliberately broken copies)."""
@@ -75,6 +79,9 @@ class Oracle:
         lib.ssu_ref_discretize.restype = None
         lib.ssu_ref_bf16_rne.argtypes = [ctypes.c_float]
         lib.ssu_ref_bf16_rne.restype = ctypes.c_uint16
+        lib.ssu_ref_copy_blocks.argtypes = [ctypes.POINTER(RefBlockTensor), _i32, ctypes.POINTER(_i32),
+                                            ctypes.POINTER(_i32), _i32]
+        lib.ssu_ref_copy_blocks.restype = _i32
         lib.ssu_ref_max_threads.argtypes = []
         lib.ssu_ref_max_threads.restype = _i32
         self.lib = lib
@@ -95,6 +102,30 @@ class Oracle:
 
     def max_threads(self) -> int:
         return int(self.lib.ssu_ref_max_threads())
+
+    # -- block copy ------------------------------------------------------------
+    def copy_blocks(self, tensors, src, dst):
+        """Copy block src[r] to block dst[r] of every tensor in place.
+
+        ``tensors``: numpy arrays whose axis 0 indexes blocks (a block is one
+        ``arr[i]``, contiguous); src, dst: int32 [nreqs]."""
+        src = np.ascontiguousarray(src, dtype=np.int32)
+        dst = np.ascontiguousarray(dst, dtype=np.int32)
+        if src.shape != dst.shape or src.ndim != 1:
+            raise ValueError("src and dst must be int32 [nreqs]")
+        descs = (RefBlockTensor * max(1, len(tensors)))()
+        for k, arr in enumerate(tensors):
+            if not arr.flags.writeable or not arr[0].flags.c_contiguous:
+                raise ValueError("each tensor must be writeable with contiguous blocks")
+            descs[k].base = arr.ctypes.data
+            descs[k].block_stride = arr.strides[0]
+            descs[k].block_bytes = arr[0].nbytes
+            descs[k].nblocks = arr.shape[0]
+        i32p = ctypes.POINTER(_i32)
+        rc = self.lib.ssu_ref_copy_blocks(descs, len(tensors), src.ctypes.data_as(i32p),
+                                          dst.ctypes.data_as(i32p), len(src))
+        if rc != 0:
+            raise ValueError({1: "bad argument", 2: "null pointer", 3: "overlapping destinations"}.get(rc, rc))
 
     # -- the step ------------------------------------------------------------
     def run(self, pool, idx, x, B, C, dt, A, dt_bias=None, D=None, dt_softplus=True,

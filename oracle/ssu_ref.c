@@ -249,3 +249,53 @@ int32_t ssu_ref_max_threads(void)
     return 1;
 #endif
 }
+
+/*
+ * Block copy for prefix caching / multi-token prediction (vLLM PR #48110,
+ * "[Perf][Hybrid] Vectorize _copy_mamba_state_block to uint64 for temporal",
+ * section "Purpose"): for every request r and every state tensor k, the block
+ * src[r] of tensor k is copied to block dst[r] of tensor k. A tensor's block
+ * i occupies bytes [base + i * block_stride, base + i * block_stride +
+ * block_bytes). Block ids outside [0, nblocks) skip that request (the same
+ * padding rule as the decode step); src == dst is a no-op. Destinations must
+ * be distinct and must not be any request's source (status 3 otherwise): the
+ * result would then depend on the order of the copies.
+ */
+typedef struct ssu_ref_block_tensor {
+    unsigned char *base;
+    int64_t block_stride, block_bytes, nblocks;
+} ssu_ref_block_tensor;
+
+int32_t ssu_ref_copy_blocks(const ssu_ref_block_tensor *t, int32_t ntensors, const int32_t *src,
+                            const int32_t *dst, int32_t nreqs)
+{
+    if (ntensors < 0 || nreqs < 0)
+        return 1;
+    if (nreqs == 0 || ntensors == 0)
+        return 0;
+    if (!t || !src || !dst)
+        return 2;
+    for (int32_t k = 0; k < ntensors; ++k)
+        if (!t[k].base || t[k].block_bytes < 0 || t[k].nblocks < 0)
+            return 1;
+    /* destinations distinct and never a source (per tensor, same ids) */
+    for (int32_t r = 0; r < nreqs; ++r) {
+        if (src[r] == dst[r])
+            continue;
+        for (int32_t q = 0; q < nreqs; ++q) {
+            if (q != r && dst[q] == dst[r] && src[q] != dst[q])
+                return 3;
+            if (src[q] == dst[r] && src[q] != dst[q])
+                return 3;
+        }
+    }
+    for (int32_t r = 0; r < nreqs; ++r)
+        for (int32_t k = 0; k < ntensors; ++k) {
+            const int64_t s = src[r], d = dst[r];
+            if (s < 0 || s >= t[k].nblocks || d < 0 || d >= t[k].nblocks || s == d)
+                continue;
+            memcpy(t[k].base + d * t[k].block_stride, t[k].base + s * t[k].block_stride,
+                   (size_t)t[k].block_bytes);
+        }
+    return 0;
+}

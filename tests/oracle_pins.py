@@ -345,3 +345,43 @@ PINS = [
     pin_kstep,
     pin_brute_force,
 ]
+
+
+def pin_copy_blocks(o):
+    """Block copy against numpy fancy-index assignment, the skip and no-op
+    rules, and the rejection of order-dependent requests."""
+    rng = _rng(12)
+    tensors = [rng.standard_normal((9, 4, 6)).astype(np.float32),
+               rng.integers(0, 65535, size=(9, 3, 5), dtype=np.uint16),
+               rng.standard_normal((9, 7)).astype(np.float64)]
+    before = [t.copy() for t in tensors]
+    src = np.array([0, 3, 5, 7], dtype=np.int32)
+    dst = np.array([1, 2, 8, 7], dtype=np.int32)  # last pair: src == dst, a no-op
+    o.copy_blocks(tensors, src, dst)
+    for t, b in zip(tensors, before):
+        want = b.copy()
+        want[dst[:3]] = b[src[:3]]
+        assert np.array_equal(t, want)
+    # out-of-range ids skip the request
+    tensors2 = [b.copy() for b in before]
+    o.copy_blocks(tensors2, np.array([-1, 4], dtype=np.int32), np.array([6, 9], dtype=np.int32))
+    for t, b in zip(tensors2, before):
+        assert np.array_equal(t, b)
+    # a destination that is also a source, or two equal destinations: rejected
+    for s_, d_ in (([0, 1], [1, 2]), ([0, 3], [4, 4])):
+        try:
+            o.copy_blocks([b.copy() for b in before], np.array(s_, dtype=np.int32), np.array(d_, dtype=np.int32))
+        except ValueError:
+            pass
+        else:
+            raise AssertionError(f"order-dependent copy accepted: {s_} -> {d_}")
+    # a strided tensor (blocks not adjacent): only the block bytes move
+    big = rng.standard_normal((6, 2, 8)).astype(np.float32)
+    view = big[:, 0]  # block stride 64 bytes, block 32 bytes
+    ref = big.copy()
+    o.copy_blocks([view], np.array([1], dtype=np.int32), np.array([4], dtype=np.int32))
+    ref[4, 0] = ref[1, 0]
+    assert np.array_equal(big, ref)
+
+
+PINS.append(pin_copy_blocks)

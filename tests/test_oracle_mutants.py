@@ -48,6 +48,18 @@ MUTANTS = [
     ("skip_check_off", "if (slot < 0 || slot >= g->pool_slots)\n                continue;",
      "if (slot < 0 || slot >= g->pool_slots)\n                slot = 0;"),
     ("dups_allowed", "if (seen[s]) {", "if (0 && seen[s]) {"),
+    ("copy_direction", "memcpy(t[k].base + d * t[k].block_stride, t[k].base + s * t[k].block_stride,",
+     "memcpy(t[k].base + s * t[k].block_stride, t[k].base + d * t[k].block_stride,"),
+    ("copy_stride_ignored", "t[k].base + s * t[k].block_stride,", "t[k].base + s * t[k].block_bytes,"),
+    ("copy_skip_off",
+     "const int64_t s = src[r], d = dst[r];\n"
+     "            if (s < 0 || s >= t[k].nblocks || d < 0 || d >= t[k].nblocks || s == d)\n"
+     "                continue;",
+     "int64_t s = src[r], d = dst[r];\n"
+     "            if (s == d) continue;\n"
+     "            if (s < 0 || s >= t[k].nblocks) s = 0;\n"
+     "            if (d < 0 || d >= t[k].nblocks) d = 0;"),
+    ("copy_overlap_allowed", "            if (src[q] == dst[r] && src[q] != dst[q])\n                return 3;\n", ""),
 ]
 
 
