@@ -459,6 +459,65 @@ def run_tokens(a):
         torch.cuda.empty_cache()
 
 
+# Per-request state blocks of the copy workload (vLLM state-block copy page,
+# "Test Plan"): 24 layers x (temporal fp32 2 MiB + conv bf16 80 KiB).
+COPY_LAYERS = 24
+COPY_TEMPORAL_BYTES = 2 * 1024 * 1024
+COPY_CONV_BYTES = 80 * 1024
+
+
+def copy_bytes_per_request():
+    return COPY_LAYERS * (COPY_TEMPORAL_BYTES + COPY_CONV_BYTES)
+
+
+def copy_gbps(nreqs, seconds):
+    """Read + written bytes per second, in GB/s (the page's convention)."""
+    return 2 * nreqs * copy_bytes_per_request() / seconds / 1e9
+
+
+def run_copy_blocks(a):
+    """ssu_copy_blocks on the page's layout, reqs from --copy-blocks; disjoint
+    block sets >= 768 MiB rotated in a HIP graph (cold HBM), median of 5 x 10
+    replays. One line per request count."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    out = open(a.out, "w") if a.out else sys.stdout
+    print("reqs K calls us_per_call GBps pct_peak tile", file=out, flush=True)
+    per_req = copy_bytes_per_request()
+    for nreqs in [int(r) for r in a.copy_blocks.split(",")]:
+        K = max(1, -(-ROTATION_BYTES // (nreqs * per_req)))
+        nblocks = 2 * K * nreqs
+        g = torch.Generator(device="cuda")
+        g.manual_seed(nreqs)
+        temporal = [torch.empty((nblocks, COPY_TEMPORAL_BYTES // 4), device="cuda").normal_(generator=g)
+                    for _ in range(COPY_LAYERS)]
+        conv = [torch.empty((nblocks, COPY_CONV_BYTES // 2), dtype=torch.bfloat16, device="cuda").normal_(generator=g)
+                for _ in range(COPY_LAYERS)]
+        tensors = temporal + conv
+        descs = ssu.block_tensors(tensors)
+        rng = np.random.Generator(np.random.PCG64([nreqs, 7]))
+        perm = rng.permutation(nblocks).astype(np.int32).reshape(K, 2, nreqs)
+        ids = [(torch.from_numpy(perm[k, 0].copy()).cuda(), torch.from_numpy(perm[k, 1].copy()).cuda())
+               for k in range(K)]
+        calls = max(20, K)
+        ssu.copy_blocks(tensors, *ids[0], tile=a.tile, descs=descs)
+        torch.cuda.synchronize()
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(graph):
+            for i in range(calls):
+                ssu.copy_blocks(tensors, *ids[i % K], tile=a.tile, descs=descs)
+        graph.replay()
+        torch.cuda.synchronize()
+        us = statistics.median([time_graph(graph, 10) / (10 * calls) for _ in range(5)]) * 1e6
+        gbs = copy_gbps(nreqs, us * 1e-6)
+        name = ssu.copy_tiles()[a.tile] if a.tile >= 0 else "default"
+        print(f"{nreqs} {K} {calls} {us:.2f} {gbs:.1f} {100 * gbs / HBM_PEAK_GBS:.2f} {name}", file=out, flush=True)
+        del graph, tensors, temporal, conv, ids
+        torch.cuda.empty_cache()
+
+
 def run_counters(a):
     """Eager calls for a rocprofv3 --pmc pass: `a.steps` headline calls rotating
     over the slot sets, then a plain device copy of a known size (256 MiB read
@@ -571,6 +630,7 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true")
     ap.add_argument("--copy-ceiling", action="store_true")
     ap.add_argument("--tokens", default="", help="comma list of tokens per call (ssu_update_tokens)")
+    ap.add_argument("--copy-blocks", default="", help="comma list of request counts (ssu_copy_blocks)")
     ap.add_argument("--summarize-counters", default="")
     ap.add_argument("--write-profile", action="store_true")
     ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
@@ -590,6 +650,8 @@ def main():
         run_copy_ceiling(a)
     elif a.tokens:
         run_tokens(a)
+    elif a.copy_blocks:
+        run_copy_blocks(a)
     elif a.sweep:
         run_sweep(a)
     else:

@@ -213,6 +213,43 @@ const char *ssu_status_string(ssu_status s);
 /* The calling thread's most recent error description ("" if none). */
 const char *ssu_last_error(void);
 
+/* ---------------------------------------------------------- block copies --
+ * Copy whole state blocks between slots, for prefix caching and multi-token
+ * prediction in hybrid models (vLLM PR #48110, "[Perf][Hybrid] Vectorize
+ * _copy_mamba_state_block to uint64 for temporal", section "Purpose"): for
+ * every request r and every tensor k, block src_blocks[r] of tensor k is
+ * copied to block dst_blocks[r] of tensor k.
+ */
+
+/* One state tensor (for example one layer's conv or temporal state). Block i
+ * occupies bytes [base + i * block_stride, base + i * block_stride +
+ * block_bytes). base, block_stride and block_bytes must be 16-byte multiples
+ * (SSU_ERR_MISALIGNED otherwise: a guardrail, there is no narrow path). */
+typedef struct ssu_block_tensor {
+    void *base;
+    int64_t block_stride; /* bytes, >= block_bytes unless nblocks <= 1 */
+    int64_t block_bytes;  /* bytes copied per block (0: tensor skipped) */
+    int64_t nblocks;      /* ids outside [0, nblocks) skip that request */
+} ssu_block_tensor;
+
+/* Enqueue the copies on `stream`. `tensors` is a host array read during the
+ * call only; src_blocks and dst_blocks are device arrays [nreqs] int32.
+ * src == dst is a no-op. Preconditions (not checked; the result would depend
+ * on the order of the copies): destinations are distinct and no destination is
+ * another request's source. tile = -1 uses the default launch configuration;
+ * 0 .. ssu_copy_tile_count()-1 forces one (for sweeps). Asynchronous,
+ * allocation-free and graph-capturable like ssu_update.
+ * Errors: SSU_ERR_INVALID_ARGUMENT (negative sizes, null pointers, tile out of
+ * range, overlapping blocks), SSU_ERR_MISALIGNED, SSU_ERR_UNSUPPORTED (more than
+ * 2^31 workgroups), SSU_ERR_HIP. nreqs == 0 or ntensors == 0 is a no-op. */
+ssu_status ssu_copy_blocks(const ssu_block_tensor *tensors, int32_t ntensors, const int32_t *src_blocks,
+                           const int32_t *dst_blocks, int32_t nreqs, int32_t tile, hipStream_t stream);
+
+/* Number of compiled copy configurations, and the name of one ("" if out of
+ * range). */
+int32_t ssu_copy_tile_count(void);
+const char *ssu_copy_tile_name(int32_t tile);
+
 /* SSU_ABI_VERSION of the built library. */
 int32_t ssu_abi_version(void);
 

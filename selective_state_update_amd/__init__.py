@@ -29,6 +29,8 @@ __all__ = [
     "Handle",
     "selective_state_update",
     "TokensArgs",
+    "copy_blocks",
+    "copy_tiles",
     "tiles",
     "library_path",
     "abi_version",
@@ -83,6 +85,10 @@ class TokensArgs(ctypes.Structure):
                 ("dt", View), ("dt_bias", View), ("A", View), ("D", View), ("out", View)]
 
 
+class BlockTensor(ctypes.Structure):
+    _fields_ = [("base", _vp), ("block_stride", _i64), ("block_bytes", _i64), ("nblocks", _i64)]
+
+
 class TileDesc(ctypes.Structure):
     _fields_ = [("dstate", _i32), ("rows_per_wave", _i32), ("waves", _i32), ("rows_per_group", _i32),
                 ("nontemporal", _i32), ("xcd_remap", _i32), ("groups_per_cu", _i32), ("name", ctypes.c_char * 48)]
@@ -110,6 +116,12 @@ _lib.ssu_status_string.argtypes = [_i32]
 _lib.ssu_status_string.restype = ctypes.c_char_p
 _lib.ssu_last_error.argtypes = []
 _lib.ssu_last_error.restype = ctypes.c_char_p
+_lib.ssu_copy_blocks.argtypes = [ctypes.POINTER(BlockTensor), _i32, _vp, _vp, _i32, _i32, _vp]
+_lib.ssu_copy_blocks.restype = _i32
+_lib.ssu_copy_tile_count.argtypes = []
+_lib.ssu_copy_tile_count.restype = _i32
+_lib.ssu_copy_tile_name.argtypes = [_i32]
+_lib.ssu_copy_tile_name.restype = ctypes.c_char_p
 _lib.ssu_abi_version.argtypes = []
 _lib.ssu_abi_version.restype = _i32
 
@@ -369,3 +381,47 @@ def selective_state_update(state, x, dt, A, B, C, D=None, dt_bias=None, dt_softp
             h = Handle(H, P, N, G, dt_softplus, tile, -1 if state.device.index is None else state.device.index)
             _handles[key] = h
     return h.update(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)
+
+
+def copy_tiles():
+    """Names of the compiled block-copy configurations (index = tile id)."""
+    return [_lib.ssu_copy_tile_name(i).decode() for i in range(_lib.ssu_copy_tile_count())]
+
+
+def block_tensors(tensors):
+    """ssu_block_tensor descriptors for torch tensors whose axis 0 indexes
+    blocks (block i is ``t[i]``, which must be contiguous)."""
+    descs = (BlockTensor * max(1, len(tensors)))()
+    for k, t in enumerate(tensors):
+        if t.dim() < 1 or not t[0].is_contiguous():
+            raise ValueError(f"tensor {k}: block t[i] must be contiguous")
+        if t.device.type != "cuda":
+            raise ValueError(f"tensor {k} must be on a GPU")
+        descs[k].base = t.data_ptr()
+        descs[k].block_stride = t.stride(0) * t.element_size()
+        descs[k].block_bytes = t[0].numel() * t.element_size()
+        descs[k].nblocks = t.shape[0]
+    return descs
+
+
+def copy_blocks(tensors, src_blocks, dst_blocks, tile=-1, stream=None, descs=None):
+    """Copy block src_blocks[r] to block dst_blocks[r] of every tensor
+    (ssu_copy_blocks). src_blocks, dst_blocks: int32 GPU tensors [nreqs].
+    ``descs`` may pass prepared block_tensors(tensors) to skip rebuilding them."""
+    torch = _torch()
+    if src_blocks.dtype != torch.int32 or dst_blocks.dtype != torch.int32:
+        raise TypeError("block ids must be int32")
+    if src_blocks.shape != dst_blocks.shape or src_blocks.dim() != 1:
+        raise ValueError("src_blocks and dst_blocks must be [nreqs]")
+    if not (src_blocks.is_contiguous() and dst_blocks.is_contiguous()):
+        raise ValueError("block ids must be contiguous")
+    if descs is None:
+        descs = block_tensors(tensors)
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = _lib.ssu_copy_blocks(descs, len(tensors), src_blocks.data_ptr(), dst_blocks.data_ptr(),
+                              src_blocks.shape[0], tile, _vp(stream))
+    if st != SSU_OK:
+        raise SSUError(st, "ssu_copy_blocks")

@@ -15,7 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRC = os.path.join(HERE, "csrc", "ssu.hip")
+SRCS = [os.path.join(HERE, "csrc", "ssu.hip"), os.path.join(HERE, "csrc", "block_copy.hip")]
 LIB = os.path.join(HERE, "libssu.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
@@ -35,7 +35,7 @@ FLAGS = [
 
 def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
     tmp = out + ".tmp"
-    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, SRC]
+    cmd = [HIPCC, *FLAGS, *extra, "-o", tmp, *SRCS]
     if verbose:
         print(" ".join(cmd), flush=True)
     res = subprocess.run(cmd, capture_output=True, text=True)

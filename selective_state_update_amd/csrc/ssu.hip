@@ -44,12 +44,9 @@
 #include <new>
 #include <vector>
 
-#include "ssu.h"
+#include "internal.h"
 
 namespace ssu {
-
-using f32x4 = float __attribute__((ext_vector_type(4)));
-using u32x2 = uint32_t __attribute__((ext_vector_type(2)));
 
 struct Params {
     float *state;
@@ -90,17 +87,6 @@ __device__ __forceinline__ uint16_t bf16_round(float f)
     return static_cast<uint16_t>(u >> 16);
 }
 
-// Read-only operands (slot ids, dt, dt_bias, A, D, x) are never written while
-// the kernel runs (the ABI forbids aliasing them with the state or out), so
-// they are read through the constant address space: at a uniform address the
-// compiler can then always use the scalar cache, even after the loop's state
-// stores, and waiting for them never waits on the vector-memory counter.
-template <typename T>
-__device__ __forceinline__ T load_ro(const T *ptr)
-{
-    return *(const __attribute__((address_space(4))) T *)(ptr);
-}
-
 template <int CTRL>
 __device__ __forceinline__ float dpp(float v)
 {
@@ -123,35 +109,6 @@ __device__ __forceinline__ float group_sum(float v)
     if constexpr (LPR >= 32)  // swizzle, bitmask mode: lane ^ 16 within 32
         v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
     return v;
-}
-
-template <bool NT>
-__device__ __forceinline__ f32x4 load4(const float *p)
-{
-    if constexpr (NT)
-        return __builtin_nontemporal_load(reinterpret_cast<const f32x4 *>(p));
-    else
-        return *reinterpret_cast<const f32x4 *>(p);
-}
-
-template <bool NT>
-__device__ __forceinline__ void store4(float *p, f32x4 v)
-{
-    if constexpr (NT)
-        __builtin_nontemporal_store(v, reinterpret_cast<f32x4 *>(p));
-    else
-        *reinterpret_cast<f32x4 *>(p) = v;
-}
-
-// Workgroups are dispatched round-robin over 8 XCDs. Map the first
-// floor(total/8)*8 of them so that logical ids [k*q, (k+1)*q) run on XCD k;
-// the tail keeps its order. A bijection on [0, total).
-__device__ __forceinline__ int xcd_order(int g, int total)
-{
-    const int q = total >> 3;
-    if (g >= (q << 3))
-        return g;
-    return (g & 7) * q + (g >> 3);
 }
 
 // One lane's share of one tile: `rows_per_group` consecutive state rows of one
@@ -549,6 +506,38 @@ int find_tile(int N, int rows_per_group, int waves, int nt, int remap, int cap)
     return -1;
 }
 
+namespace {
+thread_local char g_err[256] = "";
+}  // namespace
+
+ssu_status fail(ssu_status s, const char *fmt, ...)
+{
+    va_list ap;
+    va_start(ap, fmt);
+    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
+    va_end(ap);
+    return s;
+}
+
+DeviceLimits device_limits(int dev)
+{
+    constexpr int kMaxDevices = 64;
+    static std::atomic<int> lds_cu[kMaxDevices];
+    static std::atomic<int> lds_block[kMaxDevices];
+    if (dev < 0 || dev >= kMaxDevices)
+        return {0, 0};
+    int cu = lds_cu[dev].load(std::memory_order_acquire);
+    int blk = lds_block[dev].load(std::memory_order_acquire);
+    if (cu <= 0 || blk <= 0) {
+        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
+            hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess)
+            return {0, 0};
+        lds_cu[dev].store(cu, std::memory_order_release);
+        lds_block[dev].store(blk, std::memory_order_release);
+    }
+    return {cu, blk};
+}
+
 }  // namespace ssu
 
 // -------------------------------------------------------------- host ABI --
@@ -560,45 +549,9 @@ struct ssu_handle {
 
 namespace {
 
-thread_local char g_err[256] = "";
-
-// Per-device LDS sizes, queried once per device (host attribute queries only).
-struct DeviceLimits {
-    int lds_cu, lds_block, cus;
-};
-
-DeviceLimits device_limits(int dev)
-{
-    constexpr int kMaxDevices = 64;
-    static std::atomic<int> lds_cu[kMaxDevices];
-    static std::atomic<int> lds_block[kMaxDevices];
-    static std::atomic<int> cu_count[kMaxDevices];
-    if (dev < 0 || dev >= kMaxDevices)
-        return {0, 0, 0};
-    int cu = lds_cu[dev].load(std::memory_order_acquire);
-    int blk = lds_block[dev].load(std::memory_order_acquire);
-    int n = cu_count[dev].load(std::memory_order_acquire);
-    if (cu <= 0 || blk <= 0 || n <= 0) {
-        if (hipDeviceGetAttribute(&cu, hipDeviceAttributeMaxSharedMemoryPerMultiprocessor, dev) != hipSuccess ||
-            hipDeviceGetAttribute(&blk, hipDeviceAttributeMaxSharedMemoryPerBlock, dev) != hipSuccess ||
-            hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
-            return {0, 0, 0};
-        lds_cu[dev].store(cu, std::memory_order_release);
-        lds_block[dev].store(blk, std::memory_order_release);
-        cu_count[dev].store(n, std::memory_order_release);
-    }
-    return {cu, blk, n};
-}
-
-ssu_status fail(ssu_status s, const char *fmt, ...) __attribute__((format(printf, 2, 3)));
-ssu_status fail(ssu_status s, const char *fmt, ...)
-{
-    va_list ap;
-    va_start(ap, fmt);
-    std::vsnprintf(g_err, sizeof g_err, fmt, ap);
-    va_end(ap);
-    return s;
-}
+using ssu::DeviceLimits;
+using ssu::device_limits;
+using ssu::fail;
 
 bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
@@ -686,7 +639,7 @@ extern "C" {
 
 int32_t ssu_abi_version(void) { return SSU_ABI_VERSION; }
 
-const char *ssu_last_error(void) { return g_err; }
+const char *ssu_last_error(void) { return ssu::g_err; }
 
 const char *ssu_status_string(ssu_status s)
 {

@@ -346,3 +346,31 @@ def test_tokens_struct_layout(ssu):
     assert ctypes.sizeof(ssu.TokensArgs) == 16 + 10 * ctypes.sizeof(ssu.View)
     text = open(HEADER).read()
     assert int(re.search(r"#define SSU_MAX_TOKENS (\d+)", text).group(1)) == 1024
+
+
+# ------------------------------------------------------------ ssu_copy_blocks --
+def test_copy_blocks_validation(ssu):
+    B = ssu.BlockTensor
+    lib = ssu._lib
+    good = B(FAKE, 4096, 4096, 8)
+    ids = ctypes.c_void_p(FAKE + 0x100000)
+
+    def call(t, n=1, nreqs=2, tile=-1, src=ids, dst=ids):
+        arr = (B * max(1, n))(*([t] * max(1, n)))
+        return lib.ssu_copy_blocks(arr, n, src, dst, nreqs, tile, None)
+
+    assert call(good, nreqs=0) == 0          # no work: nothing read
+    assert call(good, n=0) == 0
+    assert call(good, nreqs=-1) == 1
+    assert call(good, n=-1) == 1
+    assert call(good, tile=10 ** 6) == 1
+    assert call(good, src=None) == 1
+    assert call(B(None, 4096, 4096, 8)) == 1
+    assert call(B(FAKE + 8, 4096, 4096, 8)) == 3
+    assert call(B(FAKE, 4100, 4096, 8)) == 3
+    assert call(B(FAKE, 4096, 4088, 8)) == 3
+    assert call(B(FAKE, 4096, 8192, 8)) == 1  # blocks overlap
+    assert call(B(FAKE, 4096, -16, 8)) == 1
+    assert lib.ssu_copy_tile_count() > 0
+    assert lib.ssu_copy_tile_name(0).decode().startswith("copy_")
+    assert lib.ssu_copy_tile_name(-1) == b""

@@ -69,3 +69,16 @@ def test_sweep_grid_is_920_points():
 def test_multi_gpu_request_exits_with_message():
     r = subprocess.run([sys.executable, bench.__file__, "--gpus", "2"], capture_output=True, text=True)
     assert r.returncode == 2 and "one GPU" in r.stderr
+
+
+def test_copy_byte_formula_reproduces_the_pages_tables():
+    """The vLLM page prints latency and GB/s for the same runs; 2 x reqs x the
+    per-request block bytes (24 x (2 MiB + 80 KiB)) over the latency must give
+    its GB/s, so the bench's copy metric is the page's."""
+    path = os.path.join(os.path.dirname(__file__), "golden", "p2_copy_kernel.txt")
+    rows = [ln.split() for ln in open(path) if ln.strip() and not ln.startswith("#")]
+    assert len(rows) >= 6
+    for gpu, reqs, us, gbps in rows:
+        got = bench.copy_gbps(int(reqs), float(us) * 1e-6)
+        assert abs(got - float(gbps)) <= 0.001 * float(gbps), (gpu, reqs, got, gbps)
+    assert abs(bench.copy_bytes_per_request() / 2 ** 20 - 49.88) < 0.01
