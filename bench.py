@@ -45,7 +45,8 @@ import ssu_inputs as si  # noqa: E402
 HBM_PEAK_GBS = 8000.0  # MI355X HBM3E, published
 LLC_BYTES = 256 * 1024 * 1024  # MI355X Infinity Cache
 ROTATION_BYTES = 3 * LLC_BYTES  # >= 3x the last-level cache
-KERNEL_SRC = os.path.join(ROOT, "selective_state_update_amd", "csrc", "ssu.hip")
+KERNEL_SRCS = [os.path.join(ROOT, "selective_state_update_amd", "csrc", "ssu.hip"),
+               os.path.join(ROOT, "selective_state_update_amd", "csrc", "internal.h")]
 COUNTER_PROFILE = os.path.join(ROOT, "profiles", "ssu_decode_h16_bs512_counters.md")
 
 WORKLOADS = {
@@ -69,11 +70,12 @@ def algorithmic_bytes(H, P, N, G, batch):
 
 
 def source_digest() -> str:
-    """Hash of the kernel source's code: comments and whitespace are removed
-    first, so only a change to the code itself invalidates counter data."""
+    """Hash of the decode kernel's source code (its file and the shared
+    header): comments and whitespace are removed first, so only a change to
+    the code itself invalidates counter data."""
     import re
 
-    text = open(KERNEL_SRC).read()
+    text = "\n".join(open(f).read() for f in KERNEL_SRCS)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
