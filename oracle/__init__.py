@@ -7,7 +7,9 @@ shares no code with the GPU library.
 This module marshals numpy arrays into the plain-C fp64 oracle in
 ``ssu_ref.c`` (see that file for the definition it computes and the passages it
 follows). Arrays are passed with their own strides, so the packed xBC views and
-the per-head broadcasts reach the oracle exactly as they are stored.
+the per-head broadcasts reach the oracle exactly as they are stored. Besides
+the decode step it holds the state-block copy and the selective scan over a
+sequence (prefill), with the fp16 conversions the scan's io needs.
 """
 from __future__ import annotations
 
@@ -59,6 +61,26 @@ class RefBlockTensor(ctypes.Structure):
     _fields_ = [("base", _vp), ("block_stride", _i64), ("block_bytes", _i64), ("nblocks", _i64)]
 
 
+class RefScanArgs(ctypes.Structure):
+    _fields_ = [
+        ("batch", _i32), ("dim", _i32), ("dstate", _i32), ("ngroups", _i32),
+        ("delta_softplus", _i32), ("io_dtype", _i32), ("nthreads", _i32), ("reserved", _i32),
+        ("seqlen", _i64),
+        ("state", _vp), ("st_b", _i64), ("st_d", _i64),
+        ("u", _vp), ("u_b", _i64), ("u_d", _i64), ("u_t", _i64),
+        ("delta", _vp), ("dl_b", _i64), ("dl_d", _i64), ("dl_t", _i64),
+        ("B", _vp), ("B_b", _i64), ("B_g", _i64), ("B_n", _i64), ("B_t", _i64),
+        ("C", _vp), ("C_b", _i64), ("C_g", _i64), ("C_n", _i64), ("C_t", _i64),
+        ("A", _vp), ("A_d", _i64), ("A_n", _i64),
+        ("D", _vp), ("delta_bias", _vp),
+        ("out", _vp), ("o_b", _i64), ("o_d", _i64), ("o_t", _i64),
+        ("state_ref", _vp), ("err_ref", _vp), ("y_ref", _vp), ("tau_ref", _vp), ("rho_ref", _vp),
+    ]
+
+
+IO_DTYPES = {"bf16": 0, "f16": 1}
+
+
 class Oracle:
     """Handle on one build of the oracle library (the default build, or any other
     path, which the tests use to load deliberately broken copies)."""
@@ -82,6 +104,12 @@ class Oracle:
         lib.ssu_ref_copy_blocks.argtypes = [ctypes.POINTER(RefBlockTensor), _i32, ctypes.POINTER(_i32),
                                             ctypes.POINTER(_i32), _i32]
         lib.ssu_ref_copy_blocks.restype = _i32
+        lib.ssu_ref_scan.argtypes = [ctypes.POINTER(RefScanArgs)]
+        lib.ssu_ref_scan.restype = _i32
+        lib.ssu_ref_f16_value.argtypes = [ctypes.c_uint16]
+        lib.ssu_ref_f16_value.restype = ctypes.c_double
+        lib.ssu_ref_f16_rne.argtypes = [ctypes.c_float]
+        lib.ssu_ref_f16_rne.restype = ctypes.c_uint16
         lib.ssu_ref_max_threads.argtypes = []
         lib.ssu_ref_max_threads.restype = _i32
         self.lib = lib
@@ -99,6 +127,14 @@ class Oracle:
     def bf16_rne(self, values) -> np.ndarray:
         v = np.asarray(values, dtype=np.float32).ravel()
         return np.array([self.lib.ssu_ref_bf16_rne(float(f)) for f in v], dtype=np.uint16)
+
+    def f16_value(self, bits) -> np.ndarray:
+        b = np.asarray(bits, dtype=np.uint16).ravel()
+        return np.array([self.lib.ssu_ref_f16_value(int(v)) for v in b], dtype=np.float64)
+
+    def f16_rne(self, values) -> np.ndarray:
+        v = np.asarray(values, dtype=np.float32).ravel()
+        return np.array([self.lib.ssu_ref_f16_rne(float(f)) for f in v], dtype=np.uint16)
 
     def max_threads(self) -> int:
         return int(self.lib.ssu_ref_max_threads())
@@ -206,6 +242,75 @@ class Oracle:
         if want_state:
             res["state"] = state
         return res
+
+    # -- selective scan over a sequence -------------------------------------
+    def scan(self, state, u, delta, A, B, C, D=None, delta_bias=None, delta_softplus=True, io="f16",
+              want_ref=True, nthreads=0, out=None):
+        """Selective scan over a sequence (see ssu_ref.c), ``state`` updated in place.
+
+        state: float32 [batch, dim, dstate] (dstate contiguous); u, delta: uint16
+        bits [batch, dim, L]; B, C: uint16 bits [batch, G, dstate, L]; A: float32
+        [dim, dstate]; D, delta_bias: float32 [dim] or None; io: "f16" or "bf16".
+
+        Returns a dict: ``out`` (uint16 bits [batch, dim, L]) and, with want_ref,
+        ``y``, ``tau``, ``rho`` (fp64 [batch, dim, L]), ``state`` and ``err``
+        (fp64 [batch, dim, dstate]).
+        """
+        bs, dim, L = u.shape
+        G, N = B.shape[1], B.shape[2]
+        if state.dtype != np.float32 or state.shape != (bs, dim, N) or state.strides[2] != 4:
+            raise ValueError(f"state must be float32 [{bs},{dim},{N}] with dstate contiguous")
+        if not state.flags.writeable:
+            raise ValueError("state must be writeable")
+        for name, arr, shp in (("delta", delta, (bs, dim, L)), ("B", B, (bs, G, N, L)), ("C", C, (bs, G, N, L))):
+            if arr.shape != shp:
+                raise ValueError(f"{name} shape {arr.shape} != {shp}")
+        for name, arr in (("u", u), ("delta", delta), ("B", B), ("C", C)):
+            if arr.dtype != np.uint16:
+                raise ValueError(f"{name} must hold {io} bits (uint16)")
+        A = np.asarray(A, dtype=np.float32)
+        if A.shape != (dim, N):
+            raise ValueError("A must be [dim, dstate]")
+        D = None if D is None else np.ascontiguousarray(D, dtype=np.float32)
+        delta_bias = None if delta_bias is None else np.ascontiguousarray(delta_bias, dtype=np.float32)
+        for name, arr in (("D", D), ("delta_bias", delta_bias)):
+            if arr is not None and arr.shape != (dim,):
+                raise ValueError(f"{name} must be [dim]")
+        if out is None:
+            out = np.zeros((bs, dim, L), dtype=np.uint16)
+        refs = {}
+        if want_ref:
+            for k, shp in (("y", (bs, dim, L)), ("tau", (bs, dim, L)), ("rho", (bs, dim, L)),
+                           ("state", (bs, dim, N)), ("err", (bs, dim, N))):
+                refs[k] = np.full(shp, np.nan)
+        a = RefScanArgs()
+        a.batch, a.dim, a.dstate, a.ngroups = bs, dim, N, G
+        a.delta_softplus, a.io_dtype, a.nthreads = int(bool(delta_softplus)), IO_DTYPES[io], int(nthreads)
+        a.seqlen = L
+        a.state = _ptr(state)
+        a.st_b, a.st_d, _ = _estrides(state)
+        a.u = _ptr(u)
+        a.u_b, a.u_d, a.u_t = _estrides(u)
+        a.delta = _ptr(delta)
+        a.dl_b, a.dl_d, a.dl_t = _estrides(delta)
+        a.B = _ptr(B)
+        a.B_b, a.B_g, a.B_n, a.B_t = _estrides(B)
+        a.C = _ptr(C)
+        a.C_b, a.C_g, a.C_n, a.C_t = _estrides(C)
+        a.A = _ptr(A)
+        a.A_d, a.A_n = _estrides(A)
+        a.D, a.delta_bias = _ptr(D), _ptr(delta_bias)
+        a.out = _ptr(out)
+        a.o_b, a.o_d, a.o_t = _estrides(out)
+        a.state_ref, a.err_ref = _ptr(refs.get("state")), _ptr(refs.get("err"))
+        a.y_ref, a.tau_ref, a.rho_ref = _ptr(refs.get("y")), _ptr(refs.get("tau")), _ptr(refs.get("rho"))
+        keep = (state, u, delta, A, B, C, D, delta_bias, out, refs)
+        rc = self.lib.ssu_ref_scan(ctypes.byref(a))
+        del keep
+        if rc != 0:
+            raise ValueError({1: "bad shape", 2: "null pointer"}.get(rc, rc))
+        return {"out": out, **refs}
+
 
 
 _default: Oracle | None = None

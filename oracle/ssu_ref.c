@@ -299,3 +299,199 @@ int32_t ssu_ref_copy_blocks(const ssu_ref_block_tensor *t, int32_t ntensors, con
         }
     return 0;
 }
+
+/*
+ * Selective scan over a sequence, for prefill (COREY: Entropy-Guided Runtime
+ * Chunk Scheduling for Selective Scan Kernels, Table 9, Table 17 and Table 18:
+ * selective_scan_fn over dim channels with d_state states each, FP16 or BF16
+ * activations, the sequence cut into static chunks of tokens with one kernel
+ * call per chunk and the state carried from one chunk to the next; Table 5
+ * calls such a kernel recurrence-preserving). The page prints no formula; the
+ * scan taken here is the standard Mamba selective scan, the length-L form of
+ * the decode step above with a decay rate per (channel, state):
+ *
+ *   for every request b, channel d and token t = 0, 1, ..., L-1 in order:
+ *     v       = delta[b,d,t] + delta_bias[d]            (delta_bias = 0 if absent)
+ *     Delta   = softplus(v) if softplus is on, else v
+ *     a[n]    = exp(A[d,n] * Delta)
+ *     h[n]    = h[n] * a[n] + (Delta * u[b,d,t]) * B[b,g(d),n,t]
+ *     y[t]    = sum_n h[n] * C[b,g(d),n,t] + D[d] * u[b,d,t]   (D = 0 if absent)
+ *     out[t]  = io_RNE(fp32_RNE(y[t]))
+ *   state[b,d,n] = fp32_RNE(h[n] after the last token)
+ *
+ * with h read from state[b,d,:] before the first token, g(d) = floor(d * G /
+ * dim) (contiguous blocks of dim/G channels per group) and the sum over n in
+ * order. Cutting the sequence into chunks and carrying h between them gives
+ * the same recurrence, so the oracle is the unchunked scan.
+ *
+ * Error scales for the acceptance test (not part of the scan; ssu_ref_scan
+ * returns them on request). With beta = (Delta u) B, per (b, d, n):
+ *   M_t = a_t M_{t-1} + |beta_t|                        (bounds |h_t|)
+ *   E_t = a_t E_{t-1} + (1 + |A Delta_t|) a_t M_{t-1} + M_t
+ * from M_{-1} = E_{-1} = |h before the first token|. E_t grows by every
+ * magnitude that a rounding step of fp32 arithmetic on this recurrence can
+ * touch (the decay, whose relative error grows with its argument, applied to
+ * the carried state, and the new state) and carries the older ones with the
+ * decay, so fp32 rounding errors in h_t stay within a small multiple of
+ * 2^-24 E_t in any association of the scan.
+ */
+typedef struct ssu_ref_scan_args {
+    int32_t batch, dim, dstate, ngroups, delta_softplus, io_dtype, nthreads, reserved;
+    int64_t seqlen;
+    /* state [batch, dim, dstate] fp32, n contiguous; read, then overwritten */
+    float *state;
+    int64_t st_b, st_d;
+    /* u, delta [batch, dim, L]; B, C [batch, G, dstate, L]: io_dtype bits
+     * (0 = bf16, 1 = fp16) */
+    const uint16_t *u;
+    int64_t u_b, u_d, u_t;
+    const uint16_t *delta;
+    int64_t dl_b, dl_d, dl_t;
+    const uint16_t *B;
+    int64_t B_b, B_g, B_n, B_t;
+    const uint16_t *C;
+    int64_t C_b, C_g, C_n, C_t;
+    /* A [dim, dstate] fp32; D, delta_bias [dim] fp32 contiguous, may be NULL */
+    const float *A;
+    int64_t A_d, A_n;
+    const float *D, *delta_bias;
+    /* out [batch, dim, L] io_dtype bits */
+    uint16_t *out;
+    int64_t o_b, o_d, o_t;
+    /* optional fp64 outputs, contiguous:
+     *   state_ref [batch, dim, dstate] : h after the last token
+     *   err_ref   [batch, dim, dstate] : E after the last token
+     *   y_ref     [batch, dim, L]      : y before rounding
+     *   tau_ref   [batch, dim, L]      : sum_n |h[n] C[n]| + |D u|
+     *   rho_ref   [batch, dim, L]      : sum_n |C[n]| E[n] */
+    double *state_ref, *err_ref, *y_ref, *tau_ref, *rho_ref;
+} ssu_ref_scan_args;
+
+/* IEEE binary16 bit pattern -> value (exact): 1 sign bit, 5 exponent bits with
+ * bias 15, 10 fraction bits; exponent 0 holds the subnormals m * 2^-24. */
+double ssu_ref_f16_value(uint16_t bits)
+{
+    const int e = (bits >> 10) & 0x1F, m = bits & 0x3FF;
+    double v;
+    if (e == 0)
+        v = ldexp((double)m, -24);
+    else if (e == 31)
+        v = m ? NAN : INFINITY;
+    else
+        v = ldexp((double)(m | 0x400), e - 25);
+    return (bits & 0x8000u) ? -v : v;
+}
+
+/* fp32 -> binary16 bit pattern, round to nearest, ties to even (from the
+ * definition: scale to an integer significand in double, where it is exact,
+ * and round with rint in the default rounding mode). */
+uint16_t ssu_ref_f16_rne(float f)
+{
+    const uint16_t sign = signbit(f) ? 0x8000u : 0u;
+    const double a = fabs((double)f);
+    if (isnan(f))
+        return (uint16_t)(sign | 0x7E00u);
+    if (isinf(f))
+        return (uint16_t)(sign | 0x7C00u);
+    if (a < ldexp(1.0, -14))                     /* subnormal range */
+        return (uint16_t)(sign | (uint16_t)rint(ldexp(a, 24)));
+    int ex;
+    frexp(a, &ex);                               /* a = fr 2^ex, fr in [0.5, 1) */
+    int E = ex - 1;                              /* a in [2^E, 2^(E+1)) */
+    double r = rint(ldexp(a, 10 - E));           /* in [1024, 2048] */
+    if (r == 2048.0) {
+        r = 1024.0;
+        E += 1;
+    }
+    if (E + 15 >= 31)
+        return (uint16_t)(sign | 0x7C00u);       /* overflow: infinity */
+    return (uint16_t)(sign | (uint16_t)((E + 15) << 10) | (uint16_t)(r - 1024.0));
+}
+
+static double ref_io_value(uint16_t bits, int32_t io_dtype)
+{
+    return io_dtype ? ssu_ref_f16_value(bits) : ref_bf16_value(bits);
+}
+
+/* Returns 0 on success; 1 bad shape; 2 null pointer. */
+int32_t ssu_ref_scan(const ssu_ref_scan_args *g)
+{
+    const int32_t bs = g->batch, Dm = g->dim, N = g->dstate, G = g->ngroups, io = g->io_dtype;
+    const int64_t L = g->seqlen;
+    if (bs < 0 || Dm <= 0 || N <= 0 || G <= 0 || Dm % G != 0 || L < 0 || (io != 0 && io != 1))
+        return 1;
+    if (bs == 0)
+        return 0;
+    if (!g->state || !g->A || (L > 0 && (!g->u || !g->delta || !g->B || !g->C || !g->out)))
+        return 2;
+
+#ifdef _OPENMP
+    int nthreads = g->nthreads > 0 ? g->nthreads : omp_get_max_threads();
+#pragma omp parallel num_threads(nthreads)
+#endif
+    {
+        double *h = (double *)malloc(sizeof(double) * 3 * (size_t)N);
+        if (!h)
+            abort();
+        double *M = h + N, *E = h + 2 * N;
+#ifdef _OPENMP
+#pragma omp for schedule(static)
+#endif
+        for (int64_t bd = 0; bd < (int64_t)bs * Dm; ++bd) {
+            const int32_t b = (int32_t)(bd / Dm), d = (int32_t)(bd % Dm);
+            const int32_t grp = (int32_t)(((int64_t)d * G) / Dm);
+            float *st = g->state + b * g->st_b + d * g->st_d;
+            for (int32_t n = 0; n < N; ++n) {
+                h[n] = (double)st[n];
+                M[n] = E[n] = fabs(h[n]);
+            }
+            const double bias = g->delta_bias ? (double)g->delta_bias[d] : 0.0;
+            const double Dv = g->D ? (double)g->D[d] : 0.0;
+            const float *Ar = g->A + d * g->A_d;
+
+            for (int64_t t = 0; t < L; ++t) {
+                const double v = ref_io_value(g->delta[b * g->dl_b + d * g->dl_d + t * g->dl_t], io) + bias;
+                const double Delta = g->delta_softplus ? ssu_ref_softplus(v) : v;
+                const double ut = ref_io_value(g->u[b * g->u_b + d * g->u_d + t * g->u_t], io);
+                const uint16_t *Bt = g->B + b * g->B_b + grp * g->B_g + t * g->B_t;
+                const uint16_t *Ct = g->C + b * g->C_b + grp * g->C_g + t * g->C_t;
+                double y = 0.0, tau = 0.0, rho = 0.0;
+                for (int32_t n = 0; n < N; ++n) {
+                    const double An = (double)Ar[n * g->A_n];
+                    const double a = exp(An * Delta);
+                    const double beta = (Delta * ut) * ref_io_value(Bt[n * g->B_n], io);
+                    h[n] = h[n] * a + beta;
+                    const double Mprev = M[n];
+                    M[n] = a * M[n] + fabs(beta);
+                    E[n] = a * E[n] + (1.0 + fabs(An * Delta)) * a * Mprev + M[n];
+                    const double c = ref_io_value(Ct[n * g->C_n], io);
+                    y += h[n] * c;
+                    tau += fabs(h[n] * c);
+                    rho += fabs(c) * E[n];
+                }
+                y += Dv * ut;
+                tau += fabs(Dv * ut);
+                const float yf = (float)y;
+                g->out[b * g->o_b + d * g->o_d + t * g->o_t] = io ? ssu_ref_f16_rne(yf) : ssu_ref_bf16_rne(yf);
+                const int64_t ri = ((int64_t)b * Dm + d) * L + t;
+                if (g->y_ref)
+                    g->y_ref[ri] = y;
+                if (g->tau_ref)
+                    g->tau_ref[ri] = tau;
+                if (g->rho_ref)
+                    g->rho_ref[ri] = rho;
+            }
+
+            for (int32_t n = 0; n < N; ++n) {
+                st[n] = (float)h[n];
+                const int64_t si = ((int64_t)b * Dm + d) * N + n;
+                if (g->state_ref)
+                    g->state_ref[si] = h[n];
+                if (g->err_ref)
+                    g->err_ref[si] = E[n];
+            }
+        }
+        free(h);
+    }
+    return 0;
+}

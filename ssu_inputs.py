@@ -43,6 +43,11 @@ __all__ = [
     "sweep_points",
     "sweep_seed",
     "CONFIGS",
+    "ScanProblem",
+    "make_scan_problem",
+    "io_bits",
+    "io_values",
+    "SCAN_CONFIGS",
 ]
 
 
@@ -188,4 +193,105 @@ CONFIGS = {
     1: dict(name="H16 P64 N128 bs8", H=16, P=64, N=128, G=1, batch=8, seed=1),
     2: dict(name="H16 P64 N128 bs128", H=16, P=64, N=128, G=1, batch=128, seed=2),
     3: dict(name="H16 P64 N128 bs512", H=16, P=64, N=128, G=1, batch=512, seed=3),
+}
+
+
+# ---------------------------------------------------------------------------
+# Selective scan over a sequence (prefill)
+#
+# Shapes and distributions follow the selective_scan_fn benchmark of the COREY
+# page (COREY: Entropy-Guided Runtime Chunk Scheduling for Selective Scan
+# Kernels, Table 9, Table 17 and Table 18): batch 1, dim 1024 channels,
+# d_state 16, sequence 4096 (also 8192), FP16 (also BF16) activations drawn
+# standard normal, static chunks of 512 tokens. The page does not give the
+# parameter distributions; the recipe below takes the usual Mamba ones.
+#
+# Recipe (seeded, deterministic), ``numpy.random.Generator(PCG64([seed, 3]))``
+# drawn in this order:
+#   * u, delta : io = RNE(N(0, 1)), [batch, dim, L];
+#   * B, C     : io = RNE(N(0, 1)), [batch, G, dstate, L];
+#   * A        : fp32 = -(n + 1) * U(0.5, 1.5), [dim, dstate] (a jittered
+#                -1, -2, ..., -dstate ladder per channel);
+#   * D        : fp32 ~ U(0.5, 1.5), [dim];
+#   * delta_bias: fp32 = log(expm1(y)), y ~ U(1e-3, 0.1), [dim];
+#   * state    : fp32 zeros (a fresh sequence), or ~ N(0, 1) on request.
+# io is fp16 or bf16, rounded to nearest even.
+# ---------------------------------------------------------------------------
+
+
+def io_bits(a, io: str) -> np.ndarray:
+    """Encode float values as fp16 or bf16 bit patterns (uint16), RNE."""
+    if io == "bf16":
+        return bf16_bits(a)
+    if io == "f16":
+        return np.ascontiguousarray(np.asarray(a, dtype=np.float32).astype(np.float16)).view(np.uint16)
+    raise ValueError(f"io must be 'f16' or 'bf16', not {io!r}")
+
+
+def io_values(bits, io: str) -> np.ndarray:
+    """Decode fp16 or bf16 bit patterns to float32 (exact)."""
+    if io == "bf16":
+        return bf16_values(bits)
+    if io == "f16":
+        return np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.float16).astype(np.float32)
+    raise ValueError(f"io must be 'f16' or 'bf16', not {io!r}")
+
+
+@dataclass
+class ScanProblem:
+    """A selective scan's inputs, in storage form (numpy arrays)."""
+
+    batch: int
+    dim: int
+    dstate: int
+    ngroups: int
+    seqlen: int
+    io: str
+    delta_softplus: bool
+    seed: int
+    u: np.ndarray          # io bits [batch, dim, L]
+    delta: np.ndarray      # io bits [batch, dim, L]
+    B: np.ndarray          # io bits [batch, G, dstate, L]
+    C: np.ndarray          # io bits [batch, G, dstate, L]
+    A: np.ndarray          # fp32 [dim, dstate]
+    D: np.ndarray          # fp32 [dim]
+    delta_bias: np.ndarray  # fp32 [dim]
+    state: np.ndarray      # fp32 [batch, dim, dstate]
+
+
+def make_scan_problem(batch: int, dim: int, dstate: int, seqlen: int, ngroups: int = 1, io: str = "f16",
+                      seed: int = 0, zero_state: bool = True, delta_softplus: bool = True) -> ScanProblem:
+    """Draw a selective scan's inputs following the recipe above."""
+    if dim % ngroups:
+        raise ValueError("dim must be a multiple of ngroups")
+    rng = np.random.Generator(np.random.PCG64([seed, 3]))
+    L = seqlen
+    u = io_bits(rng.standard_normal((batch, dim, L), dtype=np.float32), io)
+    delta = io_bits(rng.standard_normal((batch, dim, L), dtype=np.float32), io)
+    B = io_bits(rng.standard_normal((batch, ngroups, dstate, L), dtype=np.float32), io)
+    C = io_bits(rng.standard_normal((batch, ngroups, dstate, L), dtype=np.float32), io)
+    A = (-(np.arange(dstate, dtype=np.float64) + 1.0) * rng.uniform(0.5, 1.5, size=(dim, dstate))).astype(np.float32)
+    D = rng.uniform(0.5, 1.5, size=dim).astype(np.float32)
+    y = rng.uniform(1e-3, 0.1, size=dim)
+    delta_bias = np.log(np.expm1(y)).astype(np.float32)
+    if zero_state:
+        state = np.zeros((batch, dim, dstate), dtype=np.float32)
+    else:
+        state = rng.standard_normal((batch, dim, dstate), dtype=np.float32)
+    return ScanProblem(batch=batch, dim=dim, dstate=dstate, ngroups=ngroups, seqlen=L, io=io,
+                       delta_softplus=delta_softplus, seed=seed, u=u, delta=delta, B=B, C=C, A=A, D=D,
+                       delta_bias=delta_bias, state=state)
+
+
+# Scan workloads: 1-3 are the page's benchmark shapes (static chunk 512);
+# 0 is a small case the oracle finishes at once, with a ragged length.
+SCAN_CONFIGS = {
+    0: dict(name="scan b2 dim64 N16 G2 L1000 f16", batch=2, dim=64, dstate=16, ngroups=2, seqlen=1000,
+            io="f16", chunk=512, seed=10),
+    1: dict(name="scan b1 dim1024 N16 L4096 f16 chunk512", batch=1, dim=1024, dstate=16, ngroups=1,
+            seqlen=4096, io="f16", chunk=512, seed=11),
+    2: dict(name="scan b1 dim1024 N16 L4096 bf16 chunk512", batch=1, dim=1024, dstate=16, ngroups=1,
+            seqlen=4096, io="bf16", chunk=512, seed=12),
+    3: dict(name="scan b1 dim1024 N16 L8192 f16 chunk512", batch=1, dim=1024, dstate=16, ngroups=1,
+            seqlen=8192, io="f16", chunk=512, seed=13),
 }

@@ -23,6 +23,17 @@ What pins what:
   * K steps         -- the fp64 scan equals the closed form of the unrolled
     recurrence, and K single steps with fp32 storage stay within rounding of it;
   * everything      -- an independent pure-Python brute force (tests/brute.py).
+  * block copy      -- numpy fancy-index assignment; skip, no-op and rejection
+    rules; strided blocks.
+Selective scan over a sequence:
+  * fp16            -- all 65536 patterns decode to numpy's float16; fp32 ->
+    fp16 rounding matches numpy (ties, subnormals, overflow, inf, NaN);
+  * the scan        -- an explicit-sum brute force (decays as one exponential
+    of summed steps, tests/brute.py); the geometric series for constant
+    inputs; A = 0 gives numpy.cumsum; A -> -1e30 forgets everything; zero
+    steps leave the state unchanged; two pieces with the state carried equal
+    the whole; the error scales bound an fp32 numpy scan (short and long
+    memory).
 """
 from __future__ import annotations
 
@@ -385,3 +396,234 @@ def pin_copy_blocks(o):
 
 
 PINS.append(pin_copy_blocks)
+
+
+# --------------------------------------------------------------------------- #
+# Selective scan over a sequence (prefill)
+# --------------------------------------------------------------------------- #
+def _scan_problem(io="f16", seed=21, batch=2, dim=4, N=3, G=2, L=9, zero_state=False, softplus=True):
+    return si.make_scan_problem(batch, dim, N, L, G, io=io, seed=seed, zero_state=zero_state,
+                                delta_softplus=softplus)
+
+
+def _scan_run(o, p, state=None, **kw):
+    state = p.state.copy() if state is None else state
+    args = dict(D=p.D, delta_bias=p.delta_bias, delta_softplus=p.delta_softplus, io=p.io)
+    args.update(kw)
+    r = o.scan(state, args.pop("u", p.u), args.pop("delta", p.delta),
+               args.pop("A", p.A), args.pop("B", p.B), args.pop("C", p.C), **args)
+    return state, r
+
+
+def _io_round(y, io):
+    """numpy's RNE of fp32(y) into the io format, as bit patterns."""
+    f = np.asarray(y, dtype=np.float64).astype(np.float32)
+    if io == "f16":
+        return f.astype(np.float16).view(np.uint16)
+    return np.array([brute._bf16_bits_of_f32(float(v)) for v in f.ravel()], dtype=np.uint16).reshape(f.shape)
+
+
+def pin_f16_decode(o):
+    """Every binary16 bit pattern decodes to numpy's float16 value."""
+    bits = np.arange(65536, dtype=np.uint32).astype(np.uint16)
+    got = o.f16_value(bits)
+    want = bits.view(np.float16).astype(np.float64)
+    nan = np.isnan(want)
+    assert np.array_equal(np.isnan(got), nan)
+    assert np.array_equal(got[~nan], want[~nan])
+    assert np.array_equal(np.signbit(got[~nan]), np.signbit(want[~nan]))
+
+
+def pin_f16_rounding(o):
+    """fp32 -> binary16 RNE matches numpy's conversion: random values across the
+    range, exact ties between neighbours (normal and subnormal), the overflow
+    threshold, signed zero, infinity and NaN."""
+    rng = _rng(31)
+    mag = np.exp2(rng.uniform(-30, 17, size=4000))
+    vals = [mag * rng.choice([-1.0, 1.0], size=mag.size)]
+    h = rng.integers(1, 0x7BFF, size=1000, dtype=np.uint16)
+    lo = h.view(np.float16).astype(np.float64)
+    hi = (h + 1).astype(np.uint16).view(np.float16).astype(np.float64)
+    vals.append((lo + hi) / 2)                       # ties, exact in fp32
+    vals.append(np.array([65504.0, 65519.99, 65520.0, 70000.0, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26,
+                          2.0 ** -14 - 2.0 ** -25, 0.0, -0.0, np.inf, -np.inf]))
+    v = np.concatenate(vals).astype(np.float32)
+    got = o.f16_rne(v)
+    with np.errstate(over="ignore"):
+        want = v.astype(np.float16).view(np.uint16)
+    assert np.array_equal(got, want), np.flatnonzero(got != want)[:5]
+    n = o.f16_rne(np.array([np.nan], dtype=np.float32))
+    assert np.isnan(n.view(np.float16)[0])
+
+
+def pin_scan_brute_force(o):
+    """The scan against the explicit-sum brute force: fp16 and bf16, softplus on
+    and off, with and without D and delta_bias, two groups."""
+    for io in ("f16", "bf16"):
+        for softplus, with_opt in ((True, True), (False, True), (True, False)):
+            p = _scan_problem(io=io, seed=22 + softplus + 2 * with_opt, softplus=softplus)
+            if not softplus:
+                # keep the steps positive and small without the softplus
+                p.delta = si.io_bits(np.abs(si.io_values(p.delta, io)) * 0.25, io)
+                p.delta_bias = np.full(p.dim, 0.01, dtype=np.float32)
+            D, bias = (p.D, p.delta_bias) if with_opt else (None, None)
+            state, r = _scan_run(o, p, D=D, delta_bias=bias)
+            h, y = brute.scan(p.state.tolist(), p.u.tolist(), p.delta.tolist(), p.A.tolist(), p.B.tolist(),
+                              p.C.tolist(), None if D is None else D.tolist(),
+                              None if bias is None else bias.tolist(), softplus, io)
+            h, y = np.array(h), np.array(y)
+            assert np.allclose(r["state"], h, rtol=1e-12, atol=1e-14), (io, softplus, with_opt)
+            assert np.all(np.abs(r["y"] - y) <= 1e-12 * (np.abs(r["tau"]) + 1e-300)), (io, softplus, with_opt)
+            assert np.array_equal(state, h.astype(np.float32))
+            assert np.array_equal(r["out"], _io_round(r["y"], io))
+
+
+def pin_scan_closed_form(o):
+    """Constant inputs: with the same step, input and B at every token, each
+    state follows the geometric series h_t = a^(t+1) h0 + beta (1 - a^(t+1)) / (1 - a),
+    a = exp(A Delta), beta = Delta u B, with a distinct decay per state."""
+    L, N, dim = 40, 4, 3
+    p = _scan_problem(batch=1, dim=dim, N=N, G=1, L=L, seed=25)
+    io = p.io
+    uval, dval = np.float32(0.75), np.float32(-0.5)
+    p.u = np.full_like(p.u, si.io_bits([uval], io)[0])
+    p.delta = np.full_like(p.delta, si.io_bits([dval], io)[0])
+    Bv = np.array([1.0, -2.0, 0.5, 3.0], dtype=np.float32)
+    p.B = np.broadcast_to(si.io_bits(Bv, io)[None, None, :, None], p.B.shape).copy()
+    p.C = np.broadcast_to(si.io_bits(np.ones(N, np.float32), io)[None, None, :, None], p.C.shape).copy()
+    state, r = _scan_run(o, p)
+    t = np.arange(L, dtype=np.float64)
+    for d in range(dim):
+        delta = np.logaddexp(0.0, float(dval) + float(p.delta_bias[d]))
+        a = np.exp(p.A[d].astype(np.float64) * delta)               # [N]
+        beta = delta * float(uval) * Bv.astype(np.float64)
+        pw = a[:, None] ** (t[None, :] + 1)                          # [N, L]
+        h = pw * p.state[0, d].astype(np.float64)[:, None] + beta[:, None] * (1 - pw) / (1 - a[:, None])
+        y = h.sum(axis=0) + float(p.D[d]) * float(uval)
+        assert np.allclose(r["y"][0, d], y, rtol=1e-12, atol=1e-13), d
+        assert np.allclose(r["state"][0, d], h[:, -1], rtol=1e-12, atol=1e-14), d
+
+
+def pin_scan_no_decay(o):
+    """A = 0: no decay, the state is the running sum of the inputs
+    (numpy.cumsum), and y = C . h + D u (numpy.einsum)."""
+    p = _scan_problem(seed=26, L=30)
+    p.A = np.zeros_like(p.A)
+    state, r = _scan_run(o, p)
+    io = p.io
+    delta = np.logaddexp(0.0, si.io_values(p.delta, io).astype(np.float64) + p.delta_bias[None, :, None])
+    u = si.io_values(p.u, io).astype(np.float64)
+    g = np.arange(p.dim) // (p.dim // p.ngroups)
+    B = si.io_values(p.B, io).astype(np.float64)[:, g]                # [b, dim, N, L]
+    C = si.io_values(p.C, io).astype(np.float64)[:, g]
+    h = p.state.astype(np.float64)[..., None] + np.cumsum((delta * u)[:, :, None, :] * B, axis=-1)
+    y = np.einsum("bdnl,bdnl->bdl", h, C) + p.D[None, :, None] * u
+    assert np.allclose(r["state"], h[..., -1], rtol=1e-12, atol=1e-13)
+    assert np.all(np.abs(r["y"] - y) <= 1e-12 * (r["tau"] + 1e-300))
+
+
+def pin_scan_memoryless(o):
+    """A -> -1e30 makes every decay exactly 0: the state is the last token's
+    input Delta u B, and y_t = C_t . (Delta_t u_t B_t) + D u_t."""
+    p = _scan_problem(seed=27, L=11)
+    p.A = np.full_like(p.A, -1e30)
+    state, r = _scan_run(o, p)
+    io = p.io
+    delta = np.logaddexp(0.0, si.io_values(p.delta, io).astype(np.float64) + p.delta_bias[None, :, None])
+    u = si.io_values(p.u, io).astype(np.float64)
+    g = np.arange(p.dim) // (p.dim // p.ngroups)
+    B = si.io_values(p.B, io).astype(np.float64)[:, g]
+    C = si.io_values(p.C, io).astype(np.float64)[:, g]
+    beta = (delta * u)[:, :, None, :] * B
+    y = np.einsum("bdnl,bdnl->bdl", beta, C) + p.D[None, :, None] * u
+    assert np.allclose(r["state"], beta[..., -1], rtol=1e-14, atol=0)
+    assert np.all(np.abs(r["y"] - y) <= 1e-13 * (r["tau"] + 1e-300))
+
+
+def pin_scan_zero_step(o):
+    """Softplus off, delta = 0 and no bias: every step is 0, the state is left
+    exactly as it was and y = C . h0 + D u."""
+    p = _scan_problem(seed=28, softplus=False)
+    p.delta = np.zeros_like(p.delta)
+    state, r = _scan_run(o, p, delta_bias=None)
+    assert np.array_equal(state, p.state)
+    io = p.io
+    g = np.arange(p.dim) // (p.dim // p.ngroups)
+    C = si.io_values(p.C, io).astype(np.float64)[:, g]
+    y = np.einsum("bdn,bdnl->bdl", p.state.astype(np.float64), C) \
+        + p.D[None, :, None] * si.io_values(p.u, io).astype(np.float64)
+    assert np.allclose(r["y"], y, rtol=1e-13, atol=1e-13)
+
+
+def pin_scan_split(o):
+    """Two scans over consecutive pieces of a sequence, the first's fp32 state
+    carried into the second, agree with one scan over the whole (up to that
+    fp32 rounding, which the error scale bounds), and the sequence of length 0
+    changes nothing."""
+    p = _scan_problem(seed=29, L=24, zero_state=False)
+    whole_state, whole = _scan_run(o, p)
+    st = p.state.copy()
+    parts = []
+    for t0, t1 in ((0, 10), (10, 24)):
+        q = si.ScanProblem(**{**p.__dict__, "u": p.u[..., t0:t1], "delta": p.delta[..., t0:t1],
+                              "B": p.B[..., t0:t1], "C": p.C[..., t0:t1], "seqlen": t1 - t0})
+        _, r = _scan_run(o, q, state=st)
+        parts.append(r)
+    y = np.concatenate([parts[0]["y"], parts[1]["y"]], axis=-1)
+    eps = 2.0 ** -24
+    assert np.all(np.abs(y - whole["y"]) <= eps * (whole["rho"] + whole["tau"]))
+    assert np.all(np.abs(st - whole["state"]) <= eps * whole["err"] + eps * np.abs(whole["state"]))
+    q = si.ScanProblem(**{**p.__dict__, "u": p.u[..., :0], "delta": p.delta[..., :0], "B": p.B[..., :0],
+                          "C": p.C[..., :0], "seqlen": 0})
+    st0 = p.state.copy()
+    _scan_run(o, q, state=st0)
+    assert np.array_equal(st0, p.state)
+
+
+def _fp32_scan(p):
+    """Sequential fp32 scan in numpy (steps, decays, products and sums rounded
+    to fp32, as a GPU kernel computes them). Returns (h, y)."""
+    f32 = np.float32
+    io = p.io
+    v = (si.io_values(p.delta, io) + p.delta_bias[None, :, None]).astype(f32)
+    delta = (np.maximum(v, f32(0)) + np.log1p(np.exp(-np.abs(v)))).astype(f32)
+    u = si.io_values(p.u, io)
+    du = (delta * u).astype(f32)
+    B = si.io_values(p.B, io)[:, 0]
+    C = si.io_values(p.C, io)[:, 0]
+    h = p.state.copy()
+    y = np.zeros(p.u.shape, f32)
+    for t in range(p.seqlen):
+        a = np.exp((p.A[None] * delta[:, :, t, None]).astype(f32)).astype(f32)
+        h = (h * a + (du[:, :, t, None] * B[:, None, :, t]).astype(f32)).astype(f32)
+        y[..., t] = ((h * C[:, None, :, t]).astype(f32).sum(axis=-1, dtype=f32)
+                     + p.D[None] * u[..., t]).astype(f32)
+    return h, y
+
+
+def pin_scan_error_scale(o):
+    """The error scales bound what fp32 arithmetic actually does: an fp32
+    sequential scan in numpy stays within 4 * 2^-24 * E of the fp64 state and
+    within 2^-24 * (rho + N tau) of y, and E >= |h| everywhere. Two regimes:
+    the input recipe (short memory, mixed signs), and a long memory (decay
+    rates ~1e-4 over 3000 tokens) with inputs of one sign, where fp32 rounding
+    errors pile up over the whole sequence."""
+    eps = 2.0 ** -24
+    p = _scan_problem(seed=30, batch=1, dim=6, N=8, G=1, L=300, zero_state=False)
+    _, r = _scan_run(o, p)
+    h, y = _fp32_scan(p)
+    assert np.all(np.abs(h - r["state"]) <= 4 * eps * r["err"])
+    assert np.all(np.abs(y - r["y"]) <= eps * (r["rho"] + p.dstate * r["tau"]))
+    assert np.all(r["err"] >= np.abs(r["state"]))
+
+    p = _scan_problem(seed=31, batch=1, dim=6, N=8, G=1, L=3000, zero_state=True)
+    p.A = np.broadcast_to(-1e-4 * (np.arange(8, dtype=np.float32) + 1), p.A.shape).astype(np.float32)
+    p.u = si.io_bits(np.abs(si.io_values(p.u, p.io)) + 0.5, p.io)
+    p.B = si.io_bits(np.abs(si.io_values(p.B, p.io)) + 0.5, p.io)
+    _, r = _scan_run(o, p)
+    h, _ = _fp32_scan(p)
+    assert np.all(np.abs(h - r["state"]) <= 4 * eps * r["err"])
+
+
+PINS.extend([pin_f16_decode, pin_f16_rounding, pin_scan_brute_force, pin_scan_closed_form, pin_scan_no_decay,
+             pin_scan_memoryless, pin_scan_zero_step, pin_scan_split, pin_scan_error_scale])

@@ -60,6 +60,36 @@ MUTANTS = [
      "            if (s < 0 || s >= t[k].nblocks) s = 0;\n"
      "            if (d < 0 || d >= t[k].nblocks) d = 0;"),
     ("copy_overlap_allowed", "            if (src[q] == dst[r] && src[q] != dst[q])\n                return 3;\n", ""),
+    # selective scan over a sequence
+    ("scan_update_sign", "h[n] = h[n] * a + beta;", "h[n] = h[n] * a - beta;"),
+    ("scan_drop_decay", "h[n] = h[n] * a + beta;", "h[n] = h[n] + beta;"),
+    ("scan_step_not_on_u", "(Delta * ut) * ref_io_value(Bt", "(ut) * ref_io_value(Bt"),
+    ("scan_C_for_B", "ref_io_value(Bt[n * g->B_n], io)", "ref_io_value(Ct[n * g->C_n], io)"),
+    ("scan_B_for_C", "const double c = ref_io_value(Ct[n * g->C_n], io);",
+     "const double c = ref_io_value(Bt[n * g->B_n], io);"),
+    ("scan_drop_D", "y += Dv * ut;", "y += 0.0 * Dv * ut;"),
+    ("scan_D_on_step", "y += Dv * ut;", "y += Dv * Delta;"),
+    ("scan_decay_sign", "exp(An * Delta)", "exp(-An * Delta)"),
+    ("scan_decay_raw_step", "exp(An * Delta)", "exp(An * v)"),
+    ("scan_drop_bias", "io) + bias;", "io);"),
+    ("scan_softplus_ignored", "g->delta_softplus ? ssu_ref_softplus(v) : v", "v"),
+    ("scan_group_map", "(((int64_t)d * G) / Dm)", "(d % G)"),
+    ("scan_A_wrong_state", "Ar[n * g->A_n]", "Ar[((n + 1) % N) * g->A_n]"),
+    ("scan_A_channel_ignored", "const float *Ar = g->A + d * g->A_d;", "const float *Ar = g->A;"),
+    ("scan_initial_state_ignored", "h[n] = (double)st[n];", "h[n] = 0.0 * st[n];"),
+    ("scan_no_write_back", "st[n] = (float)h[n];", "(void)st;"),
+    ("scan_output_before_input", "y += h[n] * c;", "y += (h[n] - beta) * c;"),
+    ("scan_step_order_reversed", "d * g->dl_d + t * g->dl_t]", "d * g->dl_d + (L - 1 - t) * g->dl_t]"),
+    ("scan_B_lagged", "grp * g->B_g + t * g->B_t", "grp * g->B_g + (t > 0 ? t - 1 : 0) * g->B_t"),
+    ("scan_out_always_bf16", "io ? ssu_ref_f16_rne(yf) : ssu_ref_bf16_rne(yf)", "ssu_ref_bf16_rne(yf)"),
+    ("scan_error_scale_no_carry", "E[n] = a * E[n] +", "E[n] = 0.0 * E[n] +"),
+    ("f16_exponent_bias", "e - 25", "e - 24"),
+    ("f16_subnormal_zero", "v = ldexp((double)m, -24);", "v = 0.0 * m;"),
+    ("f16_implicit_bit", "(m | 0x400)", "(m)"),
+    ("f16_round_truncate", "rint(ldexp(a, 10 - E))", "floor(ldexp(a, 10 - E))"),
+    ("f16_subnormal_truncate", "(uint16_t)rint(ldexp(a, 24))", "(uint16_t)floor(ldexp(a, 24))"),
+    ("f16_overflow_saturates", "if (E + 15 >= 31)\n        return (uint16_t)(sign | 0x7C00u);",
+     "if (E + 15 >= 31)\n        return (uint16_t)(sign | 0x7BFFu);"),
 ]
 
 

@@ -11,6 +11,17 @@ smaller than its terms) an fp32 sum cannot promise 2 bf16 ulp of the tiny
 result; the floor allows the error an fp32 sum of the terms can make (the
 sequential-sum bound 128 * 2^-24 * sum|terms| is 2^-17 * sum|terms|, which is
 2 ulp of 2^-10 * sum|terms|) and no more.
+
+Selective scan over a sequence (fp32 state and arithmetic, fp16/bf16 io):
+the oracle returns error scales alongside its fp64 results (E for each final
+state, rho = sum_n |C[n]| E[n] and tau = sum_n |h[n] C[n]| + |D u| for each
+output; definitions in the oracle). Bounds, with eps = 2^-24:
+  state: |S_gpu - S_ref| <= 16 eps E;
+  out:   |out_gpu - y| <= ulp_io(|y|) + 8 eps (rho + N tau).
+An fp32 numpy scan stays below 3 eps E and 0.25 eps (rho + N tau) on the input
+recipe and below 0.05 eps E with long memory; the constants leave room for the
+GPU's own exp2, softplus and association of the scan (a tree over the tokens
+of a block), and the io rounding adds at most one unit in the last place.
 """
 from __future__ import annotations
 
@@ -58,3 +69,42 @@ def out_check(out_gpu_bits, out_ref_bits, y_ref, tau_ref):
     floor_ok = np.abs(g - y) <= OUT_ULPS * bf16_ulp(np.maximum(np.abs(y), tau_p))
     ok = literal | floor_ok
     return ~ok, int(np.count_nonzero(~literal & floor_ok))
+
+
+SCAN_STATE_C = 16.0
+SCAN_OUT_C = 8.0
+EPS32 = 2.0 ** -24
+
+
+def f16_to_f64(bits) -> np.ndarray:
+    return np.ascontiguousarray(np.asarray(bits, dtype=np.uint16)).view(np.float16).astype(np.float64)
+
+
+def f16_ulp(v) -> np.ndarray:
+    """Spacing of binary16 numbers at |v| (11 significand bits; subnormal spacing 2^-24)."""
+    a = np.abs(np.asarray(v, dtype=np.float64))
+    e = np.floor(np.log2(np.where(a > 0, a, 1.0)))
+    e = np.maximum(e, -14.0)
+    return np.where(a > 0, np.exp2(e - 10.0), 2.0 ** -24)
+
+
+def io_to_f64(bits, io):
+    return f16_to_f64(bits) if io == "f16" else bf16_to_f64(bits)
+
+
+def io_ulp(v, io):
+    return f16_ulp(v) if io == "f16" else bf16_ulp(v)
+
+
+def scan_state_violations(gpu, ref, err) -> np.ndarray:
+    """Boolean mask of final states outside 16 eps E."""
+    g = np.asarray(gpu, dtype=np.float64)
+    return ~(np.abs(g - np.asarray(ref)) <= SCAN_STATE_C * EPS32 * np.asarray(err))
+
+
+def scan_out_violations(out_bits, y_ref, tau_ref, rho_ref, dstate, io) -> np.ndarray:
+    """Boolean mask of outputs outside ulp_io(|y|) + 8 eps (rho + N tau)."""
+    g = io_to_f64(out_bits, io)
+    y = np.asarray(y_ref, dtype=np.float64)
+    tol = io_ulp(y, io) + SCAN_OUT_C * EPS32 * (np.asarray(rho_ref) + dstate * np.asarray(tau_ref))
+    return ~(np.abs(g - y) <= tol)
