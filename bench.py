@@ -23,6 +23,7 @@ bounded sample of the same workload.
     python bench.py --sweep [--heads 16] [--out FILE]   per-point GB/s (no JSON line)
     python bench.py --counters                          short eager run for rocprofv3 --pmc
     python bench.py --summarize-counters DIR --write-profile NAME
+    python bench.py --scan 1,2,3 [--chunks 64,...,4096]  selective scan (prefill) per sequence
 """
 from __future__ import annotations
 
@@ -69,17 +70,27 @@ def algorithmic_bytes(H, P, N, G, batch):
             + 4 * batch + 12 * H + 2 * batch * H * P)
 
 
-def source_digest() -> str:
-    """Hash of the decode kernel's source code (its file and the shared
-    header): comments and whitespace are removed first, so only a change to
-    the code itself invalidates counter data."""
+def scan_source_digest() -> str:
+    """Hash of the scan kernel's source (comments and whitespace stripped)."""
+    return _digest([os.path.join(ROOT, "selective_state_update_amd", "csrc", "scan.hip"),
+                    os.path.join(ROOT, "selective_state_update_amd", "csrc", "internal.h")])
+
+
+def _digest(files) -> str:
+    """Hash of source files with comments and whitespace removed, so that only
+    a change to the code itself invalidates counter data."""
     import re
 
-    text = "\n".join(open(f).read() for f in KERNEL_SRCS)
+    text = "\n".join(open(f).read() for f in files)
     text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
     text = re.sub(r"//[^\n]*", " ", text)
     text = " ".join(text.split())
     return hashlib.sha256(text.encode()).hexdigest()[:16]
+
+
+def source_digest() -> str:
+    """Hash of the decode kernel's source code (its file and the shared header)."""
+    return _digest(KERNEL_SRCS)
 
 
 # --------------------------------------------------------------------------- #
@@ -411,6 +422,22 @@ def run_copy_ceiling(a):
               f"({100 * moved / us / 1e3 / HBM_PEAK_GBS:.1f}% of 8 TB/s)", flush=True)
 
 
+def time_graph_on(g, replays, stream):
+    """Seconds for `replays` replays of a graph captured on `stream`, with
+    events recorded on that stream."""
+    import torch
+
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    with torch.cuda.stream(stream):
+        e0.record(stream)
+        for _ in range(replays):
+            g.replay()
+        e1.record(stream)
+    e1.synchronize()
+    return e0.elapsed_time(e1) * 1e-3
+
+
 def tokens_bytes(H, P, N, G, batch, K):
     """Bytes of one K-token call: the state read and written once, then K
     tokens' x, B, C, dt and out, plus idx and the per-head parameters."""
@@ -520,6 +547,146 @@ def run_copy_blocks(a):
         torch.cuda.empty_cache()
 
 
+# Selective scan over a sequence (prefill): the COREY page's kernel benchmark
+# (Table 9, Table 17, Table 18): batch 1, dim 1024, d_state 16, L 4096 (8192),
+# FP16 (BF16), static chunks of 512 tokens, one launch per chunk.
+def scan_bytes(batch, dim, N, G, L):
+    """Algorithmic HBM bytes of one scanned sequence: u, delta and out (16-bit)
+    once, B and C (16-bit) once, the fp32 state read and written once, A, D and
+    delta_bias once."""
+    return 2 * 3 * batch * dim * L + 2 * 2 * batch * G * N * L + 8 * batch * dim * N + 4 * dim * (N + 2)
+
+
+def scan_elements(batch, dim, N, L):
+    """(request, channel, state, token) elements of one sequence."""
+    return batch * dim * N * L
+
+
+def run_scan(a):
+    """ssu_scan on the page's shapes (configs from --scan), for every chunk in
+    --chunks. Input sets (u, delta, B, C, out, state) rotate so that the sets
+    together hold >= 768 MiB (cold HBM, as in prefill where each layer's
+    activations are produced just before); K sequences captured in one HIP
+    graph, median of 5 x 10 replays. One line per (config, chunk)."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    out = open(a.out, "w") if a.out else sys.stdout
+    print("config chunk launches us_per_seq ms_per_seq Mtokens_per_s GBps hbm_pct Gelem_per_s tile",
+          file=out, flush=True)
+    chunks = [int(c) for c in a.chunks.split(",")]
+    for k in [int(c) for c in a.scan.split(",")]:
+        cfg = dict(si.SCAN_CONFIGS[k])
+        name = cfg.pop("name")
+        cfg.pop("chunk")
+        bs, dim, N, G, L = cfg["batch"], cfg["dim"], cfg["dstate"], cfg["ngroups"], cfg["seqlen"]
+        nbytes = scan_bytes(bs, dim, N, G, L)
+        K = max(2, -(-ROTATION_BYTES // nbytes))
+        sets = []
+        for i in range(K):
+            p = si.make_scan_problem(**{**cfg, "seed": cfg["seed"] * 1000 + i}) if i < 2 else None
+            if p is None:
+                # further sets: the first two sets' inputs at new addresses (same values)
+                sets.append({key: t.clone() for key, t in sets[i % 2].items()})
+                continue
+            dt = torch.float16 if p.io == "f16" else torch.bfloat16
+
+            def dev(bits, dt=dt):
+                return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt).cuda()
+
+            sets.append(dict(u=dev(p.u), delta=dev(p.delta), B=dev(p.B), C=dev(p.C),
+                             A=torch.from_numpy(p.A).cuda(), D=torch.from_numpy(p.D).cuda(),
+                             bias=torch.from_numpy(p.delta_bias).cuda(),
+                             state=torch.from_numpy(p.state).cuda(),
+                             out=torch.empty((bs, dim, L), dtype=dt, device="cuda")))
+        args = [ssu.make_scan_args(s["u"], s["delta"], s["A"], s["B"], s["C"], s["state"], s["D"], s["bias"],
+                                   True, s["out"])[0] for s in sets]
+        tiles = range(len(ssu.scan_tiles())) if a.tile_sweep else [a.tile]
+        for chunk in chunks:
+            for tile in tiles:
+                launches = -(-L // chunk) if chunk > 0 else 1
+                calls = max(K, 8)
+                side = torch.cuda.Stream()
+                with torch.cuda.stream(side):
+                    ssu.scan_launch(args[0], chunk, tile, stream=side)
+                torch.cuda.synchronize()
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(calls):
+                        ssu.scan_launch(args[i % K], chunk, tile, stream=side)
+                g.replay()
+                torch.cuda.synchronize()
+                us = statistics.median([time_graph_on(g, 10, side) / (10 * calls) for _ in range(5)]) * 1e6
+                gbs = nbytes / (us * 1e-6) / 1e9
+                tname = ssu.scan_tiles()[tile] if tile >= 0 else "default"
+                print(f"{k} {chunk} {launches} {us:.2f} {us / 1e3:.4f} {bs * L / us:.2f} {gbs:.1f} "
+                      f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {tname}",
+                      file=out, flush=True)
+                del g
+        del sets, args
+        torch.cuda.empty_cache()
+
+
+def scan_launch_bytes(batch, dim, N, G, tokens):
+    """Algorithmic HBM bytes of one scan launch over `tokens` tokens: its share
+    of u, delta, out, B and C, plus the state read and written and A, D and
+    delta_bias read once per launch."""
+    return 2 * 3 * batch * dim * tokens + 2 * 2 * batch * G * N * tokens + 8 * batch * dim * N + 4 * dim * (N + 2)
+
+
+def _copy_reference():
+    """A plain device copy of known size (256 MiB read + 256 MiB written), cold,
+    four times: what FETCH_SIZE / WRITE_SIZE read for it scales the counters."""
+    import torch
+
+    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").normal_()
+    dst = torch.empty_like(src)
+    bufs = [torch.empty_like(src) for _ in range(3)]  # evict src from the cache between copies
+    for i in range(4):
+        for b in bufs:
+            b.fill_(float(i))
+        torch.mul(src, 2.0, out=dst)  # one elementwise kernel: reads src once, writes dst once
+    torch.cuda.synchronize()
+    return src.numel() * 4
+
+
+def run_scan_counters(a):
+    """Eager scans for a rocprofv3 --pmc pass: `a.steps` sequences of scan
+    config `a.scan` at its static chunk, over 4 input sets of which each is
+    evicted from the cache before reuse, then the reference copy."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    k = int(a.scan)
+    cfg = dict(si.SCAN_CONFIGS[k])
+    cfg.pop("name")
+    chunk = cfg.pop("chunk")
+    dt = torch.float16 if cfg["io"] == "f16" else torch.bfloat16
+    sets = []
+    for i in range(4):
+        p = si.make_scan_problem(**{**cfg, "seed": cfg["seed"] * 1000 + i})
+
+        def dev(bits):
+            return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt).cuda()
+
+        t = dict(u=dev(p.u), delta=dev(p.delta), B=dev(p.B), C=dev(p.C), A=torch.from_numpy(p.A).cuda(),
+                 D=torch.from_numpy(p.D).cuda(), bias=torch.from_numpy(p.delta_bias).cuda(),
+                 state=torch.from_numpy(p.state).cuda())
+        t["args"] = ssu.make_scan_args(t["u"], t["delta"], t["A"], t["B"], t["C"], t["state"], t["D"],
+                                       t["bias"])[0]
+        sets.append(t)
+    flush = torch.empty(3 * LLC_BYTES // 4, dtype=torch.float32, device="cuda")
+    for i in range(a.steps):
+        flush.fill_(float(i))  # evicts the previous sequence's inputs from the Infinity Cache
+        ssu.scan_launch(sets[i % 4]["args"], chunk, a.tile)
+    torch.cuda.synchronize()
+    n = _copy_reference()
+    print(f"# scan counters pass: {a.steps} sequences of config {k} at chunk {chunk}, 4 copies of {n} bytes",
+          flush=True)
+
+
 def run_counters(a):
     """Eager calls for a rocprofv3 --pmc pass: `a.steps` headline calls rotating
     over the slot sets, then a plain device copy of a known size (256 MiB read
@@ -536,32 +703,81 @@ def run_counters(a):
     for i in range(a.steps):
         h.launch(args[i % len(args)])
     torch.cuda.synchronize()
-    src = torch.empty(64 * 1024 * 1024, dtype=torch.float32, device="cuda").normal_()
-    dst = torch.empty_like(src)
-    bufs = [torch.empty_like(src) for _ in range(3)]  # evict src from the cache between copies
-    for i in range(4):
-        for b in bufs:
-            b.fill_(float(i))
-        torch.mul(src, 2.0, out=dst)  # one elementwise kernel: reads src once, writes dst once
-    torch.cuda.synchronize()
-    print(f"# counters pass: {a.steps} ssu calls, 4 copies of {src.numel() * 4} bytes", flush=True)
+    n = _copy_reference()
+    print(f"# counters pass: {a.steps} ssu calls, 4 copies of {n} bytes", flush=True)
+
+
+def _load_counter(dirpath, counter):
+    """(kernel name, value) rows of one counter from rocprofv3 --pmc CSV output."""
+    import csv
+    import glob
+
+    rows = []
+    for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
+        with open(f) as fh:
+            for r in csv.DictReader(fh):
+                if r.get("Counter_Name") == counter:
+                    rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
+    return rows
+
+
+SCAN_COUNTER_PROFILE = os.path.join(ROOT, "profiles", "ssu_scan_dim1024_L4096_f16_chunk512_counters.md")
+
+
+def summarize_scan_counters(a):
+    """Counter summary for the scan kernel (see run_scan_counters)."""
+    fetch_dir, write_dir = a.summarize_scan_counters.split(",")
+    fetch, write = _load_counter(fetch_dir, "FETCH_SIZE"), _load_counter(write_dir, "WRITE_SIZE")
+    fs = [v for k, v in fetch if "ssu_scan_kernel" in k]
+    ws = [v for k, v in write if "ssu_scan_kernel" in k]
+    fc = [v for k, v in fetch if "MulFunctor" in k]
+    wc = [v for k, v in write if "MulFunctor" in k]
+    if not fs or not ws or not fc or not wc:
+        raise SystemExit("no counter rows found")
+    copy_bytes = 64 * 1024 * 1024 * 4
+    f_scale = copy_bytes / (statistics.median(fc) * 1024)
+    w_scale = copy_bytes / (statistics.median(wc) * 1024)
+    k = int(a.scan)
+    c = si.SCAN_CONFIGS[k]
+    per_launch = scan_launch_bytes(c["batch"], c["dim"], c["dstate"], c["ngroups"], c["chunk"])
+    f_b = statistics.median(fs) * 1024 * f_scale
+    w_b = statistics.median(ws) * 1024 * w_scale
+    cmd = f"python3 bench.py --scan {k} --scan-counters --steps {a.steps}"
+    text = f"""# rocprofv3 HBM counters: ssu_scan_kernel, {c['name']}
+
+Commands (run from the repository root on one MI355X):
+
+    rocprofv3 --pmc FETCH_SIZE -f csv -d {a.fetch_dir_name} -o run -- {cmd}
+    rocprofv3 --pmc WRITE_SIZE -f csv -d {a.write_dir_name} -o run -- {cmd}
+    python3 bench.py --scan {k} --summarize-scan-counters {a.fetch_dir_name},{a.write_dir_name} --write-profile
+
+Counters are KiB per dispatch, scaled by the ratio (known bytes / counter) of a
+plain device copy of 268435456 bytes read + 268435456 written in the same run.
+Each dispatch is one chunk of {c['chunk']} tokens; the Infinity Cache is
+flushed between sequences.
+
+- scan_code_digest: `{scan_source_digest()}`
+- scan_dispatches: {len(fs)}
+- fetch_kib_median: {statistics.median(fs):.1f}
+- write_kib_median: {statistics.median(ws):.1f}
+- fetch_scale: {f_scale:.4f}
+- write_scale: {w_scale:.4f}
+- fetch_bytes_per_launch: {f_b:.0f}
+- write_bytes_per_launch: {w_b:.0f}
+- traffic_bytes_per_launch: {f_b + w_b:.0f}
+- algorithmic_bytes_per_launch: {per_launch}
+- traffic_over_algorithmic: {(f_b + w_b) / per_launch:.4f}
+"""
+    if a.write_profile:
+        with open(SCAN_COUNTER_PROFILE, "w") as f:
+            f.write(text)
+    print(text)
 
 
 def summarize_counters(a):
     """Read rocprofv3 --pmc CSV output (FETCH_SIZE and WRITE_SIZE runs) and write
     the counter summary that the JSON line's roofline.traffic comes from."""
-    import csv
-    import glob
-
-    def load(dirpath, counter):
-        rows = []
-        for f in glob.glob(os.path.join(dirpath, "**", "*counter_collection.csv"), recursive=True):
-            with open(f) as fh:
-                for r in csv.DictReader(fh):
-                    if r.get("Counter_Name") == counter:
-                        rows.append((r["Kernel_Name"], float(r["Counter_Value"])))
-        return rows
-
+    load = _load_counter
     fetch_dir, write_dir = a.summarize_counters.split(",")
     fetch = load(fetch_dir, "FETCH_SIZE")
     write = load(write_dir, "WRITE_SIZE")
@@ -633,6 +849,10 @@ def main():
     ap.add_argument("--copy-ceiling", action="store_true")
     ap.add_argument("--tokens", default="", help="comma list of tokens per call (ssu_update_tokens)")
     ap.add_argument("--copy-blocks", default="", help="comma list of request counts (ssu_copy_blocks)")
+    ap.add_argument("--scan", default="", help="comma list of scan configs (ssu_scan), e.g. 1,2,3")
+    ap.add_argument("--chunks", default="512", help="comma list of scan chunk sizes (0: one launch)")
+    ap.add_argument("--scan-counters", action="store_true", help="eager scans for rocprofv3 --pmc")
+    ap.add_argument("--summarize-scan-counters", default="")
     ap.add_argument("--summarize-counters", default="")
     ap.add_argument("--write-profile", action="store_true")
     ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
@@ -644,6 +864,12 @@ def main():
         sys.exit(2)
     if a.summarize_counters:
         summarize_counters(a)
+    elif a.summarize_scan_counters:
+        summarize_scan_counters(a)
+    elif a.scan and a.scan_counters:
+        run_scan_counters(a)
+    elif a.scan:
+        run_scan(a)
     elif a.counters:
         run_counters(a)
     elif a.tile_sweep:

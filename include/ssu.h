@@ -65,7 +65,8 @@ typedef enum ssu_dtype {
     SSU_F32 = 0,
     SSU_BF16 = 1,
     SSU_I32 = 2,
-    SSU_I64 = 3
+    SSU_I64 = 3,
+    SSU_F16 = 4 /* IEEE binary16 (ssu_scan activations) */
 } ssu_dtype;
 
 /* Problem shape and options, fixed for the life of a handle. */
@@ -249,6 +250,63 @@ ssu_status ssu_copy_blocks(const ssu_block_tensor *tensors, int32_t ntensors, co
  * range). */
 int32_t ssu_copy_tile_count(void);
 const char *ssu_copy_tile_name(int32_t tile);
+
+/* ------------------------------------------------ selective scan (prefill) --
+ * The selective scan over a whole sequence, as used to prefill a request
+ * before decoding (COREY: Entropy-Guided Runtime Chunk Scheduling for
+ * Selective Scan Kernels, Table 9, Table 17 and Table 18: selective_scan_fn
+ * over dim channels with d_state states each, FP16 or BF16 activations, the
+ * sequence cut into static chunks with one kernel call per chunk and the
+ * state carried between calls). For every request b, channel d and token t in
+ * order, with g = d / (dim / ngroups):
+ *   Delta  = softplus(delta[b,d,t] + delta_bias[d])   (delta_softplus = 1)
+ *          = delta[b,d,t] + delta_bias[d]             (delta_softplus = 0)
+ *   h[n]   = h[n] * exp(A[d,n] * Delta) + (Delta * u[b,d,t]) * B[b,g,n,t]
+ *   out[t] = sum_n h[n] * C[b,g,n,t] + D[d] * u[b,d,t]
+ * h starts from state[b,d,:] and is written back there after the last token,
+ * so a sequence may also be scanned piecewise over several calls. Arithmetic
+ * is fp32; out is rounded to the activation type (nearest even).
+ */
+typedef struct ssu_scan_args {
+    int32_t batch;          /* >= 0 (0: no-op) */
+    int32_t dim;            /* channels, >= 1 */
+    int32_t dstate;         /* states per channel, 1 .. 64 */
+    int32_t ngroups;        /* B/C groups, divides dim */
+    int64_t seqlen;         /* L >= 0 tokens (0: nothing to do) */
+    int32_t delta_softplus; /* 1 or 0, see above */
+    int32_t reserved;       /* must be 0 */
+    ssu_view state;         /* [batch, dim, dstate] F32, read and written; stride[2] == 1 */
+    ssu_view u;             /* [batch, dim, L] F16 or BF16; stride[2] == 1 */
+    ssu_view delta;         /* [batch, dim, L], u's dtype; stride[2] == 1 */
+    ssu_view B;             /* [batch, ngroups, dstate, L], u's dtype; stride[3] == 1 */
+    ssu_view C;             /* [batch, ngroups, dstate, L], u's dtype; stride[3] == 1 */
+    ssu_view A;             /* [dim, dstate] F32, finite */
+    ssu_view D;             /* [dim] F32, contiguous; ptr may be NULL (no skip term) */
+    ssu_view delta_bias;    /* [dim] F32, contiguous; ptr may be NULL (no bias) */
+    ssu_view out;           /* [batch, dim, L], u's dtype, written; stride[2] == 1 */
+} ssu_scan_args;
+
+/* Enqueue the scan of `args` on `stream` in ceil(L / chunk) kernel launches
+ * of `chunk` tokens each, in order, the state carried between them through
+ * `state` (chunk = 0: the whole sequence in one launch). Chunks whose size is
+ * a multiple of 512 give bitwise the same results as one launch; other chunk
+ * sizes agree within rounding. tile = -1 picks the launch configuration from
+ * the chunk size; 0 .. ssu_scan_tile_count()-1 forces one.
+ * Memory: the caller owns every buffer; the library allocates nothing and
+ * keeps no pointer after the call. out and state must not overlap each other
+ * or any input (the kernel reads inputs through the read-only cache).
+ * Asynchronous and graph-capturable; nothing is checked on the device.
+ * Errors (nothing is launched): SSU_ERR_INVALID_ARGUMENT (null pointers,
+ * negative sizes, wrong dtypes, dim % ngroups != 0, tile out of range),
+ * SSU_ERR_UNSUPPORTED (non-contiguous token or state axis, dstate > 64,
+ * batch * dim >= 2^31), SSU_ERR_MISALIGNED (elements not aligned to their
+ * size), SSU_ERR_HIP (launch failure; earlier chunks may have run). */
+ssu_status ssu_scan(const ssu_scan_args *args, int64_t chunk, int32_t tile, hipStream_t stream);
+
+/* Number of compiled scan configurations, and the name of one ("" if out of
+ * range). */
+int32_t ssu_scan_tile_count(void);
+const char *ssu_scan_tile_name(int32_t tile);
 
 /* SSU_ABI_VERSION of the built library. */
 int32_t ssu_abi_version(void);

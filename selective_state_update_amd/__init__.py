@@ -31,6 +31,11 @@ __all__ = [
     "TokensArgs",
     "copy_blocks",
     "copy_tiles",
+    "ScanArgs",
+    "make_scan_args",
+    "selective_scan",
+    "scan_launch",
+    "scan_tiles",
     "tiles",
     "library_path",
     "abi_version",
@@ -61,7 +66,7 @@ STATUS_NAMES = {
     6: "SSU_ERR_BAD_INDEX",
 }
 # ssu_dtype
-SSU_F32, SSU_BF16, SSU_I32, SSU_I64 = 0, 1, 2, 3
+SSU_F32, SSU_BF16, SSU_I32, SSU_I64, SSU_F16 = 0, 1, 2, 3, 4
 
 
 class Config(ctypes.Structure):
@@ -87,6 +92,13 @@ class TokensArgs(ctypes.Structure):
 
 class BlockTensor(ctypes.Structure):
     _fields_ = [("base", _vp), ("block_stride", _i64), ("block_bytes", _i64), ("nblocks", _i64)]
+
+
+class ScanArgs(ctypes.Structure):
+    _fields_ = [("batch", _i32), ("dim", _i32), ("dstate", _i32), ("ngroups", _i32), ("seqlen", _i64),
+                ("delta_softplus", _i32), ("reserved", _i32),
+                ("state", View), ("u", View), ("delta", View), ("B", View), ("C", View), ("A", View),
+                ("D", View), ("delta_bias", View), ("out", View)]
 
 
 class TileDesc(ctypes.Structure):
@@ -122,6 +134,12 @@ _lib.ssu_copy_tile_count.argtypes = []
 _lib.ssu_copy_tile_count.restype = _i32
 _lib.ssu_copy_tile_name.argtypes = [_i32]
 _lib.ssu_copy_tile_name.restype = ctypes.c_char_p
+_lib.ssu_scan.argtypes = [ctypes.POINTER(ScanArgs), _i64, _i32, _vp]
+_lib.ssu_scan.restype = _i32
+_lib.ssu_scan_tile_count.argtypes = []
+_lib.ssu_scan_tile_count.restype = _i32
+_lib.ssu_scan_tile_name.argtypes = [_i32]
+_lib.ssu_scan_tile_name.restype = ctypes.c_char_p
 _lib.ssu_abi_version.argtypes = []
 _lib.ssu_abi_version.restype = _i32
 
@@ -163,7 +181,8 @@ def _torch():
 
 def _dtype_tag(t, allowed, name):
     torch = _torch()
-    tags = {torch.float32: SSU_F32, torch.bfloat16: SSU_BF16, torch.int32: SSU_I32, torch.int64: SSU_I64}
+    tags = {torch.float32: SSU_F32, torch.bfloat16: SSU_BF16, torch.int32: SSU_I32, torch.int64: SSU_I64,
+            torch.float16: SSU_F16}
     tag = tags.get(t.dtype)
     if tag not in allowed:
         raise TypeError(f"{name}: dtype {t.dtype} not supported here")
@@ -425,3 +444,84 @@ def copy_blocks(tensors, src_blocks, dst_blocks, tile=-1, stream=None, descs=Non
                               src_blocks.shape[0], tile, _vp(stream))
     if st != SSU_OK:
         raise SSUError(st, "ssu_copy_blocks")
+
+
+# --------------------------------------------------------------------------- #
+# Selective scan over a sequence (prefill): ssu_scan
+# --------------------------------------------------------------------------- #
+def scan_tiles():
+    """Names of the compiled scan configurations (index = tile id)."""
+    return [_lib.ssu_scan_tile_name(i).decode() for i in range(_lib.ssu_scan_tile_count())]
+
+
+def make_scan_args(u, delta, A, B, C, state, D=None, delta_bias=None, delta_softplus=True, out=None):
+    """ScanArgs for ssu_scan from torch GPU tensors.
+
+    u, delta: [batch, dim, L] float16 or bfloat16 (token axis contiguous);
+    B, C: [batch, G, dstate, L] same dtype; A: [dim, dstate] float32;
+    state: [batch, dim, dstate] float32 (dstate contiguous), read and written;
+    D, delta_bias: [dim] float32 or None. out (optional): like u.
+    Returns (ScanArgs, out); the tensors must stay alive while it is used."""
+    torch = _torch()
+    if u.dim() != 3:
+        raise ValueError("u must be [batch, dim, L]")
+    bs, dim, L = u.shape
+    if B.dim() != 4 or B.shape[0] != bs or B.shape[3] != L:
+        raise ValueError("B must be [batch, G, dstate, L]")
+    G, N = B.shape[1], B.shape[2]
+    for name, t, shp in (("delta", delta, (bs, dim, L)), ("C", C, (bs, G, N, L)), ("A", A, (dim, N)),
+                         ("state", state, (bs, dim, N))):
+        if tuple(t.shape) != shp:
+            raise ValueError(f"{name} shape {tuple(t.shape)} != {shp}")
+    io = (SSU_F16, SSU_BF16)
+    ut = _dtype_tag(u, io, "u")
+    for name, t in (("delta", delta), ("B", B), ("C", C)):
+        if _dtype_tag(t, io, name) != ut:
+            raise TypeError(f"{name} must have u's dtype")
+    for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("A", A), ("state", state)):
+        if t.device.type != "cuda":
+            raise ValueError(f"{name} must be on a GPU")
+    if out is None:
+        out = torch.empty((bs, dim, L), dtype=u.dtype, device=u.device)
+    elif tuple(out.shape) != (bs, dim, L) or out.dtype != u.dtype:
+        raise ValueError("out must be like u")
+    a = ScanArgs()
+    a.batch, a.dim, a.dstate, a.ngroups, a.seqlen = bs, dim, N, G, L
+    a.delta_softplus, a.reserved = int(bool(delta_softplus)), 0
+    a.state = _view(state, state.stride(), _dtype_tag(state, (SSU_F32,), "state"))
+    a.u = _view(u, u.stride(), ut)
+    a.delta = _view(delta, delta.stride(), ut)
+    a.B = _view(B, B.stride(), ut)
+    a.C = _view(C, C.stride(), ut)
+    a.A = _view(A, A.stride(), _dtype_tag(A, (SSU_F32,), "A"))
+    for name, t in (("D", D), ("delta_bias", delta_bias)):
+        if t is None:
+            setattr(a, name, _null_view())
+            continue
+        if tuple(t.shape) != (dim,) or not t.is_contiguous():
+            raise ValueError(f"{name} must be a contiguous [dim] tensor")
+        setattr(a, name, _view(t, t.stride(), _dtype_tag(t, (SSU_F32,), name)))
+    a.out = _view(out, out.stride(), ut)
+    return a, out
+
+
+def scan_launch(args, chunk=0, tile=-1, stream=None):
+    """ssu_scan on prepared ScanArgs (for timing loops and graph capture)."""
+    torch = _torch()
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    st = _lib.ssu_scan(ctypes.byref(args), int(chunk), int(tile), _vp(stream))
+    if st != SSU_OK:
+        raise SSUError(st, "ssu_scan")
+
+
+def selective_scan(u, delta, A, B, C, state, D=None, delta_bias=None, delta_softplus=True, out=None,
+                   chunk=0, tile=-1, stream=None):
+    """Scan a sequence (see include/ssu.h, ssu_scan): ``state`` advances in place
+    over all L tokens, in launches of ``chunk`` tokens (0: one launch).
+    Returns out [batch, dim, L] in u's dtype."""
+    args, out = make_scan_args(u, delta, A, B, C, state, D, delta_bias, delta_softplus, out)
+    scan_launch(args, chunk, tile, stream)
+    return out

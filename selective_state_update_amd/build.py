@@ -15,7 +15,7 @@ import sys
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(HERE)
-SRCS = [os.path.join(HERE, "csrc", "ssu.hip"), os.path.join(HERE, "csrc", "block_copy.hip")]
+SRCS = [os.path.join(HERE, "csrc", n) for n in ("ssu.hip", "block_copy.hip", "scan.hip")]
 LIB = os.path.join(HERE, "libssu.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 

@@ -1,0 +1,630 @@
+// scan.hip -- ssu_scan: the selective scan over a sequence (prefill) on
+// MI355X (gfx950).
+//
+// What it computes (COREY: Entropy-Guided Runtime Chunk Scheduling for
+// Selective Scan Kernels, Table 9, Table 17 and Table 18, the selective_scan_fn
+// benchmark: dim channels with d_state states each, FP16 or BF16 activations,
+// the sequence cut into static chunks of tokens, one kernel call per chunk
+// with the state carried between calls): for every request b, channel d and
+// token t in order,
+//   Delta = softplus(delta[b,d,t] + delta_bias[d])   (or without the softplus)
+//   h[n]  = h[n] * exp(A[d,n] * Delta) + (Delta * u[b,d,t]) * B[b,g,n,t]
+//   y[t]  = sum_n h[n] * C[b,g,n,t] + D[d] * u[b,d,t]
+// with g = d / (dim / G), h read from and written back to the fp32 state.
+//
+// Work split. One wave per (request, channel). Tokens go in blocks of
+// 64 * SEG: lane l owns tokens l*SEG .. l*SEG+SEG-1 of a block, so a block's
+// activations are one coalesced vector load per lane. Per state n the
+// recurrence h -> a h + b is a composition of affine maps, and composition is
+// associative:
+//   1. each lane composes its SEG pairs (a_j, b_j) into one map (P, Q);
+//   2. a 64-lane inclusive scan of the maps in a fixed tree (DPP row shifts
+//      1, 2, 4, 8, then row broadcasts 15 and 31) gives every lane the map
+//      from the block's start to its last token; applied to the carried state
+//      it is the state after that token;
+//   3. shifted one lane up (lane 0 takes the carried state) it is each lane's
+//      start state; each lane replays its tokens from there and accumulates
+//      y_j += h_j C_j;
+//   4. lane 63's end state is the carried state for the next block.
+// The carried state is wave-uniform (one register per state), so blocks, and
+// launches that start on a block boundary, continue from exactly the value the
+// previous block ended with: chunkings whose chunks are multiples of 64 * SEG
+// give bitwise identical results.
+//
+// States per wave: NSW = 16 or 8 (a launch configuration). A channel's
+// workgroup has W = ceil(dstate / NSW) waves, NSW states each. More waves per
+// channel hide more latency at the price of computing the step sizes in every
+// wave; a one-wave instantiation has the whole register file to itself.
+//
+// y is summed in one fixed order whatever the configuration: states in groups
+// of 8, each group's partial accumulated in state order (fma), the groups
+// added in group order (waves other than the first hand their groups' partials
+// over through LDS). With the same token segment, every configuration and
+// every chunking on block boundaries gives bitwise the same outputs.
+//
+// Invalid tokens (past the end of a ragged last block) get Delta = 0 and u = 0:
+// their decay is exp2(0) = 1 and their input 0, the identity map, so they
+// leave every scan value unchanged.
+
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdint>
+#include <cstdio>
+
+#include "internal.h"
+
+namespace ssu {
+namespace {
+
+constexpr int kLanes = 64;
+constexpr int kMaxStates = 64;
+constexpr int kGroup = 8;  // states per partial sum of y
+constexpr float kLog2e = 1.44269504088896340736f;
+
+struct ScanParams {
+    const uint16_t *u, *delta, *B, *C;
+    uint16_t *out;
+    float *state;
+    const float *A, *D, *bias;
+    int64_t u_b, u_d, dl_b, dl_d, B_b, B_g, B_n, C_b, C_g, C_n, o_b, o_d, st_b, st_d, A_d, A_n;
+    int64_t t0, t1;
+    int32_t dim, dstate, ch_per_group, softplus, vec;
+};
+
+template <bool F16>
+__device__ __forceinline__ float io_to_f32(uint32_t bits)
+{
+    if constexpr (F16)
+        return static_cast<float>(__builtin_bit_cast(_Float16, static_cast<uint16_t>(bits)));
+    else
+        return __uint_as_float(bits << 16);
+}
+
+template <bool F16>
+__device__ __forceinline__ uint16_t f32_to_io(float f)
+{
+    if constexpr (F16) {
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, round to nearest even
+    } else {
+        uint32_t w = __float_as_uint(f);
+        if ((w & 0x7fffffffu) > 0x7f800000u)
+            return static_cast<uint16_t>((w >> 16) | 0x40u);  // NaN stays a quiet NaN
+        w += 0x7fffu + ((w >> 16) & 1u);
+        return static_cast<uint16_t>(w >> 16);
+    }
+}
+
+// Tokens tok .. tok+SEG-1 of a row, packed two per word. FAST: all of them
+// lie before t1 and the row is aligned for one vector load. Otherwise each is
+// read from an address clamped into [0, t1) (always valid) and tokens at or
+// past t1 read as 0; the loads stay unconditional, so they issue back to back.
+template <int SEG, bool FAST>
+__device__ __forceinline__ void load_seg(const uint16_t *row, int64_t tok, int64_t t1, uint32_t (&w)[(SEG + 1) / 2])
+{
+    if constexpr (FAST) {
+        const uint16_t *p = row + tok;
+        if constexpr (SEG == 8) {
+            const auto x = *reinterpret_cast<const uint32_t __attribute__((ext_vector_type(4))) *>(p);
+            w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
+        } else if constexpr (SEG == 4) {
+            const auto x = *reinterpret_cast<const u32x2 *>(p);
+            w[0] = x.x, w[1] = x.y;
+        } else if constexpr (SEG == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(p);
+        } else {
+            w[0] = *p;
+        }
+    } else {
+        uint32_t v[SEG];
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+            const int64_t t = tok + j;
+            const uint32_t x = row[t < t1 ? t : t1 - 1];
+            v[j] = t < t1 ? x : 0u;
+        }
+#pragma unroll
+        for (int k = 0; k < (SEG + 1) / 2; ++k)
+            w[k] = v[2 * k] | ((2 * k + 1 < SEG) ? (v[2 * k + 1] << 16) : 0u);
+    }
+}
+
+// Store tokens tok .. tok+SEG-1 of a row (those before t1).
+template <int SEG, bool FAST>
+__device__ __forceinline__ void store_seg(uint16_t *row, int64_t tok, int64_t t1, const uint16_t (&v)[SEG])
+{
+    if constexpr (FAST) {
+        uint16_t *p = row + tok;
+        uint32_t w[(SEG + 1) / 2];
+#pragma unroll
+        for (int k = 0; k < (SEG + 1) / 2; ++k)
+            w[k] = v[2 * k] | ((2 * k + 1 < SEG) ? (static_cast<uint32_t>(v[2 * k + 1]) << 16) : 0u);
+        if constexpr (SEG == 8) {
+            uint32_t __attribute__((ext_vector_type(4))) x = {w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<uint32_t __attribute__((ext_vector_type(4))) *>(p) = x;
+        } else if constexpr (SEG == 4) {
+            u32x2 x = {w[0], w[1]};
+            *reinterpret_cast<u32x2 *>(p) = x;
+        } else if constexpr (SEG == 2) {
+            *reinterpret_cast<uint32_t *>(p) = w[0];
+        } else {
+            *p = v[0];
+        }
+    } else {
+#pragma unroll
+        for (int j = 0; j < SEG; ++j)
+            if (tok + j < t1)
+                row[tok + j] = v[j];
+    }
+}
+
+template <int SEG>
+__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(SEG + 1) / 2], int j)
+{
+    return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
+}
+
+// One step of the 64-lane scan for two states at once, as in-place DPP
+// operations: every lane combines its map (P, Q) with the map of the lane that
+// the DPP control names (the earlier tokens), Q += P * Q_src, then
+// P *= P_src. A lane without a source (shifted out of its row, or in a row
+// the row mask leaves out) is not written, which is the same as combining
+// with the identity map (1, 0). The leading s_nop gives the two wait states a
+// DPP read needs after a VALU write of its source register.
+#define SSU_SCAN_STEP2(DPPCTL)                                      \
+    asm("s_nop 1\n\t"                                               \
+        "v_fmac_f32_dpp %0, %0, %2 " DPPCTL "\n\t"                  \
+        "v_fmac_f32_dpp %1, %1, %3 " DPPCTL "\n\t"                  \
+        "v_mul_f32_dpp %2, %2, %2 " DPPCTL "\n\t"                   \
+        "v_mul_f32_dpp %3, %3, %3 " DPPCTL                           \
+        : "+v"(Q0), "+v"(Q1), "+v"(P0), "+v"(P1))
+
+// DPP control of the one-lane shift of the whole wave (GFX9 encoding).
+constexpr int kWaveShr1 = 0x138;
+
+constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2(e) - (float)log2(e)
+constexpr float kLn2 = 0.693147180559945309f;
+
+// softplus(v) = max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1], and
+// log1p(e) = 2 atanh(s), s = e / (2 + e) in (0, 1/3]: the odd series
+// 2 s (1 + s^2/3 + s^4/5 + ... + s^14/15) has terms shrinking by s^2 <= 1/9, so
+// eight of them reach fp32 precision. e is the hardware exp2 of
+// -|v| log2(e), with the rounding error of that product (exact by an fma)
+// and of the constant folded back in to first order.
+__device__ __forceinline__ float softplus_f32(float v)
+{
+    const float x = -fabsf(v);
+    const float t = x * kLog2e;
+    const float r = fmaf(x, kLog2e, -t) + x * kLog2eLo;
+    const float e0 = __builtin_amdgcn_exp2f(t);
+    const float e = fmaf(e0 * kLn2, r, e0);
+    const float sv = e * __builtin_amdgcn_rcpf(2.0f + e);
+    const float s2 = sv * sv;
+    float q = 1.0f / 15.0f;
+    q = fmaf(q, s2, 1.0f / 13.0f);
+    q = fmaf(q, s2, 1.0f / 11.0f);
+    q = fmaf(q, s2, 1.0f / 9.0f);
+    q = fmaf(q, s2, 1.0f / 7.0f);
+    q = fmaf(q, s2, 1.0f / 5.0f);
+    q = fmaf(q, s2, 1.0f / 3.0f);
+    q = fmaf(q, s2, 1.0f);
+    return fmaxf(v, 0.0f) + 2.0f * sv * q;
+}
+
+// One wave's share of one (request, channel): its 16 states' carried values
+// and decay rates (wave-uniform) and the rows it reads and writes.
+template <bool F16, int SEG, int NSW, bool FULL>
+struct Chan {
+    static constexpr int BLOCK = kLanes * SEG;
+    static constexpr int WORDS = (SEG + 1) / 2;
+
+    const uint16_t *u_row, *dl_row, *B_row, *C_row;
+    uint16_t *o_row;
+    int64_t B_n, C_n;
+    float bias, Dd;
+    int ns, lane;
+    bool softplus;
+    float h0[NSW], A2[NSW];
+
+    static constexpr int GROUPS = NSW / kGroup;
+
+    // One block of 64 * SEG tokens starting at blk: the scan of every state
+    // of this wave; yg returns the partial of y over each group of 8 states.
+    // FAST: the block lies inside the chunk and every row is aligned for
+    // vector access, so all loads are unconditional vector loads.
+    template <bool FAST>
+    __device__ __forceinline__ void block(int64_t blk, int64_t t1, float (&yg)[GROUPS][SEG], uint32_t (&uw)[WORDS])
+    {
+        const int64_t tok = blk + lane * SEG;
+
+        // every load of the block first, so that one wait covers them all
+        uint32_t dw[WORDS], Bw[NSW][WORDS], Cw[NSW][WORDS];
+        load_seg<SEG, FAST>(u_row, tok, t1, uw);
+        load_seg<SEG, FAST>(dl_row, tok, t1, dw);
+#pragma unroll
+        for (int n = 0; n < NSW; ++n) {
+            const int r = FULL ? n : min(n, ns - 1);  // rows past dstate: read a valid row, zeroed below
+            load_seg<SEG, FAST>(B_row + r * B_n, tok, t1, Bw[n]);
+            load_seg<SEG, FAST>(C_row + r * C_n, tok, t1, Cw[n]);
+        }
+        if constexpr (!FULL) {
+            // states past dstate: B = C = 0 (and A2 = 0), the identity map and a
+            // zero contribution
+#pragma unroll
+            for (int n = 0; n < NSW; ++n)
+#pragma unroll
+                for (int k = 0; k < WORDS; ++k) {
+                    Bw[n][k] = n < ns ? Bw[n][k] : 0u;
+                    Cw[n][k] = n < ns ? Cw[n][k] : 0u;
+                }
+        }
+
+        // step sizes Delta_j and inputs Delta_j u_j; invalid tokens: identity
+        float dl[SEG], du[SEG];
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+            const float v = io_to_f32<F16>(half_of<SEG>(dw, j)) + bias;
+            float sv = softplus ? softplus_f32(v) : v;
+            if (!FAST)
+                sv = tok + j < t1 ? sv : 0.0f;
+            dl[j] = sv;
+            du[j] = sv * io_to_f32<F16>(half_of<SEG>(uw, j));
+        }
+#pragma unroll
+        for (int gi = 0; gi < GROUPS; ++gi)
+#pragma unroll
+            for (int j = 0; j < SEG; ++j)
+                yg[gi][j] = 0.0f;
+
+#pragma unroll
+        for (int n = 0; n < NSW; n += 2) {
+            // two states at a time, so that each one's dependent steps
+            // interleave with the other's
+            float a0[SEG], b0[SEG], a1[SEG], b1[SEG];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) {
+                a0[j] = __builtin_amdgcn_exp2f(dl[j] * A2[n]);
+                a1[j] = __builtin_amdgcn_exp2f(dl[j] * A2[n + 1]);
+                b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n], j)), 0.0f);
+                b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n + 1], j)), 0.0f);
+            }
+            // 1. this lane's maps
+            float P0 = a0[0], Q0 = b0[0], P1 = a1[0], Q1 = b1[0];
+#pragma unroll
+            for (int j = 1; j < SEG; ++j) {
+                Q0 = fmaf(a0[j], Q0, b0[j]);
+                P0 = P0 * a0[j];
+                Q1 = fmaf(a1[j], Q1, b1[j]);
+                P1 = P1 * a1[j];
+            }
+            // 2. inclusive scan over the 64 lanes: shifts 1, 2, 4, 8 within
+            // rows of 16, then lane 15 of each row into the next (rows 1, 3)
+            // and lane 31 into rows 2, 3
+            SSU_SCAN_STEP2("row_shr:1 row_mask:0xf bank_mask:0xf");
+            SSU_SCAN_STEP2("row_shr:2 row_mask:0xf bank_mask:0xf");
+            SSU_SCAN_STEP2("row_shr:4 row_mask:0xf bank_mask:0xf");
+            SSU_SCAN_STEP2("row_shr:8 row_mask:0xf bank_mask:0xf");
+            SSU_SCAN_STEP2("row_bcast:15 row_mask:0xa bank_mask:0xf");
+            SSU_SCAN_STEP2("row_bcast:31 row_mask:0xc bank_mask:0xf");
+            const float e0 = fmaf(P0, h0[n], Q0), e1 = fmaf(P1, h0[n + 1], Q1);
+            // 3. start state of each lane (lane 0: the carried state), replay
+            float g0 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n]), __float_as_int(e0),
+                                                                  kWaveShr1, 0xf, 0xf, false));
+            float g1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n + 1]), __float_as_int(e1),
+                                                                  kWaveShr1, 0xf, 0xf, false));
+            // 4. carried states
+            h0[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
+            h0[n + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1), kLanes - 1));
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) {
+                g0 = fmaf(a0[j], g0, b0[j]);
+                g1 = fmaf(a1[j], g1, b1[j]);
+                float &y = yg[n / kGroup][j];
+                y = fmaf(g0, io_to_f32<F16>(half_of<SEG>(Cw[n], j)), y);
+                y = fmaf(g1, io_to_f32<F16>(half_of<SEG>(Cw[n + 1], j)), y);
+            }
+        }
+    }
+};
+
+template <bool F16, int SEG, int NSW, int MAXW, bool FULL>
+__global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_kernel(const ScanParams p)
+{
+    using Ch = Chan<F16, SEG, NSW, FULL>;
+    constexpr int BLOCK = Ch::BLOCK;
+    constexpr int GROUPS = Ch::GROUPS;
+    // group partials of waves 1 .. W-1
+    __shared__ float ypart[MAXW > 1 ? (MAXW - 1) * GROUPS : 1][MAXW > 1 ? BLOCK : 1];
+
+    const int lane = static_cast<int>(threadIdx.x) & (kLanes - 1);
+    const int wave = MAXW > 1 ? static_cast<int>(threadIdx.x) / kLanes : 0;
+    const int nwaves = MAXW > 1 ? static_cast<int>(blockDim.x) / kLanes : 1;
+    const int64_t bd = blockIdx.x;
+    const int64_t b = bd / p.dim;
+    const int d = static_cast<int>(bd - b * p.dim);
+    const int grp = d / p.ch_per_group;
+    const int n0 = wave * NSW;
+
+    Ch c;
+    c.lane = lane;
+    c.ns = FULL ? NSW : min(NSW, p.dstate - n0);
+    c.u_row = p.u + b * p.u_b + d * p.u_d;
+    c.dl_row = p.delta + b * p.dl_b + d * p.dl_d;
+    c.B_row = p.B + b * p.B_b + grp * p.B_g + n0 * p.B_n;
+    c.C_row = p.C + b * p.C_b + grp * p.C_g + n0 * p.C_n;
+    c.o_row = p.out + b * p.o_b + d * p.o_d;
+    c.B_n = p.B_n, c.C_n = p.C_n;
+    c.softplus = p.softplus != 0;
+    float *st = p.state + b * p.st_b + d * p.st_d + n0;
+
+    // wave-uniform per-channel values
+    c.bias = p.bias ? load_ro(p.bias + d) : 0.0f;
+    c.Dd = p.D ? load_ro(p.D + d) : 0.0f;
+#pragma unroll
+    for (int n = 0; n < NSW; ++n) {
+        const int r = FULL ? n : min(n, c.ns - 1);
+        const float hv = load_ro(st + r), av = load_ro(p.A + d * p.A_d + (n0 + r) * p.A_n);
+        c.h0[n] = (FULL || n < c.ns) ? hv : 0.0f;
+        c.A2[n] = (FULL || n < c.ns) ? av * kLog2e : 0.0f;
+    }
+    const bool vec = p.vec != 0;
+
+    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+        float yg[GROUPS][SEG];
+        uint32_t uw[Ch::WORDS];
+        const bool fast = vec && blk + BLOCK <= p.t1;
+        if (fast)
+            c.template block<true>(blk, p.t1, yg, uw);
+        else
+            c.template block<false>(blk, p.t1, yg, uw);
+
+        // y: the group partials added in group order
+        float y[SEG];
+#pragma unroll
+        for (int j = 0; j < SEG; ++j) {
+            y[j] = yg[0][j];
+#pragma unroll
+            for (int gi = 1; gi < GROUPS; ++gi)
+                y[j] += yg[gi][j];
+        }
+        if constexpr (MAXW > 1) {
+            if (wave > 0) {
+#pragma unroll
+                for (int gi = 0; gi < GROUPS; ++gi)
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j)
+                        ypart[(wave - 1) * GROUPS + gi][lane * SEG + j] = yg[gi][j];
+            }
+            __syncthreads();
+            if (wave == 0) {
+                for (int k = 0; k < (nwaves - 1) * GROUPS; ++k)
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j)
+                        y[j] += ypart[k][lane * SEG + j];
+            }
+            __syncthreads();
+        }
+        if (wave == 0) {
+            uint16_t o[SEG];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j)
+                o[j] = f32_to_io<F16>(fmaf(c.Dd, io_to_f32<F16>(half_of<SEG>(uw, j)), y[j]));
+            if (fast)
+                store_seg<SEG, true>(c.o_row, blk + lane * SEG, p.t1, o);
+            else
+                store_seg<SEG, false>(c.o_row, blk + lane * SEG, p.t1, o);
+        }
+    }
+
+    // final state: lane n of the wave writes state n0 + n
+    float mine = 0.0f;
+#pragma unroll
+    for (int n = 0; n < NSW; ++n)
+        mine = lane == n ? c.h0[n] : mine;
+    if (lane < c.ns)
+        st[lane] = mine;
+}
+
+using ScanFn = hipError_t (*)(const ScanParams &, int grid, int threads, hipStream_t);
+
+template <bool F16, int SEG, int NSW, int MAXW, bool FULL>
+hipError_t launch_scan(const ScanParams &p, int grid, int threads, hipStream_t stream)
+{
+    hipLaunchKernelGGL((ssu_scan_kernel<F16, SEG, NSW, MAXW, FULL>), dim3(grid), dim3(threads), 0, stream, p);
+    return hipGetLastError();
+}
+
+// A launch configuration: SEG tokens per lane, NSW states per wave. fn[single
+// wave][dstate % NSW == 0][f16]; the single-wave entry is null where the
+// multi-wave instantiation serves every wave count.
+struct ScanTile {
+    int seg, nsw;
+    ScanFn fn[2][2][2];
+    char name[24];
+};
+
+template <int SEG, int NSW, int MAXW, bool FULL>
+void set_scan_fns(ScanTile &t)
+{
+    t.fn[MAXW == 1][FULL][0] = &launch_scan<false, SEG, NSW, MAXW, FULL>;
+    t.fn[MAXW == 1][FULL][1] = &launch_scan<true, SEG, NSW, MAXW, FULL>;
+}
+
+template <int SEG, int NSW>
+ScanTile make_scan_tile()
+{
+    ScanTile t{};
+    t.seg = SEG;
+    t.nsw = NSW;
+    set_scan_fns<SEG, NSW, kMaxStates / NSW, false>(t);
+    set_scan_fns<SEG, NSW, kMaxStates / NSW, true>(t);
+    if constexpr (NSW == 16) {
+        set_scan_fns<SEG, NSW, 1, false>(t);
+        set_scan_fns<SEG, NSW, 1, true>(t);
+    }
+    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d", SEG, NSW);
+    return t;
+}
+
+const ScanTile *scan_tiles(int *count)
+{
+    static const ScanTile table[] = {make_scan_tile<8, 16>(), make_scan_tile<4, 16>(), make_scan_tile<2, 16>(),
+                                     make_scan_tile<1, 16>(), make_scan_tile<8, 8>(),  make_scan_tile<4, 8>(),
+                                     make_scan_tile<2, 8>(),  make_scan_tile<1, 8>()};
+    *count = static_cast<int>(sizeof table / sizeof table[0]);
+    return table;
+}
+
+// Default launch configuration, from a sweep of every configuration on
+// MI355X (batch 1, dim 1024, d_state 16, 4096 fp16 tokens): the largest token
+// segment that a launch still fills (64 lanes x SEG tokens per block; chunks
+// of 64, 128, 256 and 512 tokens are fastest at SEG 1, 2, 4 and 8), with 8
+// states per wave (two waves per channel hide latency: 59 us against 70 us
+// per sequence at chunk 512), and 16 states per wave once a launch covers
+// more than two blocks, where the second wave's repeated step sizes cost more
+// than it hides (36.5 us against 37.1 us at one launch of 4096 tokens).
+int default_scan_tile(int64_t span)
+{
+    int count = 0;
+    const ScanTile *t = scan_tiles(&count);
+    int seg = 1;
+    for (int s : {8, 4, 2})
+        if (span >= int64_t(kLanes) * s) {
+            seg = s;
+            break;
+        }
+    const int nsw = span > int64_t(2) * kLanes * 8 ? 16 : 8;
+    for (int i = 0; i < count; ++i)
+        if (t[i].seg == seg && t[i].nsw == nsw)
+            return i;
+    return 0;
+}
+
+bool is_io(const ssu_view &v) { return v.dtype == SSU_F16 || v.dtype == SSU_BF16; }
+
+}  // namespace
+}  // namespace ssu
+
+extern "C" {
+
+int32_t ssu_scan_tile_count(void)
+{
+    int count = 0;
+    ssu::scan_tiles(&count);
+    return count;
+}
+
+const char *ssu_scan_tile_name(int32_t tile)
+{
+    int count = 0;
+    const ssu::ScanTile *t = ssu::scan_tiles(&count);
+    return (tile >= 0 && tile < count) ? t[tile].name : "";
+}
+
+ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStream_t stream)
+{
+    using namespace ssu;
+    if (!a)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: null args");
+    int count = 0;
+    const ScanTile *tiles = scan_tiles(&count);
+    if (tile < -1 || tile >= count)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: tile %d out of range", tile);
+    if (chunk < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: negative chunk %lld", static_cast<long long>(chunk));
+    const int32_t bs = a->batch, dim = a->dim, N = a->dstate, G = a->ngroups;
+    const int64_t L = a->seqlen;
+    if (bs < 0 || dim <= 0 || N <= 0 || G <= 0 || L < 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: bad shape batch %d dim %d dstate %d ngroups %d seqlen %lld",
+                    bs, dim, N, G, static_cast<long long>(L));
+    if (dim % G)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: dim %d is not a multiple of ngroups %d", dim, G);
+    if (N > kMaxStates)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: dstate %d > %d", N, kMaxStates);
+    if (static_cast<int64_t>(bs) * dim > 0x7fffffff)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: batch * dim too large");
+    if (a->delta_softplus != 0 && a->delta_softplus != 1)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: delta_softplus must be 0 or 1");
+    if (bs == 0)
+        return SSU_OK;
+
+    // operands
+    if (!a->state.ptr || !a->A.ptr)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: null state or A");
+    if (a->state.dtype != SSU_F32 || a->A.dtype != SSU_F32)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: state and A must be F32");
+    if (a->state.stride[2] != 1)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: the state's dstate axis must be contiguous");
+    for (const ssu_view *v : {&a->D, &a->delta_bias})
+        if (v->ptr && v->dtype != SSU_F32)
+            return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: D and delta_bias must be F32");
+    for (const ssu_view *v : {&a->state, &a->A, &a->D, &a->delta_bias})
+        if (reinterpret_cast<uintptr_t>(v->ptr) % 4)
+            return fail(SSU_ERR_MISALIGNED, "ssu_scan: F32 operand not 4-byte aligned");
+    if (L > 0) {
+        const ssu_view *io[] = {&a->u, &a->delta, &a->B, &a->C, &a->out};
+        const char *names[] = {"u", "delta", "B", "C", "out"};
+        const int tax[] = {2, 2, 3, 3, 2};  // token axis
+        for (int k = 0; k < 5; ++k) {
+            if (!io[k]->ptr)
+                return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: null %s", names[k]);
+            if (!is_io(*io[k]) || io[k]->dtype != a->u.dtype)
+                return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: %s must be F16 or BF16, the same as u", names[k]);
+            if (io[k]->stride[tax[k]] != 1)
+                return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: %s's token axis must be contiguous", names[k]);
+            if (reinterpret_cast<uintptr_t>(io[k]->ptr) % 2)
+                return fail(SSU_ERR_MISALIGNED, "ssu_scan: %s not 2-byte aligned", names[k]);
+        }
+    }
+
+    const int t = tile >= 0 ? tile : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L);
+    const ScanTile &T = tiles[t];
+    const int waves = (N + T.nsw - 1) / T.nsw;
+    const bool single = waves == 1 && T.fn[1][0][0] != nullptr;
+
+    ScanParams p{};
+    p.u = static_cast<const uint16_t *>(a->u.ptr);
+    p.delta = static_cast<const uint16_t *>(a->delta.ptr);
+    p.B = static_cast<const uint16_t *>(a->B.ptr);
+    p.C = static_cast<const uint16_t *>(a->C.ptr);
+    p.out = static_cast<uint16_t *>(const_cast<void *>(a->out.ptr));
+    p.state = static_cast<float *>(const_cast<void *>(a->state.ptr));
+    p.A = static_cast<const float *>(a->A.ptr);
+    p.D = static_cast<const float *>(a->D.ptr);
+    p.bias = static_cast<const float *>(a->delta_bias.ptr);
+    p.u_b = a->u.stride[0], p.u_d = a->u.stride[1];
+    p.dl_b = a->delta.stride[0], p.dl_d = a->delta.stride[1];
+    p.B_b = a->B.stride[0], p.B_g = a->B.stride[1], p.B_n = a->B.stride[2];
+    p.C_b = a->C.stride[0], p.C_g = a->C.stride[1], p.C_n = a->C.stride[2];
+    p.o_b = a->out.stride[0], p.o_d = a->out.stride[1];
+    p.st_b = a->state.stride[0], p.st_d = a->state.stride[1];
+    p.A_d = a->A.stride[0], p.A_n = a->A.stride[1];
+    p.dim = dim, p.dstate = N, p.ch_per_group = dim / G, p.softplus = a->delta_softplus;
+
+    // Vector loads need every row start and every chunk start aligned to
+    // 2 * SEG bytes.
+    const int64_t ealign = T.seg;  // in 16-bit elements
+    bool vec = true;
+    if (L > 0) {
+        for (const ssu_view *v : {&a->u, &a->delta, &a->out})
+            vec = vec && reinterpret_cast<uintptr_t>(v->ptr) % (2 * ealign) == 0 && v->stride[0] % ealign == 0 &&
+                  v->stride[1] % ealign == 0;
+        for (const ssu_view *v : {&a->B, &a->C})
+            vec = vec && reinterpret_cast<uintptr_t>(v->ptr) % (2 * ealign) == 0 && v->stride[0] % ealign == 0 &&
+                  v->stride[1] % ealign == 0 && v->stride[2] % ealign == 0;
+    }
+    const int64_t step = (chunk > 0 && chunk < L) ? chunk : L;
+    const bool f16 = a->u.dtype == SSU_F16;
+    const int grid = bs * dim;
+    for (int64_t t0 = 0; t0 < L; t0 += step) {
+        p.t0 = t0;
+        p.t1 = std::min(L, t0 + step);
+        p.vec = vec && (t0 % ealign == 0);
+        const hipError_t e = T.fn[single][N % T.nsw == 0][f16](p, grid, waves * kLanes, stream);
+        if (e != hipSuccess)
+            return fail(SSU_ERR_HIP, "launch of %s failed: %s", T.name, hipGetErrorString(e));
+    }
+    return SSU_OK;
+}
+
+}  // extern "C"

@@ -374,3 +374,108 @@ def test_copy_blocks_validation(ssu):
     assert lib.ssu_copy_tile_count() > 0
     assert lib.ssu_copy_tile_name(0).decode().startswith("copy_")
     assert lib.ssu_copy_tile_name(-1) == b""
+
+
+# ------------------------------------------------------------------- ssu_scan --
+def _scan_args(ssu, batch=1, dim=32, N=16, G=1, L=100, io=None, softplus=1):
+    """ScanArgs over fake device addresses, contiguous layouts; tests change one
+    field to something invalid so the call returns before any HIP call."""
+    io = ssu.SSU_F16 if io is None else io
+    a = ssu.ScanArgs()
+    a.batch, a.dim, a.dstate, a.ngroups, a.seqlen = batch, dim, N, G, L
+    a.delta_softplus, a.reserved = softplus, 0
+
+    def view(off, tag, strides):
+        v = ssu.View()
+        v.ptr = FAKE + off
+        v.dtype = tag
+        for i, s_ in enumerate(strides):
+            v.stride[i] = s_
+        return v
+
+    a.state = view(0x0, ssu.SSU_F32, (dim * N, N, 1))
+    a.u = view(0x100000, io, (dim * L, L, 1))
+    a.delta = view(0x200000, io, (dim * L, L, 1))
+    a.B = view(0x300000, io, (G * N * L, N * L, L, 1))
+    a.C = view(0x400000, io, (G * N * L, N * L, L, 1))
+    a.A = view(0x500000, ssu.SSU_F32, (N, 1))
+    a.D = view(0x600000, ssu.SSU_F32, (1,))
+    a.delta_bias = view(0x700000, ssu.SSU_F32, (1,))
+    a.out = view(0x800000, io, (dim * L, L, 1))
+    return a
+
+
+def test_scan_struct_layout(ssu):
+    assert ctypes.sizeof(ssu.ScanArgs) == 32 + 9 * ctypes.sizeof(ssu.View)
+    assert ssu.ScanArgs.state.offset == 32
+
+
+def _scan_call(ssu, a, chunk=512, tile=-1):
+    return ssu._lib.ssu_scan(ctypes.byref(a), chunk, tile, None)
+
+
+@pytest.mark.parametrize("what,mutate,code", [
+    ("negative dim", lambda a, s: setattr(a, "dim", -1), 1),
+    ("zero dstate", lambda a, s: setattr(a, "dstate", 0), 1),
+    ("dstate > 64", lambda a, s: setattr(a, "dstate", 65), 2),
+    ("ngroups does not divide dim", lambda a, s: setattr(a, "ngroups", 3), 1),
+    ("negative seqlen", lambda a, s: setattr(a, "seqlen", -5), 1),
+    ("softplus flag", lambda a, s: setattr(a, "delta_softplus", 2), 1),
+    ("null state", lambda a, s: setattr(a.state, "ptr", None), 1),
+    ("null A", lambda a, s: setattr(a.A, "ptr", None), 1),
+    ("null u", lambda a, s: setattr(a.u, "ptr", None), 1),
+    ("null out", lambda a, s: setattr(a.out, "ptr", None), 1),
+    ("state not f32", lambda a, s: setattr(a.state, "dtype", s.SSU_BF16), 1),
+    ("A not f32", lambda a, s: setattr(a.A, "dtype", s.SSU_F16), 1),
+    ("D not f32", lambda a, s: setattr(a.D, "dtype", s.SSU_BF16), 1),
+    ("u not 16-bit", lambda a, s: setattr(a.u, "dtype", s.SSU_F32), 1),
+    ("B dtype differs from u", lambda a, s: setattr(a.B, "dtype", s.SSU_BF16), 1),
+    ("state's dstate axis strided", lambda a, s: a.state.stride.__setitem__(2, 2), 2),
+    ("u's token axis strided", lambda a, s: a.u.stride.__setitem__(2, 2), 2),
+    ("C's token axis strided", lambda a, s: a.C.stride.__setitem__(3, 0), 2),
+    ("out's token axis strided", lambda a, s: a.out.stride.__setitem__(2, 3), 2),
+    ("state misaligned", lambda a, s: setattr(a.state, "ptr", FAKE + 2), 3),
+    ("u misaligned", lambda a, s: setattr(a.u, "ptr", FAKE + 0x100001), 3),
+    ("batch * dim >= 2^31", lambda a, s: (setattr(a, "batch", 1 << 20), setattr(a, "dim", 1 << 12)), 2),
+])
+def test_scan_rejects_before_launch(ssu, what, mutate, code):
+    a = _scan_args(ssu)
+    mutate(a, ssu)
+    assert _scan_call(ssu, a) == code, what
+    assert ssu._lib.ssu_last_error().decode().startswith("ssu_scan"), what
+
+
+def test_scan_other_rejections(ssu):
+    a = _scan_args(ssu)
+    assert _scan_call(ssu, a, chunk=-1) == 1
+    assert _scan_call(ssu, a, tile=ssu._lib.ssu_scan_tile_count()) == 1
+    assert _scan_call(ssu, a, tile=-2) == 1
+    assert ssu._lib.ssu_scan_tile_count() == 8
+    assert ssu._lib.ssu_scan_tile_name(0).decode().startswith("scan_")
+    assert ssu._lib.ssu_scan_tile_name(99) == b""
+
+
+def test_scan_empty_is_a_noop(ssu):
+    """batch 0, or a sequence of length 0, returns OK without any HIP call."""
+    a = _scan_args(ssu, batch=0)
+    assert _scan_call(ssu, a) == 0
+    a = _scan_args(ssu, L=0)
+    a.u.ptr = a.delta.ptr = a.B.ptr = a.C.ptr = a.out.ptr = None  # never read when L == 0
+    assert _scan_call(ssu, a) == 0
+
+
+def test_scan_binding_validates(ssu):
+    import torch
+
+    u = torch.zeros((1, 4, 8), dtype=torch.float16)
+    B = torch.zeros((1, 1, 16, 8), dtype=torch.float16)
+    A = torch.zeros((4, 16))
+    st = torch.zeros((1, 4, 16))
+    with pytest.raises(ValueError, match="on a GPU"):
+        ssu.make_scan_args(u, u, A, B, B, st)
+    with pytest.raises(ValueError, match="delta shape"):
+        ssu.make_scan_args(u, u[:, :2], A, B, B, st)
+    with pytest.raises(TypeError, match="u's dtype"):
+        ssu.make_scan_args(u, u.bfloat16(), A, B, B, st)
+    with pytest.raises(TypeError):
+        ssu.make_scan_args(u.float(), u.float(), A, B.float(), B.float(), st)

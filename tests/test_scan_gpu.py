@@ -1,0 +1,305 @@
+"""The selective scan over a sequence (ssu_scan) against the CPU oracle.
+
+Every output and every final state element is compared with the oracle's
+fp64 scan under the scan rules of tests/tolerance.py, on the workloads of
+ssu_inputs.SCAN_CONFIGS at full size (the oracle scans them in seconds), on
+ragged lengths, other state counts and groups, every launch configuration,
+unaligned (scalar-path) views and HIP graph replays. Chunkings whose chunks are
+multiples of 512 tokens must agree bitwise with one launch over the whole
+sequence (the state is carried in fp32 either way).
+"""
+import functools
+
+import numpy as np
+import pytest
+
+import ssu_inputs as si
+
+from . import gpu_util as gu
+from . import tolerance as tol
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(autouse=True)
+def _gpu():
+    gu.require_gpu()
+
+
+def _io_tensor(bits, io, device="cuda"):
+    torch = gu.torch_mod()
+    dt = torch.float16 if io == "f16" else torch.bfloat16
+    return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(dt).to(device)
+
+
+class DeviceScan:
+    """Device copies of a ScanProblem's operands (contiguous)."""
+
+    def __init__(self, p: si.ScanProblem):
+        torch = gu.torch_mod()
+        self.p = p
+        self.u = _io_tensor(p.u, p.io)
+        self.delta = _io_tensor(p.delta, p.io)
+        self.B = _io_tensor(p.B, p.io)
+        self.C = _io_tensor(p.C, p.io)
+        self.A = torch.from_numpy(p.A).cuda()
+        self.D = torch.from_numpy(p.D).cuda()
+        self.bias = torch.from_numpy(p.delta_bias).cuda()
+        self.state0 = torch.from_numpy(p.state).cuda()
+
+    def run(self, chunk=0, tile=-1, D=True, bias=True, views=None):
+        import selective_state_update_amd as ssu
+
+        torch = gu.torch_mod()
+        v = dict(u=self.u, delta=self.delta, B=self.B, C=self.C)
+        if views:
+            v.update(views)
+        state = self.state0.clone()
+        out = ssu.selective_scan(v["u"], v["delta"], self.A, v["B"], v["C"], state,
+                                 D=self.D if D else None, delta_bias=self.bias if bias else None,
+                                 delta_softplus=self.p.delta_softplus, chunk=chunk, tile=tile)
+        torch.cuda.synchronize()
+        return out.view(torch.int16).cpu().numpy().view(np.uint16), state.cpu().numpy()
+
+
+def oracle_scan(ref, p, D=True, bias=True):
+    st = p.state.copy()
+    return ref.scan(st, p.u, p.delta, p.A, p.B, p.C, p.D if D else None, p.delta_bias if bias else None,
+                    delta_softplus=p.delta_softplus, io=p.io)
+
+
+def check(p, out, state, r, what=""):
+    bad_o = tol.scan_out_violations(out, r["y"], r["tau"], r["rho"], p.dstate, p.io)
+    bad_s = tol.scan_state_violations(state, r["state"], r["err"])
+    if bad_o.any():
+        i = np.argwhere(bad_o)[0]
+        raise AssertionError(f"{what}: {bad_o.sum()} outputs out of tolerance, first {tuple(i)}: "
+                             f"gpu {tol.io_to_f64(out[tuple(i)], p.io)} ref {r['y'][tuple(i)]}")
+    if bad_s.any():
+        i = np.argwhere(bad_s)[0]
+        raise AssertionError(f"{what}: {bad_s.sum()} states out of tolerance, first {tuple(i)}: "
+                             f"gpu {state[tuple(i)]} ref {r['state'][tuple(i)]} err {r['err'][tuple(i)]}")
+
+
+def _cfg(k):
+    c = dict(si.SCAN_CONFIGS[k])
+    name, chunk = c.pop("name"), c.pop("chunk")
+    return name, chunk, c
+
+
+@functools.lru_cache(maxsize=None)
+def _config_case(k, zero_state):
+    name, chunk, c = _cfg(k)
+    p = si.make_scan_problem(**c, zero_state=zero_state)
+    return name, chunk, p
+
+
+@functools.lru_cache(maxsize=None)
+def _config_ref(k, zero_state):
+    import oracle
+
+    _, _, p = _config_case(k, zero_state)
+    return oracle_scan(oracle.get(), p)
+
+
+@pytest.mark.parametrize("k", sorted(si.SCAN_CONFIGS))
+@pytest.mark.parametrize("zero_state", [True, False], ids=["fresh", "carried"])
+def test_scan_configs(k, zero_state):
+    name, chunk, p = _config_case(k, zero_state)
+    print(f"scan parity: {name} zero_state={zero_state}", flush=True)
+    out, state = DeviceScan(p).run(chunk=chunk)
+    check(p, out, state, _config_ref(k, zero_state), name)
+
+
+def test_scan_chunk_invariance():
+    """Chunks that are multiples of 512 tokens give bitwise the results of one
+    launch, in the default configuration and in every configuration with 8
+    tokens per lane; other chunk sizes (including ragged ones) stay within
+    tolerance."""
+    import selective_state_update_amd as ssu
+
+    name, _, p = _config_case(1, False)
+    ds = DeviceScan(p)
+    o0, s0 = ds.run(chunk=0)
+    for chunk in (512, 1024, 1536, 4096):
+        o, s = ds.run(chunk=chunk)
+        assert np.array_equal(o, o0) and np.array_equal(s, s0), chunk
+    for tile, tname in enumerate(ssu.scan_tiles()):
+        if tname.startswith("scan_t8_"):
+            for chunk in (512, 0):
+                o, s = ds.run(chunk=chunk, tile=tile)
+                assert np.array_equal(o, o0) and np.array_equal(s, s0), (tname, chunk)
+    r = _config_ref(1, False)
+    for chunk in (32, 64, 100, 256, 1000):
+        o, s = ds.run(chunk=chunk)
+        check(p, o, s, r, f"{name} chunk {chunk}")
+
+
+def test_scan_every_tile():
+    """Every launch configuration, on a small case with several blocks and a
+    ragged tail, and with chunk sizes that do not fill a block."""
+    import oracle
+    import selective_state_update_amd as ssu
+
+    p = si.make_scan_problem(2, 48, 16, 1337, 2, io="f16", seed=40, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    ds = DeviceScan(p)
+    for tile, name in enumerate(ssu.scan_tiles()):
+        for chunk in (0, 200):
+            o, s = ds.run(chunk=chunk, tile=tile)
+            check(p, o, s, r, f"{name} chunk {chunk}")
+
+
+@pytest.mark.parametrize("L", [1, 7, 63, 64, 65, 511, 513, 1000])
+@pytest.mark.parametrize("io", ["f16", "bf16"])
+def test_scan_ragged_lengths(L, io):
+    import oracle
+
+    p = si.make_scan_problem(3, 40, 16, L, 1, io=io, seed=41 + L, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    ds = DeviceScan(p)
+    for chunk in (0, 64, 512):
+        o, s = ds.run(chunk=chunk)
+        check(p, o, s, r, f"L={L} {io} chunk {chunk}")
+
+
+@pytest.mark.parametrize("N,G", [(1, 1), (4, 2), (16, 4), (17, 1), (32, 2), (48, 1), (64, 8)])
+def test_scan_states_and_groups(N, G):
+    """Other state counts (one wave up to 16 states, then one wave per 16) and
+    B/C groups."""
+    import oracle
+
+    p = si.make_scan_problem(2, 64, N, 700, G, io="bf16", seed=50 + N + G, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    o, s = DeviceScan(p).run(chunk=512)
+    check(p, o, s, r, f"N={N} G={G}")
+
+
+def test_scan_options():
+    """Softplus off (positive steps), no D, no delta_bias."""
+    import oracle
+
+    p = si.make_scan_problem(2, 32, 16, 900, 1, io="f16", seed=60, zero_state=False, delta_softplus=False)
+    # without the softplus the steps are delta + bias as given: keep them positive
+    p.delta = si.io_bits(np.abs(si.io_values(p.delta, "f16")) * 0.05, "f16")
+    p.delta_bias = np.full(p.dim, 0.01, dtype=np.float32)
+    ref = oracle.get()
+    for D, bias in ((True, True), (False, True), (True, False), (False, False)):
+        r = oracle_scan(ref, p, D=D, bias=bias)
+        o, s = DeviceScan(p).run(chunk=256, D=D, bias=bias)
+        check(p, o, s, r, f"softplus off D={D} bias={bias}")
+
+
+def test_scan_special_values():
+    """A = 0 (no decay, the state is a running sum), A very negative (no
+    memory), zero steps (softplus off, delta = bias = 0: state unchanged, out =
+    C.h0 + D u) against the oracle."""
+    import oracle
+
+    ref = oracle.get()
+    base = si.make_scan_problem(1, 32, 16, 600, 1, io="f16", seed=61, zero_state=False)
+    cases = []
+    p = si.make_scan_problem(1, 32, 16, 600, 1, io="f16", seed=61, zero_state=False)
+    p.A = np.zeros_like(p.A)
+    cases.append(("A=0", p, True))
+    p = si.make_scan_problem(1, 32, 16, 600, 1, io="f16", seed=61, zero_state=False)
+    p.A = np.full_like(p.A, -1e30)
+    cases.append(("A=-1e30", p, True))
+    p = si.make_scan_problem(1, 32, 16, 600, 1, io="f16", seed=61, zero_state=False, delta_softplus=False)
+    p.delta = np.zeros_like(p.delta)
+    cases.append(("zero steps", p, False))
+    for what, p, bias in cases:
+        r = oracle_scan(ref, p, bias=bias)
+        o, s = DeviceScan(p).run(chunk=512, bias=bias)
+        check(p, o, s, r, what)
+        if what == "zero steps":
+            assert np.array_equal(s, base.state)
+
+
+def test_scan_unaligned_views():
+    """Views that are not aligned for vector access (odd element offsets, row
+    strides that are not multiples of 8) take the element-wise path, which
+    must give bitwise the same results as the vector path."""
+    torch = gu.torch_mod()
+    p = si.make_scan_problem(2, 24, 16, 777, 2, io="bf16", seed=62, zero_state=False)
+    ds = DeviceScan(p)
+    o0, s0 = ds.run(chunk=512)
+
+    def shifted(t):
+        # same values, stored one element further into a wider buffer
+        big = torch.zeros(t.shape[:-1] + (t.shape[-1] + 3,), dtype=t.dtype, device=t.device)
+        big[..., 1:1 + t.shape[-1]] = t
+        return big[..., 1:1 + t.shape[-1]]
+
+    views = dict(u=shifted(ds.u), delta=shifted(ds.delta), B=shifted(ds.B), C=shifted(ds.C))
+    o, s = ds.run(chunk=512, views=views)
+    assert np.array_equal(o, o0) and np.array_equal(s, s0)
+    o, s = ds.run(chunk=100, views=views)   # chunk starts not multiples of 8 either
+    import oracle
+
+    check(p, o, s, oracle_scan(oracle.get(), p), "unaligned chunk 100")
+
+
+def test_scan_batch_and_strided_state():
+    """Several requests with a state that is a strided view into a larger
+    buffer (rows of a state pool), and the output of one request unaffected by
+    another's inputs."""
+    import oracle
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    p = si.make_scan_problem(4, 32, 16, 530, 1, io="f16", seed=63, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    ds = DeviceScan(p)
+    pool = torch.full((9, 32, 16), 7.0, dtype=torch.float32, device="cuda")
+    st = pool[1::2]  # rows 1, 3, 5, 7 of the pool: a non-contiguous view
+    st.copy_(ds.state0)
+    out = ssu.selective_scan(ds.u, ds.delta, ds.A, ds.B, ds.C, st, D=ds.D, delta_bias=ds.bias, chunk=512)
+    torch.cuda.synchronize()
+    o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+    check(p, o, st.cpu().numpy(), r, "strided state")
+    assert np.all(pool[0::2].cpu().numpy() == 7.0)
+
+
+def test_scan_empty():
+    """batch 0 and length 0 are no-ops."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    p = si.make_scan_problem(2, 16, 16, 0, 1, io="f16", seed=64, zero_state=False)
+    ds = DeviceScan(p)
+    o, s = ds.run(chunk=512)
+    assert o.size == 0 and np.array_equal(s, p.state)
+    act = torch.zeros((0, 16, 5), dtype=torch.float16, device="cuda")
+    bc = torch.zeros((0, 1, 16, 5), dtype=torch.float16, device="cuda")
+    state = torch.zeros((0, 16, 16), dtype=torch.float32, device="cuda")
+    out = ssu.selective_scan(act, act, ds.A, bc, bc, state, chunk=512)
+    assert out.shape == (0, 16, 5)
+
+
+def test_scan_graph_replays():
+    """The chunked scan captured in a HIP graph: every replay (state reset
+    between replays by an eager copy) matches the eager result bitwise."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    name, chunk, p = _config_case(0, False)
+    ds = DeviceScan(p)
+    o_ref, s_ref = ds.run(chunk=chunk)
+    state = ds.state0.clone()
+    args, out = ssu.make_scan_args(ds.u, ds.delta, ds.A, ds.B, ds.C, state, ds.D, ds.bias)
+    s = torch.cuda.Stream()
+    with torch.cuda.stream(s):
+        ssu.scan_launch(args, chunk, stream=s)  # warm up outside the capture
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=s):
+        ssu.scan_launch(args, chunk, stream=s)
+    for rep in range(3):
+        state.copy_(ds.state0)
+        out.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        o = out.view(torch.int16).cpu().numpy().view(np.uint16)
+        assert np.array_equal(o, o_ref) and np.array_equal(state.cpu().numpy(), s_ref), rep
