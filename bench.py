@@ -192,6 +192,15 @@ def cpu_oracle_baseline(H, P, N, G, batch, seed, budget_s=20.0):
         times.append(time.perf_counter() - t0)
     med = statistics.median(times)
     gbs = algorithmic_bytes(H, P, N, G, batch) / med / 1e9
+    # the same calls on one core
+    one = []
+    for _ in range(2):
+        pool = p.pool.copy()
+        t0 = time.perf_counter()
+        ref.run(pool, p.idx, p.x, p.B, p.C, p.dt, p.A, p.dt_bias, p.D, True, want_state=False,
+                want_y=False, nthreads=1)
+        one.append(time.perf_counter() - t0)
+    one_med = statistics.median(one)
     cpu_model = ""
     try:
         for line in open("/proc/cpuinfo"):
@@ -203,7 +212,9 @@ def cpu_oracle_baseline(H, P, N, G, batch, seed, budget_s=20.0):
     return {"value": round(gbs, 3), "unit": "GB/s", "cores": threads, "kind": "oracle",
             "sample": f"{len(times)} whole calls of H{H} P{P} N{N} batch {batch} (median "
                       f"{med * 1e3:.1f} ms/call, fp64 C oracle, OpenMP {threads} threads, {cpu_model})",
-            "us_per_call": round(med * 1e6, 1)}
+            "us_per_call": round(med * 1e6, 1),
+            "one_core": {"value": round(algorithmic_bytes(H, P, N, G, batch) / one_med / 1e9, 3), "unit": "GB/s",
+                         "us_per_call": round(one_med * 1e6, 1), "sample": "2 whole calls, 1 thread"}}
 
 
 def counter_traffic():
@@ -565,15 +576,17 @@ def scan_elements(batch, dim, N, L):
 def run_scan(a):
     """ssu_scan on the page's shapes (configs from --scan), for every chunk in
     --chunks. Input sets (u, delta, B, C, out, state) rotate so that the sets
-    together hold >= 768 MiB (cold HBM, as in prefill where each layer's
-    activations are produced just before); K sequences captured in one HIP
-    graph, median of 5 x 10 replays. One line per (config, chunk)."""
+    together hold >= 768 MiB (cold HBM); K sequences captured in one HIP graph,
+    median of 5 x 10 replays. warm_us_per_seq repeats one set instead, so its
+    inputs stay in the Infinity Cache, as when the kernels before the scan have
+    just written them (and as a harness that reuses one tensor measures). One
+    line per (config, chunk, configuration)."""
     import torch
 
     import selective_state_update_amd as ssu
 
     out = open(a.out, "w") if a.out else sys.stdout
-    print("config chunk launches us_per_seq ms_per_seq Mtokens_per_s GBps hbm_pct Gelem_per_s tile",
+    print("config chunk launches us_per_seq ms_per_seq Mtokens_per_s GBps hbm_pct Gelem_per_s warm_us_per_seq tile",
           file=out, flush=True)
     chunks = [int(c) for c in a.chunks.split(",")]
     for k in [int(c) for c in a.scan.split(",")]:
@@ -618,12 +631,22 @@ def run_scan(a):
                 g.replay()
                 torch.cuda.synchronize()
                 us = statistics.median([time_graph_on(g, 10, side) / (10 * calls) for _ in range(5)]) * 1e6
+                del g
+                # warm: the same set every call (its 25 MB stay in the Infinity Cache), as when the
+                # activations were just written by the kernels before the scan
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=side):
+                    for i in range(calls):
+                        ssu.scan_launch(args[0], chunk, tile, stream=side)
+                g.replay()
+                torch.cuda.synchronize()
+                warm = statistics.median([time_graph_on(g, 10, side) / (10 * calls) for _ in range(5)]) * 1e6
+                del g
                 gbs = nbytes / (us * 1e-6) / 1e9
                 tname = ssu.scan_tiles()[tile] if tile >= 0 else "default"
                 print(f"{k} {chunk} {launches} {us:.2f} {us / 1e3:.4f} {bs * L / us:.2f} {gbs:.1f} "
-                      f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {tname}",
-                      file=out, flush=True)
-                del g
+                      f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {warm:.2f} "
+                      f"{tname}", file=out, flush=True)
         del sets, args
         torch.cuda.empty_cache()
 
@@ -653,8 +676,9 @@ def _copy_reference():
 
 def run_scan_counters(a):
     """Eager scans for a rocprofv3 --pmc pass: `a.steps` sequences of scan
-    config `a.scan` at its static chunk, over 4 input sets of which each is
-    evicted from the cache before reuse, then the reference copy."""
+    config `a.scan` at the first of --chunks (default: its static chunk), over
+    4 input sets of which each is evicted from the cache before reuse, then the
+    reference copy."""
     import torch
 
     import selective_state_update_amd as ssu
@@ -663,6 +687,8 @@ def run_scan_counters(a):
     cfg = dict(si.SCAN_CONFIGS[k])
     cfg.pop("name")
     chunk = cfg.pop("chunk")
+    if a.chunks:
+        chunk = int(a.chunks.split(",")[0])
     dt = torch.float16 if cfg["io"] == "f16" else torch.bfloat16
     sets = []
     for i in range(4):

@@ -23,8 +23,9 @@
 //      from the block's start to its last token; applied to the carried state
 //      it is the state after that token;
 //   3. shifted one lane up (lane 0 takes the carried state) it is each lane's
-//      start state; each lane replays its tokens from there and accumulates
-//      y_j += h_j C_j;
+//      start state g; the lane's state after its token j is its prefix map
+//      applied to g, h_j = P_j g + Q_j (P_j, Q_j kept from step 1), computed
+//      for every j independently, and y_j += h_j C_j;
 //   4. lane 63's end state is the carried state for the next block.
 // The carried state is wave-uniform (one register per state), so blocks, and
 // launches that start on a block boundary, continue from exactly the value the
@@ -171,7 +172,7 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(SEG + 1) / 2], 
 // the row mask leaves out) is not written, which is the same as combining
 // with the identity map (1, 0). The leading s_nop gives the two wait states a
 // DPP read needs after a VALU write of its source register.
-#define SSU_SCAN_STEP2(DPPCTL)                                      \
+#define SSU_SCAN_STEP2(DPPCTL, Q0, Q1, P0, P1)                      \
     asm("s_nop 1\n\t"                                               \
         "v_fmac_f32_dpp %0, %0, %2 " DPPCTL "\n\t"                  \
         "v_fmac_f32_dpp %1, %1, %3 " DPPCTL "\n\t"                  \
@@ -288,40 +289,43 @@ struct Chan {
                 b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n], j)), 0.0f);
                 b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n + 1], j)), 0.0f);
             }
-            // 1. this lane's maps
-            float P0 = a0[0], Q0 = b0[0], P1 = a1[0], Q1 = b1[0];
+            // 1. this lane's maps from its first token to each of its tokens
+            // (the prefix products P_j of the decays and the states Q_j reached
+            // from 0), the last of which is the lane's whole map
+            float P0[SEG], Q0[SEG], P1[SEG], Q1[SEG];
+            P0[0] = a0[0], Q0[0] = b0[0], P1[0] = a1[0], Q1[0] = b1[0];
 #pragma unroll
             for (int j = 1; j < SEG; ++j) {
-                Q0 = fmaf(a0[j], Q0, b0[j]);
-                P0 = P0 * a0[j];
-                Q1 = fmaf(a1[j], Q1, b1[j]);
-                P1 = P1 * a1[j];
+                Q0[j] = fmaf(a0[j], Q0[j - 1], b0[j]);
+                P0[j] = P0[j - 1] * a0[j];
+                Q1[j] = fmaf(a1[j], Q1[j - 1], b1[j]);
+                P1[j] = P1[j - 1] * a1[j];
             }
-            // 2. inclusive scan over the 64 lanes: shifts 1, 2, 4, 8 within
-            // rows of 16, then lane 15 of each row into the next (rows 1, 3)
-            // and lane 31 into rows 2, 3
-            SSU_SCAN_STEP2("row_shr:1 row_mask:0xf bank_mask:0xf");
-            SSU_SCAN_STEP2("row_shr:2 row_mask:0xf bank_mask:0xf");
-            SSU_SCAN_STEP2("row_shr:4 row_mask:0xf bank_mask:0xf");
-            SSU_SCAN_STEP2("row_shr:8 row_mask:0xf bank_mask:0xf");
-            SSU_SCAN_STEP2("row_bcast:15 row_mask:0xa bank_mask:0xf");
-            SSU_SCAN_STEP2("row_bcast:31 row_mask:0xc bank_mask:0xf");
-            const float e0 = fmaf(P0, h0[n], Q0), e1 = fmaf(P1, h0[n + 1], Q1);
-            // 3. start state of each lane (lane 0: the carried state), replay
-            float g0 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n]), __float_as_int(e0),
-                                                                  kWaveShr1, 0xf, 0xf, false));
-            float g1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n + 1]), __float_as_int(e1),
-                                                                  kWaveShr1, 0xf, 0xf, false));
+            // 2. inclusive scan of the lanes' whole maps over the 64 lanes:
+            // shifts 1, 2, 4, 8 within rows of 16, then lane 15 of each row into
+            // the next (rows 1, 3) and lane 31 into rows 2, 3
+            float SP0 = P0[SEG - 1], SQ0 = Q0[SEG - 1], SP1 = P1[SEG - 1], SQ1 = Q1[SEG - 1];
+            SSU_SCAN_STEP2("row_shr:1 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            SSU_SCAN_STEP2("row_shr:2 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            SSU_SCAN_STEP2("row_shr:4 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            SSU_SCAN_STEP2("row_shr:8 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            SSU_SCAN_STEP2("row_bcast:15 row_mask:0xa bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            SSU_SCAN_STEP2("row_bcast:31 row_mask:0xc bank_mask:0xf", SQ0, SQ1, SP0, SP1);
+            const float e0 = fmaf(SP0, h0[n], SQ0), e1 = fmaf(SP1, h0[n + 1], SQ1);
+            // 3. start state of each lane (lane 0: the carried state); each of
+            // the lane's states is its prefix map applied to it, independently
+            const float g0 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n]), __float_as_int(e0),
+                                                                        kWaveShr1, 0xf, 0xf, false));
+            const float g1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n + 1]), __float_as_int(e1),
+                                                                        kWaveShr1, 0xf, 0xf, false));
             // 4. carried states
             h0[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
             h0[n + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1), kLanes - 1));
 #pragma unroll
             for (int j = 0; j < SEG; ++j) {
-                g0 = fmaf(a0[j], g0, b0[j]);
-                g1 = fmaf(a1[j], g1, b1[j]);
                 float &y = yg[n / kGroup][j];
-                y = fmaf(g0, io_to_f32<F16>(half_of<SEG>(Cw[n], j)), y);
-                y = fmaf(g1, io_to_f32<F16>(half_of<SEG>(Cw[n + 1], j)), y);
+                y = fmaf(fmaf(P0[j], g0, Q0[j]), io_to_f32<F16>(half_of<SEG>(Cw[n], j)), y);
+                y = fmaf(fmaf(P1[j], g1, Q1[j]), io_to_f32<F16>(half_of<SEG>(Cw[n + 1], j)), y);
             }
         }
     }
@@ -476,26 +480,25 @@ const ScanTile *scan_tiles(int *count)
 }
 
 // Default launch configuration, from a sweep of every configuration on
-// MI355X (batch 1, dim 1024, d_state 16, 4096 fp16 tokens): the largest token
-// segment that a launch still fills (64 lanes x SEG tokens per block; chunks
-// of 64, 128, 256 and 512 tokens are fastest at SEG 1, 2, 4 and 8), with 8
-// states per wave (two waves per channel hide latency: 59 us against 70 us
-// per sequence at chunk 512), and 16 states per wave once a launch covers
-// more than two blocks, where the second wave's repeated step sizes cost more
-// than it hides (36.5 us against 37.1 us at one launch of 4096 tokens).
+// MI355X (batch 1, dim 1024, d_state 16, 4096 fp16 tokens, cold and warm
+// caches): the largest token segment that a launch still fills (64 lanes x SEG
+// tokens per block; chunks of 64, 128, 256 and 512 tokens are fastest at
+// SEG 1, 2, 4 and 8), with 8 states per wave: two waves per channel hide
+// latency that one wave cannot (59.4 us against 69.9 us per sequence at chunk
+// 512), and are within 1% of 16 states per wave when a launch covers the
+// whole sequence.
 int default_scan_tile(int64_t span)
 {
     int count = 0;
     const ScanTile *t = scan_tiles(&count);
     int seg = 1;
-    for (int s : {8, 4, 2})
-        if (span >= int64_t(kLanes) * s) {
-            seg = s;
+    for (int sg : {8, 4, 2})
+        if (span >= int64_t(kLanes) * sg) {
+            seg = sg;
             break;
         }
-    const int nsw = span > int64_t(2) * kLanes * 8 ? 16 : 8;
     for (int i = 0; i < count; ++i)
-        if (t[i].seg == seg && t[i].nsw == nsw)
+        if (t[i].seg == seg && t[i].nsw == 8)
             return i;
     return 0;
 }
