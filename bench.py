@@ -647,6 +647,17 @@ def run_scan(a):
                 print(f"{k} {chunk} {launches} {us:.2f} {us / 1e3:.4f} {bs * L / us:.2f} {gbs:.1f} "
                       f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {warm:.2f} "
                       f"{tname}", file=out, flush=True)
+        if k == 1 and not a.no_cpu_baseline:
+            # the CPU oracle on one sequence of this workload, for context
+            import oracle
+
+            p = si.make_scan_problem(**cfg)
+            threads = len(os.sched_getaffinity(0))
+            t0 = time.perf_counter()
+            oracle.get().scan(p.state.copy(), p.u, p.delta, p.A, p.B, p.C, p.D, p.delta_bias, io=p.io,
+                              want_ref=False, nthreads=threads)
+            print(f"# cpu oracle (fp64, {threads} threads): {(time.perf_counter() - t0) * 1e3:.1f} ms per sequence of "
+                  f"{name}", file=out, flush=True)
         del sets, args
         torch.cuda.empty_cache()
 

@@ -303,3 +303,18 @@ def test_scan_graph_replays():
         torch.cuda.synchronize()
         o = out.view(torch.int16).cpu().numpy().view(np.uint16)
         assert np.array_equal(o, o_ref) and np.array_equal(state.cpu().numpy(), s_ref), rep
+
+
+def test_scan_long_sequence():
+    """A sequence of about a million tokens (ragged, several launches of
+    2^18 tokens and one launch): 64-bit token offsets and many blocks, every
+    output and the final state against the oracle."""
+    import oracle
+
+    L = 1_000_003
+    p = si.make_scan_problem(1, 4, 16, L, 1, io="bf16", seed=65, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    ds = DeviceScan(p)
+    for chunk in (1 << 18, 0):
+        o, s = ds.run(chunk=chunk)
+        check(p, o, s, r, f"L={L} chunk {chunk}")
