@@ -892,8 +892,8 @@ def main():
     ap.add_argument("--summarize-scan-counters", default="")
     ap.add_argument("--summarize-counters", default="")
     ap.add_argument("--write-profile", action="store_true")
-    ap.add_argument("--fetch-dir-name", default="gpurun_out/pmc_fetch")
-    ap.add_argument("--write-dir-name", default="gpurun_out/pmc_write")
+    ap.add_argument("--fetch-dir-name", default="pmc/fetch", help="FETCH_SIZE output directory (for the summary text)")
+    ap.add_argument("--write-dir-name", default="pmc/write", help="WRITE_SIZE output directory (for the summary text)")
     a = ap.parse_args()
     if a.gpus != 1:
         print("bench.py measures one GPU: selective_state_update has no cross-GPU exchange, and this "

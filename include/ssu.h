@@ -54,7 +54,7 @@ extern "C" {
 typedef enum ssu_status {
     SSU_OK = 0,
     SSU_ERR_INVALID_ARGUMENT = 1, /* null pointer, negative size, wrong dtype tag, bad config */
-    SSU_ERR_UNSUPPORTED = 2,      /* shape or layout this build does not run (see ssu_update) */
+    SSU_ERR_UNSUPPORTED = 2,      /* shape or layout the library does not run (see ssu_update) */
     SSU_ERR_MISALIGNED = 3,       /* state or B/C address not aligned for vector access */
     SSU_ERR_HIP = 4,              /* a HIP runtime call failed (launch, device query, copy) */
     SSU_ERR_NO_MEMORY = 5,        /* host allocation failed */
@@ -159,8 +159,8 @@ typedef struct ssu_tile_desc {
 
 /* Validate `cfg` and create a handle. Does not touch the GPU.
  * Errors: SSU_ERR_INVALID_ARGUMENT (null, H/P/N/G out of range, G not dividing
- * H, tile index out of range), SSU_ERR_UNSUPPORTED (P or N this build does not
- * compile for), SSU_ERR_NO_MEMORY. */
+ * H, tile index out of range), SSU_ERR_UNSUPPORTED (P or N the library has no
+ * kernel for), SSU_ERR_NO_MEMORY. */
 ssu_status ssu_create(const ssu_config *cfg, ssu_handle **out);
 
 /* Enqueue one decode step on `stream` (NULL: the null stream).
