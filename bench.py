@@ -497,6 +497,22 @@ def run_tokens(a):
               file=out, flush=True)
         del g, rot, args
         torch.cuda.empty_cache()
+        if not a.no_cpu_baseline:
+            # the CPU oracle on one K-token call of this workload, for context
+            import oracle
+
+            base = si.make_problem(H, P, N, G, bs, bs, a.config)
+            rng = np.random.Generator(np.random.PCG64([a.config, K]))
+            xs = si.bf16_bits(rng.standard_normal((K, bs, H, P), dtype=np.float32))
+            bcs = si.bf16_bits(rng.standard_normal((K, bs, G, N), dtype=np.float32))
+            dts = si.bf16_bits(rng.standard_normal((K, bs, H), dtype=np.float32))
+            threads = len(os.sched_getaffinity(0))
+            pool = base.pool.copy()
+            t0 = time.perf_counter()
+            oracle.get().run(pool, base.idx, xs, bcs, bcs, dts, base.A, base.dt_bias, base.D, True,
+                             want_state=False, want_y=False, nthreads=threads)
+            print(f"# cpu oracle (fp64, {threads} threads): {(time.perf_counter() - t0) * 1e3:.1f} ms for one "
+                  f"{K}-token call", file=out, flush=True)
 
 
 # Per-request state blocks of the copy workload (vLLM state-block copy page,
@@ -556,6 +572,22 @@ def run_copy_blocks(a):
         print(f"{nreqs} {K} {calls} {us:.2f} {gbs:.1f} {100 * gbs / HBM_PEAK_GBS:.2f} {name}", file=out, flush=True)
         del graph, tensors, temporal, conv, ids
         torch.cuda.empty_cache()
+        if not a.no_cpu_baseline:
+            # the CPU oracle (a memcpy loop) on one call of the same layout, for context
+            import oracle
+
+            host = [np.zeros((2 * nreqs, COPY_TEMPORAL_BYTES // 4), dtype=np.float32) for _ in range(COPY_LAYERS)] + \
+                   [np.zeros((2 * nreqs, COPY_CONV_BYTES // 2), dtype=np.uint16) for _ in range(COPY_LAYERS)]
+            for t in host:
+                t.fill(1)  # touch the pages before timing
+            src = np.arange(nreqs, dtype=np.int32)
+            dst = src + nreqs
+            t0 = time.perf_counter()
+            oracle.get().copy_blocks(host, src, dst)
+            sec = time.perf_counter() - t0
+            print(f"# cpu oracle (memcpy loop, 1 thread): {sec * 1e3:.1f} ms for one call of {nreqs} requests "
+                  f"({copy_gbps(nreqs, sec):.1f} GB/s)", file=out, flush=True)
+            del host
 
 
 # Selective scan over a sequence (prefill): the COREY page's kernel benchmark
