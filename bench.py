@@ -172,7 +172,7 @@ def time_graph(g, replays):
 def cpu_oracle_baseline(H, P, N, G, batch, seed, budget_s=20.0):
     """The CPU oracle (fp64, OpenMP over (request, head)) on host cores, on a
     bounded sample: whole calls of the same workload, repeated until about
-    `budget_s` of CPU time has passed (at least 2 calls, at most 5)."""
+    `budget_s` seconds have passed (at least 2 calls)."""
     import oracle
 
     ref = oracle.get()
@@ -184,7 +184,7 @@ def cpu_oracle_baseline(H, P, N, G, batch, seed, budget_s=20.0):
     p = si.make_problem(H, P, N, G, batch, slots, seed)
     times = []
     t_start = time.perf_counter()
-    while len(times) < 5 and (len(times) < 2 or time.perf_counter() - t_start < budget_s):
+    while len(times) < 2 or time.perf_counter() - t_start < budget_s:
         pool = p.pool.copy()
         t0 = time.perf_counter()
         ref.run(pool, p.idx, p.x, p.B, p.C, p.dt, p.A, p.dt_bias, p.D, True, want_state=False,
