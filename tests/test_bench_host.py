@@ -82,3 +82,20 @@ def test_copy_byte_formula_reproduces_the_pages_tables():
         got = bench.copy_gbps(int(reqs), float(us) * 1e-6)
         assert abs(got - float(gbps)) <= 0.001 * float(gbps), (gpu, reqs, got, gbps)
     assert abs(bench.copy_bytes_per_request() / 2 ** 20 - 49.88) < 0.01
+
+
+def test_scan_byte_formulas():
+    """The scan's algorithmic bytes, written out term by term for the page's
+    shape (batch 1, dim 1024, d_state 16, one group, 4096 tokens, 16-bit io),
+    and one launch's share at a static chunk of 512 tokens."""
+    import bench
+
+    bs, dim, N, G, L = 1, 1024, 16, 1, 4096
+    u = delta = out = 2 * bs * dim * L
+    Bb = Cb = 2 * bs * G * N * L
+    state_rw = 2 * 4 * bs * dim * N
+    params = 4 * dim * N + 4 * dim + 4 * dim   # A, D, delta_bias
+    assert bench.scan_bytes(bs, dim, N, G, L) == u + delta + out + Bb + Cb + state_rw + params == 25_559_040
+    per_launch = 3 * 2 * dim * 512 + 2 * 2 * N * 512 + state_rw + params
+    assert bench.scan_launch_bytes(bs, dim, N, G, 512) == per_launch == 3_383_296
+    assert bench.scan_elements(bs, dim, N, L) == 67_108_864
