@@ -95,7 +95,7 @@ def test_scan_byte_formulas():
     Bb = Cb = 2 * bs * G * N * L
     state_rw = 2 * 4 * bs * dim * N
     params = 4 * dim * N + 4 * dim + 4 * dim   # A, D, delta_bias
-    assert bench.scan_bytes(bs, dim, N, G, L) == u + delta + out + Bb + Cb + state_rw + params == 25_559_040
+    assert bench.scan_bytes(bs, dim, N, G, L) == u + delta + out + Bb + Cb + state_rw + params == 25_632_768
     per_launch = 3 * 2 * dim * 512 + 2 * 2 * N * 512 + state_rw + params
     assert bench.scan_launch_bytes(bs, dim, N, G, 512) == per_launch == 3_383_296
     assert bench.scan_elements(bs, dim, N, L) == 67_108_864
