@@ -318,3 +318,31 @@ def test_scan_long_sequence():
     for chunk in (1 << 18, 0):
         o, s = ds.run(chunk=chunk)
         check(p, o, s, r, f"L={L} chunk {chunk}")
+
+
+@pytest.mark.parametrize("case", range(12))
+def test_scan_random_shapes(case):
+    """Seeded random shapes: batch, dim, states, groups, length, activation
+    type, chunk, softplus and which optional parameters are present drawn
+    together, each against the oracle."""
+    import oracle
+
+    rng = np.random.Generator(np.random.PCG64([77, case]))
+    N = int(rng.integers(1, 65))
+    G = int(rng.choice([1, 2, 4]))
+    dim = G * int(rng.integers(1, 24))
+    batch = int(rng.integers(1, 4))
+    L = int(rng.integers(1, 3000))
+    io = str(rng.choice(["f16", "bf16"]))
+    softplus = bool(rng.integers(0, 2))
+    chunk = int(rng.choice([0, 64, 100, 512, 777]))
+    p = si.make_scan_problem(batch, dim, N, L, G, io=io, seed=1000 + case, zero_state=bool(rng.integers(0, 2)),
+                             delta_softplus=softplus)
+    if not softplus:
+        p.delta = si.io_bits(np.abs(si.io_values(p.delta, io)) * 0.05, io)
+        p.delta_bias = np.full(dim, 0.01, dtype=np.float32)
+    D, bias = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    r = oracle_scan(oracle.get(), p, D=D, bias=bias)
+    o, s = DeviceScan(p).run(chunk=chunk, D=D, bias=bias)
+    check(p, o, s, r, f"case {case}: batch {batch} dim {dim} N {N} G {G} L {L} {io} chunk {chunk} "
+                      f"softplus {softplus} D {D} bias {bias}")
