@@ -242,7 +242,10 @@ typedef struct ssu_block_tensor {
  * allocation-free and graph-capturable like ssu_update.
  * Errors: SSU_ERR_INVALID_ARGUMENT (negative sizes, null pointers, tile out of
  * range, overlapping blocks), SSU_ERR_MISALIGNED, SSU_ERR_UNSUPPORTED (more than
- * 2^31 workgroups), SSU_ERR_HIP. nreqs == 0 or ntensors == 0 is a no-op. */
+ * 2^31 workgroups in one launch), SSU_ERR_HIP. All of them but SSU_ERR_HIP are
+ * found before anything is enqueued; more than 32 tensors take one launch per
+ * 32, and SSU_ERR_HIP from a later launch leaves the earlier ones enqueued.
+ * nreqs == 0 or ntensors == 0 is a no-op. */
 ssu_status ssu_copy_blocks(const ssu_block_tensor *tensors, int32_t ntensors, const int32_t *src_blocks,
                            const int32_t *dst_blocks, int32_t nreqs, int32_t tile, hipStream_t stream);
 
@@ -297,10 +300,11 @@ typedef struct ssu_scan_args {
  * or any input (the kernel reads inputs through the read-only cache).
  * Asynchronous and graph-capturable; nothing is checked on the device.
  * Errors (nothing is launched): SSU_ERR_INVALID_ARGUMENT (null pointers,
- * negative sizes, wrong dtypes, dim % ngroups != 0, tile out of range),
- * SSU_ERR_UNSUPPORTED (non-contiguous token or state axis, dstate > 64,
- * batch * dim >= 2^31), SSU_ERR_MISALIGNED (elements not aligned to their
- * size), SSU_ERR_HIP (launch failure; earlier chunks may have run). */
+ * negative sizes or strides, wrong dtypes, non-zero reserved fields,
+ * dim % ngroups != 0, tile out of range), SSU_ERR_UNSUPPORTED (non-contiguous
+ * token or state axis, D or delta_bias, dstate > 64, batch * dim >= 2^31),
+ * SSU_ERR_MISALIGNED (elements not aligned to their size), SSU_ERR_HIP
+ * (launch failure; earlier chunks may have run). */
 ssu_status ssu_scan(const ssu_scan_args *args, int64_t chunk, int32_t tile, hipStream_t stream);
 
 /* Number of compiled scan configurations, and the name of one ("" if out of

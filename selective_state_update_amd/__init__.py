@@ -199,6 +199,14 @@ def _view(t, strides, tag) -> View:
     return v
 
 
+def _stream_of(stream, device):
+    """hipStream_t for ``stream``: a torch stream, a raw handle, or None for
+    torch's current stream on ``device`` (the operands' device)."""
+    if stream is None:
+        return _torch().cuda.current_stream(device).cuda_stream
+    return getattr(stream, "cuda_stream", stream)
+
+
 def _null_view() -> View:
     v = View()
     v.ptr = None
@@ -335,14 +343,12 @@ class Handle:
         a.out = _view(out, out.stride(), SSU_BF16)
         return a
 
-    def launch(self, args, stream=None):
+    def launch(self, args, stream=None, device=None):
         """Enqueue ssu_update (Args) or ssu_update_tokens (TokensArgs) with
         prepared arguments on ``stream`` (torch stream, raw hipStream_t int, or
-        None for torch's current stream)."""
-        if stream is None:
-            stream = _torch().cuda.current_stream().cuda_stream
-        elif hasattr(stream, "cuda_stream"):
-            stream = stream.cuda_stream
+        None for torch's current stream on ``device``, by default the current
+        device)."""
+        stream = _stream_of(stream, device)
         if isinstance(args, TokensArgs):
             st = _lib.ssu_update_tokens(self._h, ctypes.byref(args), _vp(stream))
             where = "ssu_update_tokens"
@@ -359,7 +365,7 @@ class Handle:
         if out is None:
             out = _torch().empty(x.shape, dtype=_torch().bfloat16, device=x.device)
         args = self.make_tokens_args(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)
-        self.launch(args, stream)
+        self.launch(args, stream, state.device)
         return out
 
     def update(self, state, state_batch_indices, x, B, C, dt, A, D=None, dt_bias=None, out=None,
@@ -369,12 +375,10 @@ class Handle:
             out = _torch().empty(x.shape, dtype=_torch().bfloat16, device=x.device)
         args = self.make_args(state, state_batch_indices, x, B, C, dt, A, D, dt_bias, out)
         if check_indices:
-            s = _torch().cuda.current_stream().cuda_stream if stream is None else getattr(
-                stream, "cuda_stream", stream)
-            st = _lib.ssu_check_indices(ctypes.byref(args), _vp(s))
+            st = _lib.ssu_check_indices(ctypes.byref(args), _vp(_stream_of(stream, state.device)))
             if st != SSU_OK:
                 raise SSUError(st, "ssu_check_indices")
-        self.launch(args, stream)
+        self.launch(args, stream, state.device)
         return out
 
 
@@ -412,7 +416,9 @@ def block_tensors(tensors):
     blocks (block i is ``t[i]``, which must be contiguous)."""
     descs = (BlockTensor * max(1, len(tensors)))()
     for k, t in enumerate(tensors):
-        if t.dim() < 1 or not t[0].is_contiguous():
+        if t.dim() < 1:
+            raise ValueError(f"tensor {k}: axis 0 must index blocks")
+        if t.shape[0] > 0 and not t[0].is_contiguous():
             raise ValueError(f"tensor {k}: block t[i] must be contiguous")
         if t.device.type != "cuda":
             raise ValueError(f"tensor {k} must be on a GPU")
@@ -434,14 +440,16 @@ def copy_blocks(tensors, src_blocks, dst_blocks, tile=-1, stream=None, descs=Non
         raise ValueError("src_blocks and dst_blocks must be [nreqs]")
     if not (src_blocks.is_contiguous() and dst_blocks.is_contiguous()):
         raise ValueError("block ids must be contiguous")
+    if src_blocks.device.type != "cuda" or dst_blocks.device != src_blocks.device:
+        raise ValueError("block ids must be on the same GPU")
+    if any(t.device != src_blocks.device for t in tensors):
+        raise ValueError("state tensors must be on the block ids' GPU")
     if descs is None:
         descs = block_tensors(tensors)
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    elif len(descs) < len(tensors):
+        raise ValueError("descs has fewer entries than tensors")
     st = _lib.ssu_copy_blocks(descs, len(tensors), src_blocks.data_ptr(), dst_blocks.data_ptr(),
-                              src_blocks.shape[0], tile, _vp(stream))
+                              src_blocks.shape[0], tile, _vp(_stream_of(stream, src_blocks.device)))
     if st != SSU_OK:
         raise SSUError(st, "ssu_copy_blocks")
 
@@ -478,13 +486,16 @@ def make_scan_args(u, delta, A, B, C, state, D=None, delta_bias=None, delta_soft
     for name, t in (("delta", delta), ("B", B), ("C", C)):
         if _dtype_tag(t, io, name) != ut:
             raise TypeError(f"{name} must have u's dtype")
-    for name, t in (("u", u), ("delta", delta), ("B", B), ("C", C), ("A", A), ("state", state)):
-        if t.device.type != "cuda":
-            raise ValueError(f"{name} must be on a GPU")
+    if u.device.type != "cuda":
+        raise ValueError("u must be on a GPU")
     if out is None:
         out = torch.empty((bs, dim, L), dtype=u.dtype, device=u.device)
     elif tuple(out.shape) != (bs, dim, L) or out.dtype != u.dtype:
         raise ValueError("out must be like u")
+    for name, t in (("delta", delta), ("B", B), ("C", C), ("A", A), ("state", state), ("D", D),
+                    ("delta_bias", delta_bias), ("out", out)):
+        if t is not None and t.device != u.device:
+            raise ValueError(f"{name} is on {t.device}, u on {u.device}")
     a = ScanArgs()
     a.batch, a.dim, a.dstate, a.ngroups, a.seqlen = bs, dim, N, G, L
     a.delta_softplus, a.reserved = int(bool(delta_softplus)), 0
@@ -505,14 +516,11 @@ def make_scan_args(u, delta, A, B, C, state, D=None, delta_bias=None, delta_soft
     return a, out
 
 
-def scan_launch(args, chunk=0, tile=-1, stream=None):
-    """ssu_scan on prepared ScanArgs (for timing loops and graph capture)."""
-    torch = _torch()
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    st = _lib.ssu_scan(ctypes.byref(args), int(chunk), int(tile), _vp(stream))
+def scan_launch(args, chunk=0, tile=-1, stream=None, device=None):
+    """ssu_scan on prepared ScanArgs (for timing loops and graph capture);
+    stream None: torch's current stream on ``device`` (default: the current
+    device)."""
+    st = _lib.ssu_scan(ctypes.byref(args), int(chunk), int(tile), _vp(_stream_of(stream, device)))
     if st != SSU_OK:
         raise SSUError(st, "ssu_scan")
 
@@ -523,5 +531,5 @@ def selective_scan(u, delta, A, B, C, state, D=None, delta_bias=None, delta_soft
     over all L tokens, in launches of ``chunk`` tokens (0: one launch).
     Returns out [batch, dim, L] in u's dtype."""
     args, out = make_scan_args(u, delta, A, B, C, state, D, delta_bias, delta_softplus, out)
-    scan_launch(args, chunk, tile, stream)
+    scan_launch(args, chunk, tile, stream, u.device)
     return out

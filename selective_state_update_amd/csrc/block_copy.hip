@@ -107,9 +107,10 @@ void add_copy_tiles(std::vector<CopyTile> &v)
             t.remap = remap;
             t.chunk = int64_t(U) * kThreads * 16;
             t.fn = &launch_copy<U>;
-            std::snprintf(t.name, sizeof t.name, "copy_u%d%s%s", U, remap ? "_xcd" : "", "");
             if (cap)
                 std::snprintf(t.name, sizeof t.name, "copy_u%d%s_g%d", U, remap ? "_xcd" : "", cap);
+            else
+                std::snprintf(t.name, sizeof t.name, "copy_u%d%s", U, remap ? "_xcd" : "");
             v.push_back(t);
         }
 }
@@ -192,32 +193,45 @@ ssu_status ssu_copy_blocks(const ssu_block_tensor *tensors, int32_t ntensors, co
             return fail(SSU_ERR_HIP, "cannot query the LDS size of device %d", dev);
         lds = lds_for_cap(T.cap, lim.lds_cu, lim.lds_block);
     }
-    // Launch over groups of up to kMaxTensors tensors.
+    // Launch over groups of up to kMaxTensors tensors. Every group's size is
+    // checked before the first launch, so a size error enqueues nothing.
+    auto group_chunks = [&](int32_t k0, CopyParams *p) -> int64_t {
+        int64_t chunks = 0;
+        int32_t n = 0;
+        for (int32_t k = k0; k < ntensors && n < kMaxTensors; ++k, ++n) {
+            const ssu_block_tensor &t = tensors[k];
+            const int64_t bytes = (t.block_bytes > 0 && t.nblocks > 0) ? t.block_bytes : 0;
+            if (p) {
+                p->t[n].base = static_cast<char *>(t.base);
+                p->t[n].stride = t.block_stride;
+                p->t[n].bytes = bytes;
+                p->t[n].nblocks = t.nblocks;
+                p->first_chunk[n] = static_cast<int32_t>(chunks);
+            }
+            chunks += (bytes + T.chunk - 1) / T.chunk;
+            if (chunks > 0x7fffffff)
+                return -1;
+        }
+        if (p) {
+            p->first_chunk[n] = static_cast<int32_t>(chunks);
+            p->ntensors = n;
+        }
+        return chunks;
+    };
+    for (int32_t k0 = 0; k0 < ntensors; k0 += kMaxTensors) {
+        const int64_t chunks = group_chunks(k0, nullptr);
+        if (chunks < 0 || chunks * nreqs > 0x7fffffff)
+            return fail(SSU_ERR_UNSUPPORTED, "ssu_copy_blocks: more than 2^31 workgroups in one launch");
+    }
     for (int32_t k0 = 0; k0 < ntensors; k0 += kMaxTensors) {
         CopyParams p{};
         p.src = src_blocks;
         p.dst = dst_blocks;
         p.xcd_remap = T.remap;
-        int64_t chunks = 0;
-        int32_t n = 0;
-        for (int32_t k = k0; k < ntensors && n < kMaxTensors; ++k, ++n) {
-            const ssu_block_tensor &t = tensors[k];
-            p.t[n].base = static_cast<char *>(t.base);
-            p.t[n].stride = t.block_stride;
-            p.t[n].bytes = (t.block_bytes > 0 && t.nblocks > 0) ? t.block_bytes : 0;
-            p.t[n].nblocks = t.nblocks;
-            p.first_chunk[n] = static_cast<int32_t>(chunks);
-            chunks += (p.t[n].bytes + T.chunk - 1) / T.chunk;
-            if (chunks > 0x7fffffff)
-                return fail(SSU_ERR_UNSUPPORTED, "ssu_copy_blocks: blocks too large");
-        }
-        p.first_chunk[n] = static_cast<int32_t>(chunks);
-        p.ntensors = n;
+        const int64_t chunks = group_chunks(k0, &p);
         if (chunks == 0)
             continue;
         const int64_t total = chunks * nreqs;
-        if (total > 0x7fffffff)
-            return fail(SSU_ERR_UNSUPPORTED, "ssu_copy_blocks: too many chunks for one launch");
         p.chunks_per_req = static_cast<int32_t>(chunks);
         p.total = static_cast<int32_t>(total);
         const hipError_t e = T.fn(p, static_cast<int>(total), lds, stream);

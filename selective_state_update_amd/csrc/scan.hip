@@ -548,8 +548,24 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
         return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: batch * dim too large");
     if (a->delta_softplus != 0 && a->delta_softplus != 1)
         return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: delta_softplus must be 0 or 1");
+    if (a->reserved != 0)
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: reserved field must be 0");
     if (bs == 0)
         return SSU_OK;
+    {
+        const ssu_view *vs[] = {&a->state, &a->u, &a->delta, &a->B, &a->C, &a->A, &a->D, &a->delta_bias, &a->out};
+        const char *names[] = {"state", "u", "delta", "B", "C", "A", "D", "delta_bias", "out"};
+        const int rank[] = {3, 3, 3, 4, 4, 2, 1, 1, 3};
+        for (int k = 0; k < 9; ++k) {
+            if (!vs[k]->ptr)
+                continue;
+            if (vs[k]->reserved != 0)
+                return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: %s: reserved field must be 0", names[k]);
+            for (int i = 0; i < rank[k]; ++i)
+                if (vs[k]->stride[i] < 0)
+                    return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: %s: negative stride[%d]", names[k], i);
+        }
+    }
 
     // operands
     if (!a->state.ptr || !a->A.ptr)
@@ -558,9 +574,12 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
         return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: state and A must be F32");
     if (a->state.stride[2] != 1)
         return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: the state's dstate axis must be contiguous");
-    for (const ssu_view *v : {&a->D, &a->delta_bias})
+    for (const ssu_view *v : {&a->D, &a->delta_bias}) {
         if (v->ptr && v->dtype != SSU_F32)
             return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_scan: D and delta_bias must be F32");
+        if (v->ptr && dim > 1 && v->stride[0] != 1)
+            return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: D and delta_bias must be contiguous");
+    }
     for (const ssu_view *v : {&a->state, &a->A, &a->D, &a->delta_bias})
         if (reinterpret_cast<uintptr_t>(v->ptr) % 4)
             return fail(SSU_ERR_MISALIGNED, "ssu_scan: F32 operand not 4-byte aligned");

@@ -34,6 +34,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdarg>
 #include <initializer_list>
@@ -42,6 +43,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <utility>
 #include <vector>
 
 #include "internal.h"
@@ -976,27 +978,37 @@ ssu_status ssu_check_indices(const ssu_args *a, hipStream_t stream)
     const bool i64 = a->idx.dtype == SSU_I64;
     if (!a->idx.ptr || (!i64 && a->idx.dtype != SSU_I32) || a->idx.stride[0] != 1)
         return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_check_indices: idx must be a contiguous i32/i64 view");
+    // Memory in proportion to the batch, never to the pool: the in-range
+    // (slot, position) pairs are sorted and neighbours compared.
     const size_t esz = i64 ? 8 : 4;
-    std::vector<unsigned char> host(esz * static_cast<size_t>(a->batch));
+    std::vector<unsigned char> host;
+    std::vector<std::pair<int64_t, int32_t>> live;
+    try {
+        host.resize(esz * static_cast<size_t>(a->batch));
+        live.reserve(static_cast<size_t>(a->batch));
+    } catch (const std::bad_alloc &) {
+        return fail(SSU_ERR_NO_MEMORY, "ssu_check_indices: out of host memory for %d entries", a->batch);
+    }
     if (hipMemcpyAsync(host.data(), a->idx.ptr, host.size(), hipMemcpyDeviceToHost, stream) != hipSuccess ||
         hipStreamSynchronize(stream) != hipSuccess)
         return fail(SSU_ERR_HIP, "ssu_check_indices: copy of idx failed");
-    std::vector<unsigned char> seen(static_cast<size_t>(a->pool_slots), 0);
     for (int32_t b = 0; b < a->batch; ++b) {
         int64_t s;
         if (i64) {
-            std::memcpy(&s, host.data() + 8 * b, 8);
+            std::memcpy(&s, host.data() + 8 * static_cast<size_t>(b), 8);
         } else {
             int32_t s32;
-            std::memcpy(&s32, host.data() + 4 * b, 4);
+            std::memcpy(&s32, host.data() + 4 * static_cast<size_t>(b), 4);
             s = s32;
         }
-        if (s < 0 || s >= a->pool_slots)
-            continue;
-        if (seen[s])
-            return fail(SSU_ERR_BAD_INDEX, "idx[%d] = %lld repeats an earlier entry", b, static_cast<long long>(s));
-        seen[s] = 1;
+        if (s >= 0 && s < a->pool_slots)
+            live.emplace_back(s, b);
     }
+    std::sort(live.begin(), live.end());
+    for (size_t k = 1; k < live.size(); ++k)
+        if (live[k].first == live[k - 1].first)
+            return fail(SSU_ERR_BAD_INDEX, "idx[%d] = %lld repeats idx[%d]", live[k].second,
+                        static_cast<long long>(live[k].first), live[k - 1].second);
     return SSU_OK;
 }
 

@@ -374,6 +374,22 @@ def test_copy_blocks_validation(ssu):
     assert lib.ssu_copy_tile_count() > 0
     assert lib.ssu_copy_tile_name(0).decode().startswith("copy_")
     assert lib.ssu_copy_tile_name(-1) == b""
+    names = [lib.ssu_copy_tile_name(i).decode() for i in range(lib.ssu_copy_tile_count())]
+    assert len(set(names)) == len(names) and "copy_u2_xcd" in names
+
+
+def test_copy_blocks_checks_every_group_before_launching(ssu):
+    """More than 32 tensors take one launch per 32; a size error in a later
+    group is reported before the first launch (here, with no GPU, a launch
+    attempt would return SSU_ERR_HIP instead)."""
+    B = ssu.BlockTensor
+    ids = ctypes.c_void_p(FAKE + 0x100000)
+    small = B(FAKE, 4096, 4096, 8)
+    huge = B(FAKE, 1 << 40, 1 << 40, 1)   # 2^27 chunks of 8 KiB per request
+    ts = [small] * 32 + [huge] + [small] * 7
+    arr = (B * len(ts))(*ts)
+    assert ssu._lib.ssu_copy_blocks(arr, len(ts), ids, ids, 32, -1, None) == 2  # 2^32 workgroups
+    assert "2^31" in ssu._lib.ssu_last_error().decode()
 
 
 # ------------------------------------------------------------------- ssu_scan --
@@ -437,6 +453,14 @@ def _scan_call(ssu, a, chunk=512, tile=-1):
     ("state misaligned", lambda a, s: setattr(a.state, "ptr", FAKE + 2), 3),
     ("u misaligned", lambda a, s: setattr(a.u, "ptr", FAKE + 0x100001), 3),
     ("batch * dim >= 2^31", lambda a, s: (setattr(a, "batch", 1 << 20), setattr(a, "dim", 1 << 12)), 2),
+    ("reserved field", lambda a, s: setattr(a, "reserved", 1), 1),
+    ("view reserved field", lambda a, s: setattr(a.B, "reserved", 7), 1),
+    ("negative state stride", lambda a, s: a.state.stride.__setitem__(1, -16), 1),
+    ("negative u stride", lambda a, s: a.u.stride.__setitem__(0, -100), 1),
+    ("negative B stride", lambda a, s: a.B.stride.__setitem__(2, -100), 1),
+    ("negative A stride", lambda a, s: a.A.stride.__setitem__(0, -16), 1),
+    ("D strided", lambda a, s: a.D.stride.__setitem__(0, 2), 2),
+    ("delta_bias strided", lambda a, s: a.delta_bias.stride.__setitem__(0, 0), 2),
 ])
 def test_scan_rejects_before_launch(ssu, what, mutate, code):
     a = _scan_args(ssu)

@@ -6,6 +6,8 @@ state within 1e-5 * (1 + |ref|), out within 2 bf16 ulp of bf16(fp32(y)) (with
 the cancellation floor of tests/tolerance.py), untouched slots bitwise
 unchanged, reruns and launch configurations bitwise identical.
 """
+import ctypes
+
 import numpy as np
 import pytest
 
@@ -271,8 +273,24 @@ def test_check_indices_detects_duplicates():
     h.update(dp.pool, dp.idx, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out, check_indices=True)
     dup = dp.idx.clone()
     dup[3] = dup[0]
-    with pytest.raises(ssu.SSUError, match="BAD_INDEX"):
+    with pytest.raises(ssu.SSUError, match=r"BAD_INDEX.*idx\[3\].*repeats idx\[0\]"):
         h.update(dp.pool, dup, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out, check_indices=True)
+
+    # padding entries (outside [0, pool_slots)) may repeat
+    pad = dp.idx.clone()
+    pad[1], pad[2] = -1, 8
+    pad[3] = -1
+    args = h.make_args(dp.pool, pad, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out)
+    assert ssu._lib.ssu_check_indices(ctypes.byref(args), None) == 0
+
+    # the check needs no memory in proportion to the pool: a pool of 2^40
+    # slots (never dereferenced here) is checked like any other
+    args = h.make_args(dp.pool, dup, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out)
+    args.pool_slots = 1 << 40
+    assert ssu._lib.ssu_check_indices(ctypes.byref(args), None) == 6
+    args = h.make_args(dp.pool, dp.idx, dp.x, dp.B, dp.C, dp.dt, dp.A, dp.D, dp.dt_bias, dp.out)
+    args.pool_slots = 1 << 40
+    assert ssu._lib.ssu_check_indices(ctypes.byref(args), None) == 0
 
 
 def test_strided_pool_view(ref):
