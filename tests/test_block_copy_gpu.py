@@ -100,3 +100,40 @@ def test_copy_page_layout_sample(ref):
     host, dev = _tensors(rng, 16, shapes)
     src, dst = _ids(rng, 16, 8)
     _check(ref, host, dev, src, dst)
+
+
+def test_copy_hip_graph_replays(ref):
+    """Copies captured in one HIP graph and replayed three times, the source
+    blocks changed by eager work before each replay: every replay copies the
+    current sources (checked against the oracle on the same host bits)."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    rng = np.random.Generator(np.random.PCG64(54))
+    host, dev = _tensors(rng, 11, SHAPES[:3])
+    src, dst = _ids(rng, 11, 4)
+    s_d, d_d = torch.from_numpy(src).cuda(), torch.from_numpy(dst).cuda()
+    src_rows = torch.from_numpy(src.astype(np.int64)).cuda()
+    descs = ssu.block_tensors(dev)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        ssu.copy_blocks(dev, s_d, d_d, descs=descs)  # warm-up, applied to the host copy too
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    ref.copy_blocks(host, src, dst)
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        ssu.copy_blocks(dev, s_d, d_d, descs=descs)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for h_, d_ in zip(host, dev):
+            new = rng.integers(0, 2 ** 16, size=h_[src].shape, dtype=np.uint16)
+            h_[src] = new
+            d_[src_rows] = torch.from_numpy(new.view(np.int16)).cuda()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        ref.copy_blocks(host, src, dst)
+        for j, (h_, d_) in enumerate(zip(host, dev)):
+            assert np.array_equal(d_.cpu().numpy().view(np.uint16), h_.view(np.uint16)), f"replay {k} tensor {j}"

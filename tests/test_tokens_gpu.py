@@ -160,3 +160,53 @@ def test_tokens_headline_shape_sampled(ref):
     ob = gu.bits(out)[sample]
     for t in range(K):
         gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"tokens headline t{t}")
+
+
+def test_tokens_hip_graph_replays_match_eager(ref):
+    """Two 3-token calls on disjoint slot sets captured in one HIP graph and
+    replayed three times with eager work in between: every replay equals the
+    eager round from the same state, and the first round matches the oracle."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    K = 3
+    tp = TokenProblem(4, 64, 128, 1, 5, 10, K, seed=3400)
+    other = np.setdiff1d(np.arange(10), tp.base.idx).astype(np.int32)
+    idx_sets = [torch.from_numpy(tp.base.idx).cuda(), torch.from_numpy(other).cuda()]
+    h = ssu.Handle(4, 64, 128, 1, True)
+    pool = torch.from_numpy(tp.base.pool).cuda()
+    d = tp.device(pool)
+    outs = [torch.empty((5, K, 4, 64), dtype=torch.bfloat16, device="cuda") for _ in idx_sets]
+
+    def calls():
+        for i, o in zip(idx_sets, outs):
+            h.update_tokens(pool, i, d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"], o)
+
+    start = pool.clone()
+    eager = []
+    for _ in range(3):
+        calls()
+        torch.cuda.synchronize()
+        eager.append((pool.clone(), [o.clone() for o in outs]))
+    pool.copy_(start)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        calls()  # warm-up on the side stream
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        calls()
+    pool.copy_(start)
+    torch.cuda.synchronize()
+    for k in range(3):
+        g.replay()
+        torch.cuda.synchronize()
+        _ = (pool[:1].sum() + 1).item()  # eager work between replays
+        want_pool, want_outs = eager[k]
+        assert torch.equal(pool.view(torch.int32), want_pool.view(torch.int32)), f"replay {k} state"
+        for o, w in zip(outs, want_outs):
+            assert torch.equal(o.view(torch.int16), w.view(torch.int16)), f"replay {k} out"
+    r = tp.oracle(ref, tp.base.pool.copy())
+    gu.assert_state(eager[0][0].cpu().numpy()[tp.base.idx], r["state"], "graph round 0")
