@@ -396,6 +396,54 @@ def run_tile_sweep(a):
         del g
 
 
+def parse_shapes(spec):
+    """'HxPxNxGxB,...' -> [(H, P, N, G, batch), ...]."""
+    shapes = []
+    for item in spec.split(","):
+        f = [int(v) for v in item.lower().split("x")]
+        if len(f) != 5 or min(f) < 1:
+            raise SystemExit(f"--shapes: '{item}' is not HxPxNxGxBATCH")
+        shapes.append(tuple(f))
+    return shapes
+
+
+def run_shapes(a):
+    """The decode step at other shapes (d_state, headdim, groups, heads,
+    batch), same rotation and graph method as the headline: one line per
+    shape with the library's launch configuration, and with --tile-sweep one
+    line per compiled configuration of that d_state."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    out = open(a.out, "w") if a.out else sys.stdout
+    print("H P N G batch state_MiB tile us_per_call GBps pct_peak", file=out, flush=True)
+    for (H, P, N, G, bs) in parse_shapes(a.shapes):
+        nbytes = algorithmic_bytes(H, P, N, G, bs)
+        rot = Rotation(H, P, N, G, bs, seed=7000 + H + P + N + G + bs)
+        auto = ssu.Handle(H, P, N, G, True, -1).selected_tile(bs)
+        ids = [auto]
+        if a.tile_sweep:
+            ids += [t["id"] for t in ssu.tiles()
+                    if t["dstate"] == N and P % t["rows_per_group"] == 0 and t["id"] != auto]
+        for tid in ids:
+            h = ssu.Handle(H, P, N, G, True, tid)
+            args = rot.args(h)
+            calls = max(20, rot.K)
+            g = capture(h, args, 0, calls)
+            g.replay()
+            torch.cuda.synchronize()
+            reps = [time_graph(g, 10) / (10 * calls) for _ in range(5)]
+            us = statistics.median(reps) * 1e6
+            gbs = nbytes / (us * 1e-6) / 1e9
+            name = ssu.tiles()[tid]["name"] + ("*" if tid == auto else "")  # * = the library's choice
+            print(f"{H} {P} {N} {G} {bs} {state_bytes(H, P, N, bs) / 2 ** 21:.0f} {name} {us:.3f} {gbs:.1f} "
+                  f"{100 * gbs / HBM_PEAK_GBS:.2f}", file=out, flush=True)
+            del g, args
+        del rot
+        torch.cuda.empty_cache()
+
+
 def run_copy_ceiling(a):
     """Attainable read+write HBM bandwidth on this machine: plain device copies of
     the headline call's state volume (256 MiB read + 256 MiB written), rotated
@@ -915,6 +963,7 @@ def main():
     ap.add_argument("--out", default="")
     ap.add_argument("--counters", action="store_true")
     ap.add_argument("--tile-sweep", action="store_true")
+    ap.add_argument("--shapes", default="", help="comma list of HxPxNxGxBATCH decode shapes")
     ap.add_argument("--copy-ceiling", action="store_true")
     ap.add_argument("--tokens", default="", help="comma list of tokens per call (ssu_update_tokens)")
     ap.add_argument("--copy-blocks", default="", help="comma list of request counts (ssu_copy_blocks)")
@@ -928,8 +977,8 @@ def main():
     ap.add_argument("--write-dir-name", default="pmc/write", help="WRITE_SIZE output directory (for the summary text)")
     a = ap.parse_args()
     if a.gpus != 1:
-        print("bench.py measures one GPU: selective_state_update has no cross-GPU exchange, and this "
-              "build runs on a single MI355X. Use --gpus 1.", file=sys.stderr)
+        print("bench.py measures one GPU: selective_state_update exchanges nothing between GPUs (each "
+              "GPU holds its heads' or requests' share), so only --gpus 1 is measured.", file=sys.stderr)
         sys.exit(2)
     if a.summarize_counters:
         summarize_counters(a)
@@ -941,6 +990,8 @@ def main():
         run_scan(a)
     elif a.counters:
         run_counters(a)
+    elif a.shapes:
+        run_shapes(a)
     elif a.tile_sweep:
         run_tile_sweep(a)
     elif a.copy_ceiling:

@@ -99,3 +99,13 @@ def test_scan_byte_formulas():
     per_launch = 3 * 2 * dim * 512 + 2 * 2 * N * 512 + state_rw + params
     assert bench.scan_launch_bytes(bs, dim, N, G, 512) == per_launch == 3_383_296
     assert bench.scan_elements(bs, dim, N, L) == 67_108_864
+
+
+def test_shape_list_parsing():
+    assert bench.parse_shapes("16x64x128x1x512,8X32x16x2x4") == [(16, 64, 128, 1, 512), (8, 32, 16, 2, 4)]
+    for bad in ("16x64x128x1", "16x64x128x1x0", "16x64x128xGx512"):
+        try:
+            bench.parse_shapes(bad)
+        except (SystemExit, ValueError):
+            continue
+        raise AssertionError(f"accepted {bad!r}")
