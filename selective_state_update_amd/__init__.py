@@ -50,6 +50,14 @@ if not os.path.exists(_LIB_PATH):
         "(there is no fallback implementation)"
     )
 
+# libssu must bind to the HIP runtime torch has loaded. torch ships its own
+# libamdhip64 (soname libamdhip64.so.7) and its libraries ask for it by file
+# name; if libssu were loaded first, it would bring in the system ROCm's
+# runtime under that soname, torch would then load its own copy as well, and
+# one of the two runtimes would see no device. Importing torch first makes
+# libssu's libamdhip64.so.7 resolve to torch's copy.
+import torch  # noqa: E402,F401
+
 _lib = ctypes.CDLL(_LIB_PATH)
 
 _i32, _i64, _vp = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p

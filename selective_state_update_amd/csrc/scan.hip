@@ -191,10 +191,14 @@ constexpr float kLn2 = 0.693147180559945309f;
 // 2 s (1 + s^2/3 + s^4/5 + ... + s^14/15) has terms shrinking by s^2 <= 1/9, so
 // eight of them reach fp32 precision. e is the hardware exp2 of
 // -|v| log2(e), with the rounding error of that product (exact by an fma)
-// and of the constant folded back in to first order.
+// and of the constant folded back in to first order. -|v| is clamped at -128,
+// where exp2 is already 0 in fp32, so that infinite v give e = 0 rather than
+// inf - inf; the positive part is a select that lets NaN through (fmaxf would
+// drop it): softplus(+inf) = +inf, softplus(-inf) = 0, softplus(NaN) = NaN,
+// and every finite v gives the same bits as without the clamp.
 __device__ __forceinline__ float softplus_f32(float v)
 {
-    const float x = -fabsf(v);
+    const float x = __builtin_amdgcn_fmed3f(-fabsf(v), -128.0f, 0.0f);  // NaN: carried by the select below
     const float t = x * kLog2e;
     const float r = fmaf(x, kLog2e, -t) + x * kLog2eLo;
     const float e0 = __builtin_amdgcn_exp2f(t);
@@ -209,7 +213,7 @@ __device__ __forceinline__ float softplus_f32(float v)
     q = fmaf(q, s2, 1.0f / 5.0f);
     q = fmaf(q, s2, 1.0f / 3.0f);
     q = fmaf(q, s2, 1.0f);
-    return fmaxf(v, 0.0f) + 2.0f * sv * q;
+    return (v <= 0.0f ? 0.0f : v) + 2.0f * sv * q;
 }
 
 // One wave's share of one (request, channel): its 16 states' carried values

@@ -343,3 +343,48 @@ def test_largest_sweep_point_sampled(ref):
     torch.cuda.synchronize()
     assert torch.equal(out.view(torch.int16), o1.view(torch.int16))
     assert torch.equal(pool[sl].view(torch.int32), s1.view(torch.int32))
+
+
+def test_nonfinite_values_stay_in_their_rows(ref):
+    """NaN and infinity in the state, in x and in dt reach exactly the state
+    elements and outputs the recurrence routes them to, with the oracle's IEEE
+    class and sign, and every finite result keeps its tolerance: nothing
+    spreads across rows, heads or requests (the row sums and the cross-lane
+    reduction included)."""
+    from . import tolerance as tol
+
+    torch = gu.torch_mod()
+    p = si.make_problem(H=2, P=64, N=128, batch=5, pool_slots=9, seed=1400)
+    s = p.idx
+    p.pool[s[0], 0, 5, 7] = np.nan       # one state element
+    p.pool[s[1], 1, 10, 3] = np.inf      # infinities in two rows of one head
+    p.pool[s[1], 1, 11, 4] = -np.inf
+    P = p.headdim
+    p.xbc[2, 0 * P + 20] = 0x7FC0        # NaN in x (request 2, head 0, row 20)
+    p.xbc[3, 1 * P + 30] = 0x7F80        # +inf in x (request 3, head 1, row 30)
+    p.dt[4, 0] = 0x7FC0                  # NaN step: the whole (request 4, head 0)
+    before = p.pool.copy()
+    dp = gu.DeviceProblem(p)
+    out = dp.run()
+    torch.cuda.synchronize()
+    r = gu.oracle_step(ref, p, before.copy())
+
+    got = dp.pool.cpu().numpy()[s].astype(np.float64)
+    want = r["state"]
+    for cls in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(cls(got), cls(want)), f"state class {cls.__name__}"
+    assert np.isnan(want).any() and np.isinf(want).any()
+    fin = np.isfinite(want)
+    assert not tol.state_violations(got[fin], want[fin]).any(), "finite state"
+
+    ob = gu.bits(out)
+    g = tol.bf16_to_f64(ob)
+    y = r["y"]
+    for cls in (np.isnan, np.isposinf, np.isneginf):
+        assert np.array_equal(cls(g), cls(y)), f"out class {cls.__name__}"
+    assert np.isnan(y[4, 0]).all() and np.isfinite(y[4, 1]).all()
+    fin = np.isfinite(y)
+    fail, _ = tol.out_check(ob[fin], r["out"][fin], y[fin], r["tau"][fin])
+    assert not fail.any(), "finite out"
+    untouched = np.setdiff1d(np.arange(p.pool_slots), s)
+    assert np.array_equal(dp.pool.cpu().numpy()[untouched].view(np.uint32), before[untouched].view(np.uint32))

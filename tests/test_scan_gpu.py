@@ -346,3 +346,51 @@ def test_scan_random_shapes(case):
     o, s = DeviceScan(p).run(chunk=chunk, D=D, bias=bias)
     check(p, o, s, r, f"case {case}: batch {batch} dim {dim} N {N} G {G} L {L} {io} chunk {chunk} "
                       f"softplus {softplus} D {D} bias {bias}")
+
+
+def _same_nonfinite(gpu, ref, what):
+    """Finite exactly where the oracle is; NaN where it is NaN; where it is
+    infinite, the same infinity or NaN. (A state that has become infinite
+    stays infinite in the sequential oracle, since every decay is positive; the
+    kernel composes a block's decays into one product, which underflows to 0
+    for fast-decaying states, and 0 * inf is NaN.)"""
+    g = np.asarray(gpu, dtype=np.float64)
+    assert np.array_equal(np.isfinite(g), np.isfinite(ref)), f"{what}: finite pattern"
+    assert np.isnan(g[np.isnan(ref)]).all(), f"{what}: NaN"
+    for sign in (np.isposinf, np.isneginf):
+        m = sign(ref)
+        assert (sign(g[m]) | np.isnan(g[m])).all(), f"{what}: {sign.__name__}"
+
+
+def test_scan_nonfinite_inputs():
+    """Infinite and NaN activations reach exactly the outputs and states the
+    recurrence routes them to: a step of -inf (softplus 0) is the identity, a
+    step of +inf wipes the channel's memory and makes it non-finite from that
+    token on, a NaN input poisons its channel from that token on; earlier
+    tokens and other channels keep their tolerance."""
+    import oracle
+
+    ref = oracle.get()
+    p = si.make_scan_problem(1, 8, 16, 1100, 1, io="f16", seed=63, zero_state=False)
+    p.delta[0, 1, 100] = 0x7C00   # +inf
+    p.delta[0, 2, 300] = 0xFC00   # -inf
+    p.u[0, 3, 500] = 0x7E00       # NaN
+    r = oracle_scan(ref, p)
+    o, s = DeviceScan(p).run(chunk=512)
+    g = tol.io_to_f64(o, p.io)
+    y, st = r["y"], r["state"]
+    _same_nonfinite(g, y, "out")
+    _same_nonfinite(s, st, "state")
+    # where they land
+    assert np.isfinite(y[0, 1, :100]).all() and not np.isfinite(y[0, 1, 100:]).any()
+    assert np.isinf(st[0, 1]).all()
+    assert np.isfinite(y[0, 2]).all() and np.isfinite(st[0, 2]).all()
+    assert np.isfinite(y[0, 3, :500]).all() and np.isnan(y[0, 3, 500:]).all() and np.isnan(st[0, 3]).all()
+    others = [0, 4, 5, 6, 7]
+    assert np.isfinite(y[0, others]).all() and np.isfinite(st[0, others]).all()
+    fin = np.isfinite(y)
+    bad = tol.scan_out_violations(o[fin], y[fin], r["tau"][fin], r["rho"][fin], p.dstate, p.io)
+    assert not bad.any(), "finite outputs"
+    fin = np.isfinite(st)
+    bad = tol.scan_state_violations(s[fin], st[fin], r["err"][fin])
+    assert not bad.any(), "finite states"
