@@ -80,8 +80,9 @@ typedef struct ssu_config {
                             >= 0: always use tile #tile (for sweeps; see ssu_tile_info).
                             The environment variable SSU_TILE, read by ssu_create,
                             overrides a -1 here the same way. */
-    int32_t device;      /* HIP device ordinal that launches run on; -1: the
-                            device current at the first launch */
+    int32_t device;      /* HIP device ordinal that launches run on (made
+                            current for the call, then restored); -1: the
+                            device current at each call */
     int32_t reserved;    /* must be 0 */
 } ssu_config;
 
