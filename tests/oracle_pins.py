@@ -625,5 +625,32 @@ def pin_scan_error_scale(o):
     assert np.all(np.abs(h - r["state"]) <= 4 * eps * r["err"])
 
 
+def pin_scan_infinite_step(o):
+    """A step of -inf with softplus on has size softplus(-inf) = 0: decay 1,
+    input 0, so the scan is exactly the scan of the sequence with that token
+    deleted (final state and every other token's y, bitwise in fp64), and its
+    own y is C . h + D u of the state before it. Softplus of -inf is 0 in the
+    limit; a form such as u + log1p(exp(-u)) gives NaN there."""
+    p = _scan_problem(seed=31, L=12, zero_state=False)
+    t = 5
+    p.delta[..., t] = 0xFC00  # -inf (fp16)
+    state, r = _scan_run(o, p)
+    keep = np.array([k for k in range(p.seqlen) if k != t])
+    q = si.ScanProblem(**{**p.__dict__, "u": p.u[..., keep], "delta": p.delta[..., keep], "B": p.B[..., keep],
+                          "C": p.C[..., keep], "seqlen": p.seqlen - 1})
+    q_state, rq = _scan_run(o, q)
+    assert np.array_equal(r["state"], rq["state"]) and np.array_equal(state, q_state)
+    assert np.array_equal(r["y"][..., keep], rq["y"])
+    before = p.__dict__.copy()
+    pre = si.ScanProblem(**{**before, "u": p.u[..., :t], "delta": p.delta[..., :t], "B": p.B[..., :t],
+                            "C": p.C[..., :t], "seqlen": t})
+    _, rp = _scan_run(o, pre)
+    g = np.arange(p.dim) // (p.dim // p.ngroups)
+    C_t = si.io_values(p.C[..., t], p.io).astype(np.float64)[:, g]        # [batch, dim, N]
+    u_t = si.io_values(p.u[..., t], p.io).astype(np.float64)
+    y_t = np.einsum("bdn,bdn->bd", rp["state"], C_t) + p.D[None, :] * u_t
+    assert np.allclose(r["y"][..., t], y_t, rtol=1e-13, atol=1e-13)
+
+
 PINS.extend([pin_f16_decode, pin_f16_rounding, pin_scan_brute_force, pin_scan_closed_form, pin_scan_no_decay,
-             pin_scan_memoryless, pin_scan_zero_step, pin_scan_split, pin_scan_error_scale])
+             pin_scan_memoryless, pin_scan_zero_step, pin_scan_split, pin_scan_error_scale, pin_scan_infinite_step])

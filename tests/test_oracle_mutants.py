@@ -31,6 +31,7 @@ MUTANTS = [
     ("drop_bias", "double u = dt + dt_bias;", "double u = dt;"),
     ("softplus_sign", "log1p(exp(-fabs(u)))", "log1p(exp(fabs(u)))"),
     ("softplus_naive", "return fmax(u, 0.0) + log1p(exp(-fabs(u)));", "return log(1.0 + exp(u));"),
+    ("softplus_shifted_form", "return fmax(u, 0.0) + log1p(exp(-fabs(u)));", "return u + log1p(exp(-u));"),
     ("softplus_ignored", "double d = softplus ? ssu_ref_softplus(u) : u;", "double d = u;"),
     ("group_map", "(((int64_t)h * G) / H)", "(h % G)"),
     ("slot_is_request", "g->state + slot * g->st_slot", "g->state + (int64_t)b * g->st_slot"),
