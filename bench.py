@@ -442,6 +442,10 @@ def run_shapes(a):
             del g, args
         del rot
         torch.cuda.empty_cache()
+        if not a.no_cpu_baseline:
+            cb = cpu_oracle_baseline(H, P, N, G, bs, seed=7000 + H + P + N + G + bs, budget_s=2.0)
+            print(f"# cpu oracle (fp64, {cb['cores']} threads): {cb['us_per_call'] / 1e3:.2f} ms per call, "
+                  f"{cb['value']:.1f} GB/s", file=out, flush=True)
 
 
 def run_copy_ceiling(a):
