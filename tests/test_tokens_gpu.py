@@ -210,3 +210,25 @@ def test_tokens_hip_graph_replays_match_eager(ref):
             assert torch.equal(o.view(torch.int16), w.view(torch.int16)), f"replay {k} out"
     r = tp.oracle(ref, tp.base.pool.copy())
     gu.assert_state(eager[0][0].cpu().numpy()[tp.base.idx], r["state"], "graph round 0")
+
+
+@pytest.mark.parametrize("K", [100, 1024])
+def test_tokens_beyond_one_discretisation_batch(ref, K):
+    """More tokens than one wave discretises at once (64 per batch, one per
+    lane), up to the maximum of 1024: the fused call still equals K successive
+    one-token calls bitwise, and the oracle's fp64 scan within the state and
+    out tolerances (the decays keep fp32 rounding from accumulating: an fp32
+    emulation stays near 1e-7 relative at K = 1024)."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    tp = TokenProblem(2, 64, 128, 1, 3, 7, K, seed=3500 + K)
+    h = ssu.Handle(2, 64, 128, 1, True)
+    pool_f, out_f, pool_s, out_s = _fused_and_sequential(tp, h)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "out differs from sequential"
+    assert torch.equal(pool_f.view(torch.int32), pool_s.view(torch.int32)), "state differs from sequential"
+    r = tp.oracle(ref, tp.base.pool.copy())
+    gu.assert_state(pool_f.cpu().numpy()[tp.base.idx], r["state"], f"K={K} state")
+    ob = gu.bits(out_f)
+    for t in (0, 63, 64, K - 1):
+        gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"K={K} token {t}")
