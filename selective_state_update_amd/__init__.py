@@ -241,10 +241,12 @@ class Handle:
         self.dt_softplus = bool(dt_softplus)
         self.tile = tile
 
-    def __del__(self):
+    # bound when the class is defined: at interpreter exit the module's
+    # globals may already be cleared when the last handles are collected
+    def __del__(self, _destroy=_lib.ssu_destroy):
         h = getattr(self, "_h", None)
         if h is not None and h.value:
-            _lib.ssu_destroy(h)
+            _destroy(h)
             self._h = None
 
     def selected_tile(self, batch: int, ntokens: int = 1) -> int:

@@ -503,3 +503,17 @@ def test_scan_binding_validates(ssu):
         ssu.make_scan_args(u, u.bfloat16(), A, B, B, st)
     with pytest.raises(TypeError):
         ssu.make_scan_args(u.float(), u.float(), A, B.float(), B.float(), st)
+
+
+def test_handle_released_after_module_globals_are_cleared(ssu):
+    """At interpreter exit a module's globals may be cleared (set to None)
+    before the last handles are collected; a handle must still release itself
+    then (seen as an 'Exception ignored in Handle.__del__' message at exit)."""
+    h = ssu.Handle(16, 64, 128)
+    saved = ssu._lib
+    try:
+        ssu._lib = None  # what finalization does to the module's globals
+        h.__del__()
+    finally:
+        ssu._lib = saved
+    assert h._h is None
