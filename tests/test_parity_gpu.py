@@ -388,3 +388,47 @@ def test_nonfinite_values_stay_in_their_rows(ref):
     assert not fail.any(), "finite out"
     untouched = np.setdiff1d(np.arange(p.pool_slots), s)
     assert np.array_equal(dp.pool.cpu().numpy()[untouched].view(np.uint32), before[untouched].view(np.uint32))
+
+
+@pytest.mark.parametrize("case", range(16))
+def test_random_shapes(ref, case):
+    """Seeded random shapes and options drawn together: d_state, headdim,
+    heads, groups, batch, pool size, padding entries, int32 or int64 ids,
+    softplus, dt_bias and D present or not, and the library's launch
+    configuration or a random compiled one; every element against the oracle,
+    untouched slots bitwise."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    rng = np.random.Generator(np.random.PCG64([88, case]))
+    N = int(rng.choice([16, 32, 64, 128, 256]))
+    P = 16 * int(rng.integers(1, 17))
+    H = int(rng.integers(1, 25))
+    G = int(rng.choice([g for g in range(1, H + 1) if H % g == 0]))
+    per_unit = P * N * 4
+    bs = int(rng.integers(1, max(2, min(40, (48 << 20) // (per_unit * H)) + 1)))
+    slots = bs + int(rng.integers(0, 11))
+    softplus = bool(rng.integers(0, 2))
+    use_bias, use_D = bool(rng.integers(0, 2)), bool(rng.integers(0, 2))
+    p = si.make_problem(H=H, P=P, N=N, G=G, batch=bs, pool_slots=slots, seed=5000 + case, dt_softplus=softplus)
+    if not softplus:
+        # steps dt + dt_bias >= 0, as a step size is: a negative one makes the
+        # decay exp(A * delta) grow and can overflow fp32
+        p.dt = p.dt & np.uint16(0x7FFF)
+        p.dt_bias = np.full(H, 0.01, dtype=np.float32)
+    idx = p.idx.copy()
+    if bs > 1 and rng.integers(0, 2):
+        idx[int(rng.integers(0, bs))] = -1 if rng.integers(0, 2) else slots  # padding
+    p.idx = idx
+    tile = -1
+    if rng.integers(0, 10) < 3:
+        fits = [t["id"] for t in ssu.tiles() if t["dstate"] == N and P % t["rows_per_group"] == 0]
+        tile = int(rng.choice(fits))
+    what = (f"case {case}: N {N} P {P} H {H} G {G} bs {bs} slots {slots} softplus {softplus} "
+            f"bias {use_bias} D {use_D} tile {tile}")
+    print(what, flush=True)
+    dp = gu.DeviceProblem(p)
+    ids = dp.idx.to(torch.int64) if rng.integers(0, 2) else dp.idx
+    out = dp.run(tile=tile, use_bias=use_bias, use_D=use_D, idx=ids)
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, what, use_bias=use_bias, use_D=use_D)
