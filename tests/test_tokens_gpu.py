@@ -232,3 +232,31 @@ def test_tokens_beyond_one_discretisation_batch(ref, K):
     ob = gu.bits(out_f)
     for t in (0, 63, 64, K - 1):
         gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"K={K} token {t}")
+
+
+@pytest.mark.parametrize("case", range(8))
+def test_tokens_random_shapes(ref, case):
+    """Seeded random K-token calls: d_state, headdim, heads, groups, batch and
+    K (1 .. 80) drawn together; fused = sequential bitwise, and the oracle's
+    fp64 scan within tolerance."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    rng = np.random.Generator(np.random.PCG64([89, case]))
+    N = int(rng.choice([16, 32, 64, 128, 256]))
+    P = 16 * int(rng.integers(1, 17))
+    H = int(rng.integers(1, 9))
+    G = int(rng.choice([g for g in range(1, H + 1) if H % g == 0]))
+    bs = int(rng.integers(1, 9))
+    K = int(rng.integers(1, 81))
+    print(f"case {case}: N {N} P {P} H {H} G {G} bs {bs} K {K}", flush=True)
+    tp = TokenProblem(H, P, N, G, bs, bs + 3, K, seed=3600 + case)
+    h = ssu.Handle(H, P, N, G, True)
+    pool_f, out_f, pool_s, out_s = _fused_and_sequential(tp, h)
+    assert torch.equal(out_f.view(torch.int16), out_s.view(torch.int16)), "out differs from sequential"
+    assert torch.equal(pool_f.view(torch.int32), pool_s.view(torch.int32)), "state differs from sequential"
+    r = tp.oracle(ref, tp.base.pool.copy())
+    gu.assert_state(pool_f.cpu().numpy()[tp.base.idx], r["state"], f"case {case} state")
+    ob = gu.bits(out_f)
+    for t in sorted({0, K // 2, K - 1}):
+        gu.assert_out(ob[:, t], {k: r[k][t] for k in ("out", "y", "tau")}, f"case {case} token {t}")
