@@ -670,13 +670,16 @@ def run_scan(a):
     import selective_state_update_amd as ssu
 
     out = open(a.out, "w") if a.out else sys.stdout
-    print("config chunk launches us_per_seq ms_per_seq Mtokens_per_s GBps hbm_pct Gelem_per_s warm_us_per_seq tile",
-          file=out, flush=True)
+    print("config chunk launches us_per_seq ms_per_seq Mtokens_per_s GBps hbm_pct Gelem_per_s warm_us_per_seq tile "
+          "batch", file=out, flush=True)
     chunks = [int(c) for c in a.chunks.split(",")]
     for k in [int(c) for c in a.scan.split(",")]:
         cfg = dict(si.SCAN_CONFIGS[k])
         name = cfg.pop("name")
         cfg.pop("chunk")
+        if a.scan_batch:
+            cfg["batch"] = a.scan_batch
+            name += f", batch {a.scan_batch}"
         bs, dim, N, G, L = cfg["batch"], cfg["dim"], cfg["dstate"], cfg["ngroups"], cfg["seqlen"]
         nbytes = scan_bytes(bs, dim, N, G, L)
         K = max(2, -(-ROTATION_BYTES // nbytes))
@@ -730,8 +733,8 @@ def run_scan(a):
                 tname = ssu.scan_tiles()[tile] if tile >= 0 else "default"
                 print(f"{k} {chunk} {launches} {us:.2f} {us / 1e3:.4f} {bs * L / us:.2f} {gbs:.1f} "
                       f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {warm:.2f} "
-                      f"{tname}", file=out, flush=True)
-        if k == 1 and not a.no_cpu_baseline:
+                      f"{tname} {bs}", file=out, flush=True)
+        if k == 1 and not a.no_cpu_baseline and not a.scan_batch:
             # the CPU oracle on one sequence of this workload, for context
             import oracle
 
@@ -973,6 +976,7 @@ def main():
     ap.add_argument("--copy-blocks", default="", help="comma list of request counts (ssu_copy_blocks)")
     ap.add_argument("--scan", default="", help="comma list of scan configs (ssu_scan), e.g. 1,2,3")
     ap.add_argument("--chunks", default="512", help="comma list of scan chunk sizes (0: one launch)")
+    ap.add_argument("--scan-batch", type=int, default=0, help="override the scan workload's batch (requests)")
     ap.add_argument("--scan-counters", action="store_true", help="eager scans for rocprofv3 --pmc")
     ap.add_argument("--summarize-scan-counters", default="")
     ap.add_argument("--summarize-counters", default="")
