@@ -24,8 +24,10 @@
 //   * out[p] = sum_n S'[p,n] C[n]: each lane sums its own columns in order
 //     (an fma chain), then the LPR lanes of a row combine in a fixed butterfly
 //     (DPP quad permutes, row half-mirror, row mirror, then a swizzle across
-//     the two 16-lane rows). The order depends only on N, never on the tile,
-//     so every tile gives bitwise-identical results, and no atomics are used.
+//     the two 16-lane rows), taken as a reduce-scatter over a lane's rows so
+//     that each level adds only the rows the lane keeps. A row's order depends
+//     only on N, never on the tile, so every tile gives bitwise-identical
+//     results, and no atomics are used.
 //   * No MFMA: 2 flops of update and 2 of contraction per 8 bytes of state is
 //     far below the vector-ALU ridge; the bound is HBM bandwidth.
 //   * Optional XCD-aware ordering: workgroups are dispatched round-robin over
@@ -95,23 +97,99 @@ __device__ __forceinline__ float dpp(float v)
     return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, true));
 }
 
-// Sum over each aligned group of LPR lanes (LPR in 4..32); every lane of the
-// group receives the same bits. Butterfly order: lane pairs, quads, eights,
-// sixteens, then the two 16-lane rows of a 32-lane half.
-template <int LPR>
-__device__ __forceinline__ float group_sum(float v)
+// Butterfly partner of level k (0-based) within an aligned group of LPR
+// lanes: lane ^ 1, lane ^ 2 (quad permutes), the mirror of each 8 and of each
+// 16 lanes (row half-mirror, row mirror), then lane ^ 16 within 32 (swizzle,
+// bitmask mode). Any value summed over these five pairings in this order gets
+// the same bits in every lane of the group.
+template <int K>
+__device__ __forceinline__ float partner(float v)
 {
-    static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "LPR");
-    v += dpp<0xB1>(v);  // quad_perm [1,0,3,2]: lane ^ 1
-    v += dpp<0x4E>(v);  // quad_perm [2,3,0,1]: lane ^ 2
-    if constexpr (LPR >= 8)
-        v += dpp<0x141>(v);  // row_half_mirror: pairs quad 0 with quad 1 of each 8
-    if constexpr (LPR >= 16)
-        v += dpp<0x140>(v);  // row_mirror: pairs the two 8-lane halves of each row
-    if constexpr (LPR >= 32)  // swizzle, bitmask mode: lane ^ 16 within 32
-        v += __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
-    return v;
+    if constexpr (K == 0)
+        return dpp<0xB1>(v);  // quad_perm [1,0,3,2]
+    else if constexpr (K == 1)
+        return dpp<0x4E>(v);  // quad_perm [2,3,0,1]
+    else if constexpr (K == 2)
+        return dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i of each 8
+    else if constexpr (K == 3)
+        return dpp<0x140>(v);  // row_mirror: lane i <-> 15 - i of each 16
+    else
+        return __int_as_float(__builtin_amdgcn_ds_swizzle(__float_as_int(v), 0x401F));
 }
+
+// Which half of its rows a lane keeps at reduce-scatter level k: a function
+// of the lane's bits that differs between the level's two partners and agrees
+// between the partners of every other level (level 2 pairs lanes that differ
+// in bits 0-2, level 3 in bits 0-3), so a lane and its partner always hold
+// the same rows, and after the last level all lanes that share a row hold it.
+__device__ __forceinline__ bool keep_upper(int lane, int k)
+{
+    const int b0 = lane & 1, b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1;
+    switch (k) {
+    case 0: return (b0 ^ b2) != 0;
+    case 1: return (b1 ^ b2) != 0;
+    case 2: return (b2 ^ b3) != 0;
+    default: return b3 != 0;
+    }
+}
+
+// a if sel, else b, as a bit blend: straight-line code that the compiler
+// cannot turn into a dynamically indexed load from the caller's array (which
+// it would have to place in memory).
+__device__ __forceinline__ float pick(bool sel, float a, float b)
+{
+    const uint32_t m = 0u - static_cast<uint32_t>(sel);
+    return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
+}
+
+// Sums of R rows, each split over an aligned group of LPR lanes (LPR in
+// 4..32, R in 1..16), as a reduce-scatter: at level k every lane keeps half of
+// its rows, adds its partner's partial of each kept row and sends the other
+// half, until one row per lane is left (or R / LPR rows when R > LPR); the
+// levels that remain sum that row as a plain butterfly. Each row's total is
+// the sum over the same pairings in the same order as summing the row alone
+// (fp32 addition commutes), so its bits do not depend on R. On return y[0 ..
+// KEEP) hold the totals of rows first + i, and x[] the matching x values.
+template <int LPR, int R>
+struct RowSums {
+    static constexpr int log2(int v) { return v <= 1 ? 0 : 1 + log2(v / 2); }
+    static constexpr int LEVELS = log2(LPR);
+    static constexpr int SPLIT = log2(R) < LEVELS ? log2(R) : LEVELS;
+    static constexpr int KEEP = R >> SPLIT;
+    static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "LPR");
+    static_assert(R >= 1 && R <= 16 && (R & (R - 1)) == 0, "R");
+
+    template <int K>
+    __device__ __forceinline__ static void level(float (&y)[R], float (&x)[R], int lane, int &first)
+    {
+        if constexpr (K < LEVELS) {
+            if constexpr (K < SPLIT) {
+                constexpr int HALF = R >> (K + 1);
+                const bool up = keep_upper(lane, K);
+#pragma unroll
+                for (int i = 0; i < HALF; ++i) {
+                    const float lo = y[i], hi = y[i + HALF];
+                    y[i] = pick(up, hi, lo) + partner<K>(pick(up, lo, hi));
+                    x[i] = pick(up, x[i + HALF], x[i]);
+                }
+                first += up ? HALF : 0;
+            } else {
+#pragma unroll
+                for (int i = 0; i < KEEP; ++i)
+                    y[i] += partner<K>(y[i]);
+            }
+            level<K + 1>(y, x, lane, first);
+        }
+    }
+
+    // Returns the index of the first row this lane holds.
+    __device__ __forceinline__ static int run(float (&y)[R], float (&x)[R], int lane)
+    {
+        int first = 0;
+        level<0>(y, x, lane, first);
+        return first;
+    }
+};
 
 // One lane's share of one tile: `rows_per_group` consecutive state rows of one
 // (request, head), split over the workgroup's waves (R row groups of RPI rows
@@ -131,19 +209,25 @@ struct Work {
     int b, h, grp, c, sub, wrow, p0;
     float *sp;
     int64_t jstep;
-    u32x2 Bw[VEC], Cw[VEC];
     f32x4 s[R][VEC];
     uint32_t dtbits;
     float bias, Ah, Dh;
-    uint32_t xbits[R];
+
+    // One token's operands for this lane: its columns of B and C (bf16
+    // pairs) and the x of its rows (bf16 in the upper half of each word).
+    struct Ops {
+        u32x2 Bw[VEC], Cw[VEC];
+        uint32_t xbits[R];
+    };
+    Ops op;  // token 0's, requested by fetch()
 
     // This lane's columns of B and C for token t (8-byte vector loads).
-    __device__ __forceinline__ void load_bc(const Params &p, int t)
+    __device__ __forceinline__ void load_bc(const Params &p, int t, Ops &o) const
     {
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + t * p.B_t + grp * p.B_g + 4 * c + 128 * v);
-            Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + t * p.C_t + grp * p.C_g + 4 * c + 128 * v);
+            o.Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + t * p.B_t + grp * p.B_g + 4 * c + 128 * v);
+            o.Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + t * p.C_t + grp * p.C_g + 4 * c + 128 * v);
         }
     }
 
@@ -158,19 +242,21 @@ struct Work {
     // x of this lane's rows wrow + sub + j*RPI for token t. With two rows per
     // instruction the wave's rows are R whole 32-bit words at a uniform
     // address (scalar loads); otherwise each lane reads its own values.
-    __device__ __forceinline__ void load_x(const Params &p, int t)
+    __device__ __forceinline__ void load_x(const Params &p, int t, Ops &o) const
     {
         const uint16_t *xrow = p.x + b * p.x_b + t * p.x_t + h * p.x_h + wrow;
         if constexpr (RPI == 2) {
+            // one byte permute per row: this lane's half of the word into the
+            // upper half (byte selectors 0-3 name the word's bytes, 0x0C a zero)
             const uint32_t *xw = reinterpret_cast<const uint32_t *>(xrow);
-            const uint32_t sh = 16u * static_cast<uint32_t>(1 - sub);
+            const uint32_t sel = sub ? 0x03020C0Cu : 0x01000C0Cu;
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                xbits[j] = (load_ro(xw + j) << sh) & 0xffff0000u;
+                o.xbits[j] = __builtin_amdgcn_perm(0u, load_ro(xw + j), sel);
         } else {
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
+                o.xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
         }
     }
 
@@ -204,7 +290,7 @@ struct Work {
         // B and C do not depend on the slot: requested first (vector-memory
         // counters retire in order, so anything issued after the state stream
         // could only be used after it).
-        load_bc(p, 0);
+        load_bc(p, 0, op);
 
         const int64_t slot = p.idx64 ? load_ro(static_cast<const int64_t *>(p.idx) + b)
                                      : static_cast<int64_t>(load_ro(static_cast<const int32_t *>(p.idx) + b));
@@ -227,30 +313,30 @@ struct Work {
         Ah = load_ro(p.A + h * p.A_h);
         Dh = p.D ? load_ro(p.D + h * p.D_h) : 0.0f;
         load_dt(p, 0);
-        load_x(p, 0);
+        load_x(p, 0, op);
     }
 
-    // Advance the state by token t with its discretisation (delta, dA);
-    // write the state back when LAST.
+    // Advance the state by token t (operands o) with its discretisation
+    // (delta, dA); write the state back when LAST.
     template <bool LAST>
-    __device__ __forceinline__ void step(const Params &p, int t, float delta, float dA)
+    __device__ __forceinline__ void step(const Params &p, int t, const Ops &o, float delta, float dA)
     {
         float Bv[VEC][4], Cv[VEC][4];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            Bv[v][0] = __uint_as_float(Bw[v].x << 16);
-            Bv[v][1] = __uint_as_float(Bw[v].x & 0xffff0000u);
-            Bv[v][2] = __uint_as_float(Bw[v].y << 16);
-            Bv[v][3] = __uint_as_float(Bw[v].y & 0xffff0000u);
-            Cv[v][0] = __uint_as_float(Cw[v].x << 16);
-            Cv[v][1] = __uint_as_float(Cw[v].x & 0xffff0000u);
-            Cv[v][2] = __uint_as_float(Cw[v].y << 16);
-            Cv[v][3] = __uint_as_float(Cw[v].y & 0xffff0000u);
+            Bv[v][0] = __uint_as_float(o.Bw[v].x << 16);
+            Bv[v][1] = __uint_as_float(o.Bw[v].x & 0xffff0000u);
+            Bv[v][2] = __uint_as_float(o.Bw[v].y << 16);
+            Bv[v][3] = __uint_as_float(o.Bw[v].y & 0xffff0000u);
+            Cv[v][0] = __uint_as_float(o.Cw[v].x << 16);
+            Cv[v][1] = __uint_as_float(o.Cw[v].x & 0xffff0000u);
+            Cv[v][2] = __uint_as_float(o.Cw[v].y << 16);
+            Cv[v][3] = __uint_as_float(o.Cw[v].y & 0xffff0000u);
         }
         float xv[R];
 #pragma unroll
         for (int j = 0; j < R; ++j)
-            xv[j] = __uint_as_float(xbits[j]);
+            xv[j] = __uint_as_float(o.xbits[j]);
 
         // Update in registers (write back after the last token) and form each
         // lane's partial output.
@@ -279,24 +365,16 @@ struct Work {
             }
         }
 
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            y[j] = group_sum<LPR>(y[j]);
-
-        // Lane c of each row group writes row (k + c) of its R rows, so one
-        // store instruction covers up to LPR rows per sub-row.
+        // Row totals: this lane ends up with KEEP of them, rows first + i.
+        // When R < LPR several lanes of a row group hold each row; lane c < R
+        // is its one writer (the map from c to first is one to one on those).
+        using RS = RowSums<LPR, R>;
+        const int first = RS::run(y, xv, sub * LPR + c);  // the wave lane
         uint16_t *op = p.out + b * p.o_b + t * p.o_t + h * p.o_h + p0;
+        if (R >= LPR || c < R) {
 #pragma unroll
-        for (int k = 0; k < R; k += LPR) {
-            float yo = y[k], xo = xv[k];
-#pragma unroll
-            for (int j = k + 1; j < R && j < k + LPR; ++j)
-                if (c == j - k) {
-                    yo = y[j];
-                    xo = xv[j];
-                }
-            if (c < R - k)
-                op[(k + c) * RPI] = bf16_round(fmaf(Dh, xo, yo));
+            for (int i = 0; i < RS::KEEP; ++i)
+                op[(first + i) * RPI] = bf16_round(fmaf(Dh, xv[i], y[i]));
         }
     }
 
@@ -304,7 +382,7 @@ struct Work {
     {
         float delta, dA;
         discretize(p, dtbits, delta, dA);
-        step<true>(p, 0, delta, dA);
+        step<true>(p, 0, op, delta, dA);
     }
 };
 
@@ -323,10 +401,12 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
 // One workgroup per tile, p.ntokens tokens: the state is read once, advanced
 // token by token in registers with the same arithmetic as the one-token
 // kernel, and written once; each token's out is written as it is formed. The
-// operands of token t+1 are requested before token t is computed, and the
-// per-token discretisation is done 64 tokens at a time, one token per lane
-// (the same fp32 operations as the one-token kernel, so the same bits), then
-// read back with a uniform lane read.
+// operands of token t+1 are requested before token t is computed, into the
+// other of two operand sets (the loop goes two tokens per trip, so the sets
+// alternate without register copies), and the per-token discretisation is
+// done 64 tokens at a time, one token per lane (the same fp32 operations as
+// the one-token kernel, so the same bits), then read back with a uniform lane
+// read.
 template <int N, int R, int W, bool NT>
 __global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params p)
 {
@@ -339,31 +419,42 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params 
         return;
     const int K = p.ntokens;
     float lane_delta = 0.0f, lane_dA = 1.0f;
-    for (int t = 0; t < K; ++t) {
+    // (delta, dA) of token t, discretising tokens t .. t+63 when t starts a
+    // group of 64
+    auto disc = [&](int t, float &delta, float &dA) {
         const int tl = t & 63;
-        if (tl == 0 && t + lane < K) {  // discretise tokens t .. t+63, one per lane
+        if (tl == 0 && t + lane < K) {
             const int64_t dte = w.b * p.dt_b + (t + lane) * p.dt_t + w.h * p.dt_h + p.dt_off;
             const uint32_t dtw = p.dt_words[dte >> 1];
             w.discretize(p, (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu), lane_delta, lane_dA);
         }
-        const float delta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_delta), tl));
-        const float dA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_dA), tl));
-        if (t + 1 == K) {
-            w.template step<true>(p, t, delta, dA);
-            break;
-        }
-        WK next = w;  // same tile; only the token operands are replaced below
-        next.load_bc(p, t + 1);
-        next.load_x(p, t + 1);
-        w.template step<false>(p, t, delta, dA);
-#pragma unroll
-        for (int v = 0; v < WK::VEC; ++v) {
-            w.Bw[v] = next.Bw[v];
-            w.Cw[v] = next.Cw[v];
-        }
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            w.xbits[j] = next.xbits[j];
+        delta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_delta), tl));
+        dA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_dA), tl));
+    };
+    typename WK::Ops o1;
+    float delta, dA;
+    int t = 0;
+    for (; t + 2 < K; t += 2) {  // tokens t (operands w.op) and t+1 (o1)
+        w.load_bc(p, t + 1, o1);
+        w.load_x(p, t + 1, o1);
+        disc(t, delta, dA);
+        w.template step<false>(p, t, w.op, delta, dA);
+        w.load_bc(p, t + 2, w.op);
+        w.load_x(p, t + 2, w.op);
+        disc(t + 1, delta, dA);
+        w.template step<false>(p, t + 1, o1, delta, dA);
+    }
+    // one or two tokens left, the first with operands w.op
+    if (t + 1 < K) {
+        w.load_bc(p, t + 1, o1);
+        w.load_x(p, t + 1, o1);
+        disc(t, delta, dA);
+        w.template step<false>(p, t, w.op, delta, dA);
+        disc(t + 1, delta, dA);
+        w.template step<true>(p, t + 1, o1, delta, dA);
+    } else {
+        disc(t, delta, dA);
+        w.template step<true>(p, t, w.op, delta, dA);
     }
 }
 
@@ -587,8 +678,10 @@ int select_tile(const ssu_config &c, int32_t batch, int32_t ntokens)
         // Several tokens per call make each workgroup's work longer and
         // ALU-heavier: full occupancy hides that better than the cap, and
         // from 4 tokens on, eight loads per lane (fewer waves repeating the
-        // per-token work) win (batch 512, 8 tokens: 129 us against 139 us
-        // with four loads uncapped and 202 us capped).
+        // per-token work) win (batch 512, 8 tokens: 108.3 us against 120.9 us
+        // with four loads uncapped and 173.3 us with four loads capped at 12;
+        // at 4 tokens the two are within 1% at batch 512, eight loads 2.6%
+        // ahead at batch 128).
         const int loads = ntokens >= 4 ? 8 : 4;
         const int id = pick(loads, 1, ntokens > 1 ? 0 : 12);
         if (id >= 0)

@@ -101,20 +101,31 @@ def test_tokens_match_sequential_bitwise_and_oracle(ref, N, P, H, G, bs, K):
     assert np.array_equal(gpu[untouched].view(np.uint32), tp.base.pool[untouched].view(np.uint32))
 
 
-def test_tokens_every_tile_bitwise():
+@pytest.mark.parametrize("N", [128, 16, 32, 64, 256])
+def test_tokens_every_tile_bitwise(ref, N):
+    """Every launch configuration of every dstate (each splits a state row
+    over its own number of lanes and sums rows in its own grouping) gives the
+    same bits; the first is also checked against the oracle."""
     import selective_state_update_amd as ssu
 
     torch = gu.torch_mod()
-    tp = TokenProblem(4, 64, 128, 1, 6, 13, 3, seed=3100)
+    tp = TokenProblem(4, 64, N, 1, 6, 13, 3, seed=3100 + N)
     base = None
-    for t in [x for x in ssu.tiles() if x["dstate"] == 128]:
-        h = ssu.Handle(4, 64, 128, 1, True, t["id"])
+    ids = [x for x in ssu.tiles() if x["dstate"] == N and 64 % x["rows_per_group"] == 0]
+    assert ids
+    for t in ids:
+        h = ssu.Handle(4, 64, N, 1, True, t["id"])
         pool = torch.from_numpy(tp.base.pool).cuda()
         d = tp.device(pool)
         o = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
         torch.cuda.synchronize()
         if base is None:
             base = (o.clone(), pool.clone())
+            r = tp.oracle(ref, tp.base.pool.copy())
+            gu.assert_state(pool.cpu().numpy()[tp.base.idx], r["state"], f"N={N} {t['name']} state")
+            ob = gu.bits(o)
+            for k in range(tp.K):
+                gu.assert_out(ob[:, k], {key: r[key][k] for key in ("out", "y", "tau")}, f"N={N} token {k}")
         else:
             assert torch.equal(o.view(torch.int16), base[0].view(torch.int16)), t["name"]
             assert torch.equal(pool.view(torch.int32), base[1].view(torch.int32)), t["name"]
