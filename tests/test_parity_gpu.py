@@ -124,6 +124,32 @@ def test_padding_and_int64_indices(ref):
     assert np.array_equal(dp2.pool.cpu().numpy().view(np.uint32), pool_gpu.view(np.uint32))
 
 
+def test_request_permutation_bitwise(ref):
+    """Requests are independent: permuting (idx, x, B, C, dt) together over
+    the batch permutes out the same way, bitwise, and leaves the same pool,
+    in launch configurations with and without XCD-ordered workgroups."""
+    import dataclasses
+
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    p = si.make_problem(H=4, P=64, N=128, batch=11, pool_slots=25, seed=810)
+    perm = np.random.default_rng(810).permutation(p.batch)
+    q = dataclasses.replace(p, xbc=p.xbc[perm].copy(), dt=p.dt[perm].copy(), idx=p.idx[perm].copy())
+    tiles = [-1] + [t["id"] for t in ssu.tiles()
+                    if t["name"] in ("n128_r8_w1_nt_xcd_g12", "n128_r4_w2_nt", "n128_r16_w2_xcd")]
+    assert len(tiles) == 4
+    for tile in tiles:
+        dp, dq = gu.DeviceProblem(p), gu.DeviceProblem(q)
+        op = dp.run(tile=tile)
+        oq = dq.run(tile=tile)
+        torch.cuda.synchronize()
+        if tile == -1:
+            gu.compare_full(ref, dp, p.pool.copy(), op, "unpermuted")
+        assert np.array_equal(gu.bits(oq), gu.bits(op)[perm]), f"tile {tile}: out not permuted alike"
+        assert torch.equal(dq.pool.view(torch.int32), dp.pool.view(torch.int32)), f"tile {tile}: pools differ"
+
+
 def test_dt_zero_leaves_state_unchanged(ref):
     torch = gu.torch_mod()
     p = si.make_problem(H=4, P=64, N=128, batch=5, pool_slots=9, seed=900, dt_softplus=False)
