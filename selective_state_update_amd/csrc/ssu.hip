@@ -270,6 +270,9 @@ struct Work {
     }
 
     // graw: workgroup-order tile id (>= total_groups: nothing to do).
+    // PRIO: the caller raised the wave's priority; it is lowered once the
+    // state loads are issued.
+    template <bool PRIO = false>
     __device__ __forceinline__ void fetch(const Params &p, int graw, int rows_group, int wave, int lane)
     {
         if (graw >= p.total_groups) {
@@ -306,6 +309,9 @@ struct Work {
 #pragma unroll
             for (int v = 0; v < VEC; ++v)
                 s[j][v] = load4<NT>(sp + j * jstep + 128 * v);
+
+        if constexpr (PRIO)
+            __builtin_amdgcn_s_setprio(0);
 
         // Per-head parameters and token 0's dt and x through the scalar cache,
         // while the state is in flight.
@@ -414,7 +420,11 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params 
     const int lane = static_cast<int>(threadIdx.x) & 63;
     const int wave = __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) >> 6);
     WK w;
-    w.fetch(p, static_cast<int>(blockIdx.x), WK::ROWS_WAVE * W, wave, lane);
+    // Until its state is requested a wave takes issue slots before the waves
+    // computing tokens on state that has arrived (fetch() drops the priority
+    // after the state loads), so the state stream starts sooner.
+    __builtin_amdgcn_s_setprio(2);
+    w.template fetch<true>(p, static_cast<int>(blockIdx.x), WK::ROWS_WAVE * W, wave, lane);
     if (!w.live)
         return;
     const int K = p.ntokens;
