@@ -686,14 +686,20 @@ int select_tile(const ssu_config &c, int32_t batch, int32_t ntokens)
     };
     if (state_bytes >= (int64_t(32) << 20)) {
         // Several tokens per call make each workgroup's work longer and
-        // ALU-heavier: full occupancy hides that better than the cap, and
-        // from 4 tokens on, eight loads per lane (fewer waves repeating the
-        // per-token work) win (batch 512, 8 tokens: 108.3 us against 120.9 us
-        // with four loads uncapped and 173.3 us with four loads capped at 12;
-        // at 4 tokens the two are within 1% at batch 512, eight loads 2.6%
-        // ahead at batch 128).
-        const int loads = ntokens >= 4 ? 8 : 4;
-        const int id = pick(loads, 1, ntokens > 1 ? 0 : 12);
+        // ALU-heavier: full occupancy hides that better than the cap. From 8
+        // tokens on (from 4 below 128 MiB of state), eight loads per lane win
+        // (fewer waves repeating the per-token work; batch 512, 8 tokens:
+        // 107.8 us against 120.0 us with four loads, 172.2 us with four loads
+        // capped at 12), and from 16 tokens two-wave groups (batch 512:
+        // 154.6 us against 156.8 us with one wave). At 4 tokens four loads
+        // lead at batch 512 (96.6 against 98.6 us), eight at batch 128 (29.2
+        // against 30.1 us).
+        const bool big = state_bytes >= (int64_t(128) << 20);
+        const int loads = (ntokens >= 8 || (ntokens >= 4 && !big)) ? 8 : 4;
+        const int waves = ntokens >= 16 ? 2 : 1;
+        int id = pick(loads, waves, ntokens > 1 ? 0 : 12);
+        if (id < 0 && waves > 1)
+            id = pick(loads, 1, 0);
         if (id >= 0)
             return id;
     }

@@ -146,6 +146,36 @@ def test_select_tile_fits_shape(ssu, N, P):
     ssu._lib.ssu_destroy(h)
 
 
+@pytest.mark.parametrize("bs,K,name", [
+    (512, 1, "n128_r8_w1_nt_xcd_g12"), (128, 1, "n128_r8_w1_nt_xcd_g12"), (8, 1, "n128_r4_w2_nt_xcd"),
+    (512, 2, "n128_r8_w1_nt_xcd"), (512, 3, "n128_r8_w1_nt_xcd"), (512, 4, "n128_r8_w1_nt_xcd"),
+    (512, 8, "n128_r16_w1_nt_xcd"), (512, 16, "n128_r16_w2_nt_xcd"),
+    (128, 4, "n128_r16_w1_nt_xcd"), (128, 16, "n128_r16_w2_nt_xcd"),
+])
+def test_launch_rule_at_the_swept_points(ssu, bs, K, name):
+    """The launch table picks, at H16 P64 N128, the configurations the tile
+    sweeps measured fastest (or within 0.2% of it)."""
+    st, h = _create(ssu)
+    assert st == 0
+    i = ssu._lib.ssu_select_tile_tokens(h, bs, K) if K > 1 else ssu._lib.ssu_select_tile(h, bs)
+    assert ssu.tiles()[i]["name"] == name
+    ssu._lib.ssu_destroy(h)
+
+
+@pytest.mark.parametrize("N", [16, 32, 64, 256])
+@pytest.mark.parametrize("P", [16, 64, 256])
+def test_select_tile_tokens_fits_shape(ssu, N, P):
+    st, h = _create(ssu, dstate=N, headdim=P)
+    assert st == 0
+    t = ssu.tiles()
+    for bs in (1, 8, 128, 512, 1024):
+        for K in (2, 4, 8, 16, 64):
+            i = ssu._lib.ssu_select_tile_tokens(h, bs, K)
+            assert i >= 0
+            assert t[i]["dstate"] == N and P % t[i]["rows_per_group"] == 0
+    ssu._lib.ssu_destroy(h)
+
+
 # ---------------------------------------------------------------- ssu_update --
 FAKE = 0x7F0000000000  # 256-byte aligned fake device address, never dereferenced
 
