@@ -149,18 +149,22 @@ def test_tokens_padding():
     assert np.array_equal(pool.cpu().numpy()[untouched], tp.base.pool[untouched])
 
 
-def test_tokens_headline_shape_sampled(ref):
-    """H16 P64 N128, batch 512, 4 tokens (the state read and written once):
-    sampled requests against the oracle's scan."""
+@pytest.mark.parametrize("K,tile", [(4, "n128_r8_w1_nt_xcd"), (8, "n128_r16_w1_nt_xcd"),
+                                    (16, "n128_r16_w2_nt_xcd")])
+def test_tokens_headline_shape_sampled(ref, K, tile):
+    """H16 P64 N128, batch 512, K tokens (the state read and written once), in
+    the launch configuration the library picks for K: sampled requests against
+    the oracle's scan."""
     import selective_state_update_amd as ssu
 
     torch = gu.torch_mod()
-    bs, K = 512, 4
-    tp = TokenProblem(16, 64, 128, 1, bs, bs, K, seed=3300, host_pool=False)
+    bs = 512
+    tp = TokenProblem(16, 64, 128, 1, bs, bs, K, seed=3300 + K, host_pool=False)
     pool = torch.empty((bs, 16, 64, 128), device="cuda")
     si.draw_pool_on_device(pool, 3300)
     before = pool.clone()
     h = ssu.Handle(16, 64, 128, 1, True)
+    assert ssu.tiles()[h.selected_tile(bs, K)]["name"] == tile
     d = tp.device(pool)
     out = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
     torch.cuda.synchronize()
