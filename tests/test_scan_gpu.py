@@ -394,3 +394,28 @@ def test_scan_nonfinite_inputs():
     fin = np.isfinite(st)
     bad = tol.scan_state_violations(s[fin], st[fin], r["err"][fin])
     assert not bad.any(), "finite states"
+
+
+def test_scan_many_requests_sampled():
+    """The saturation workload: 16 requests x 1024 channels, d_state 16, 4096
+    fp16 tokens, static chunk 512. Chunk 512 is bitwise equal to one launch,
+    and sampled (request, channel) pairs, the corners among them, match the
+    oracle's scan of that pair alone."""
+    import dataclasses
+
+    import oracle
+
+    p = si.make_scan_problem(16, 1024, 16, 4096, io="f16", seed=17, zero_state=False)
+    ds = DeviceScan(p)
+    out512, st512 = ds.run(chunk=512)
+    out1, st1 = ds.run(chunk=0)
+    assert np.array_equal(out512, out1), "chunk 512 and one launch differ (out)"
+    assert np.array_equal(st512.view(np.uint32), st1.view(np.uint32)), "chunk 512 and one launch differ (state)"
+    rng = np.random.default_rng(17)
+    pairs = [(0, 0), (15, 1023), (7, 512)] + [(int(rng.integers(16)), int(rng.integers(1024))) for _ in range(5)]
+    for b, d in pairs:
+        q = dataclasses.replace(p, batch=1, dim=1, u=p.u[b:b + 1, d:d + 1], delta=p.delta[b:b + 1, d:d + 1],
+                                B=p.B[b:b + 1], C=p.C[b:b + 1], A=p.A[d:d + 1], D=p.D[d:d + 1],
+                                delta_bias=p.delta_bias[d:d + 1], state=p.state[b:b + 1, d:d + 1])
+        r = oracle_scan(oracle.get(), q)
+        check(q, out512[b:b + 1, d:d + 1], st512[b:b + 1, d:d + 1], r, f"request {b} channel {d}")
