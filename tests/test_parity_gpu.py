@@ -335,6 +335,37 @@ def test_strided_pool_view(ref):
     assert torch.equal(big[:, [0, 2]], other)
 
 
+@pytest.mark.parametrize("H,P,N,G,bs", [
+    (16, 64, 16, 1, 4096), (16, 64, 32, 1, 2048), (16, 64, 64, 1, 1024), (16, 64, 256, 1, 256),
+    (16, 32, 128, 1, 1024), (16, 128, 128, 1, 256), (16, 64, 128, 2, 512), (16, 64, 128, 8, 512),
+])
+def test_other_shapes_at_bench_size_sampled(ref, H, P, N, G, bs):
+    """The other-shape workloads at their measured size (256 MiB of state per
+    call) in the launch configuration the library picks: sampled requests
+    against the oracle, untouched slots bitwise."""
+    torch = gu.torch_mod()
+    slots = bs + 16
+    p = si.make_problem(H=H, P=P, N=N, G=G, batch=bs, pool_slots=slots, seed=900 + N + P + G, host_pool=False)
+    pool = torch.empty((slots, H, P, N), device="cuda")
+    si.draw_pool_on_device(pool, p.seed)
+    dp = gu.DeviceProblem(p, pool=pool)
+    backup = pool.clone()
+    out = dp.run()
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(N + P + G))
+    sample = np.sort(np.concatenate([[0, bs - 1], rng.choice(np.arange(1, bs - 1), size=4, replace=False)]))
+    sl = torch.from_numpy(p.idx[sample].astype(np.int64)).cuda()
+    sub_pool = backup[sl].cpu().numpy()
+    r = ref.run(sub_pool, np.arange(len(sample), dtype=np.int32), p.x[sample], p.B[sample], p.C[sample],
+                p.dt[sample], p.A, p.dt_bias, p.D)
+    what = f"H{H} P{P} N{N} G{G} bs{bs}"
+    gu.assert_state(pool[sl].cpu().numpy(), r["state"], what)
+    gu.assert_out(gu.bits(out)[sample], r, what)
+    mask = torch.ones(slots, dtype=torch.bool, device="cuda")
+    mask[torch.from_numpy(p.idx.astype(np.int64)).cuda()] = False
+    assert torch.equal(pool[mask].view(torch.int32), backup[mask].view(torch.int32)), what
+
+
 def test_largest_sweep_point_sampled(ref):
     """H=128, batch 1024 (4 GiB of state per call) in the launch configuration
     the library picks: sampled requests against the oracle, untouched slots
