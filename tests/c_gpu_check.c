@@ -2,8 +2,10 @@
  * runtime is the system ROCm's. A decode step and a two-chunk scan run on
  * hipMalloc'd buffers and are checked against the CPU oracle, compiled into
  * this program from oracle/ssu_ref.c, under the same acceptance rules as the
- * Python parity tests. Prints "ok" and returns 0 when everything passes; any
- * HIP or libssu error is printed and returns 1.
+ * Python parity tests; a 3-token call must equal three one-token calls
+ * bitwise, and a block copy must move exactly the named blocks. Prints "ok"
+ * and returns 0 when everything passes; any HIP or libssu error is printed and
+ * returns 1.
  *
  * Built by __graft_entry__.build() (gcc, next to this file); run by
  * tests/test_c_gpu.py on a GPU. */
@@ -244,6 +246,104 @@ static int check_scan(void)
     return bad != 0;
 }
 
+/* ssu_update_tokens (3 tokens) against three ssu_update calls: bitwise. */
+static int check_tokens(void)
+{
+    enum { H = 2, P = 64, N = 128, G = 1, BS = 3, K = 3, SLOTS = 4, ROW = H * P + 2 * G * N };
+    const int32_t idx[BS] = {3, 0, 2};
+    static float pool[SLOTS * H * P * N], pool_f[SLOTS * H * P * N], pool_s[SLOTS * H * P * N];
+    static uint16_t xbc[BS * K * ROW], dt[BS * K * H], out_f[BS * K * H * P], out_s[BS * K * H * P];
+    float A[H], D[H], bias[H];
+    for (int i = 0; i < SLOTS * H * P * N; ++i)
+        pool[i] = 2.0f * rand_unit() - 1.0f;
+    for (int i = 0; i < BS * K * ROW; ++i)
+        xbc[i] = rand_bf16();
+    for (int i = 0; i < BS * K * H; ++i)
+        dt[i] = rand_bf16();
+    for (int h = 0; h < H; ++h)
+        A[h] = -(0.5f + rand_unit()), D[h] = rand_unit(), bias[h] = -2.0f * rand_unit();
+
+    float *d_pool = to_device(pool, sizeof pool);
+    void *d_idx = to_device(idx, sizeof idx), *d_xbc = to_device(xbc, sizeof xbc), *d_dt = to_device(dt, sizeof dt);
+    void *d_A = to_device(A, sizeof A), *d_D = to_device(D, sizeof D), *d_bias = to_device(bias, sizeof bias);
+    void *d_out = NULL;
+    HIP_OK(hipMalloc(&d_out, sizeof out_f));
+    ssu_config cfg = {H, P, N, G, 1, -1, -1, 0};
+    ssu_handle *h = NULL;
+    SSU_OK_(ssu_create(&cfg, &h));
+
+    /* [request, token, ...] layouts: xBC rows and dt per (request, token) */
+    ssu_tokens_args a;
+    memset(&a, 0, sizeof a);
+    a.batch = BS, a.ntokens = K, a.pool_slots = SLOTS;
+    a.state = (ssu_view){d_pool, SSU_F32, 0, {H * P * N, P * N, N, 1}};
+    a.idx = (ssu_view){d_idx, SSU_I32, 0, {1, 0, 0, 0}};
+    a.x = (ssu_view){d_xbc, SSU_BF16, 0, {K * ROW, ROW, P, 1}};
+    a.B = (ssu_view){(uint16_t *)d_xbc + H * P, SSU_BF16, 0, {K * ROW, ROW, N, 1}};
+    a.C = (ssu_view){(uint16_t *)d_xbc + H * P + G * N, SSU_BF16, 0, {K * ROW, ROW, N, 1}};
+    a.dt = (ssu_view){d_dt, SSU_BF16, 0, {K * H, H, 1, 0}};
+    a.dt_bias = (ssu_view){d_bias, SSU_F32, 0, {1, 0, 0, 0}};
+    a.A = (ssu_view){d_A, SSU_F32, 0, {1, 0, 0, 0}};
+    a.D = (ssu_view){d_D, SSU_F32, 0, {1, 0, 0, 0}};
+    a.out = (ssu_view){d_out, SSU_BF16, 0, {K * H * P, H * P, P, 1}};
+    SSU_OK_(ssu_update_tokens(h, &a, NULL));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(pool_f, d_pool, sizeof pool, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(out_f, d_out, sizeof out_f, hipMemcpyDeviceToHost));
+
+    HIP_OK(hipMemcpy(d_pool, pool, sizeof pool, hipMemcpyHostToDevice));
+    HIP_OK(hipMemset(d_out, 0, sizeof out_f));
+    for (int t = 0; t < K; ++t) {
+        ssu_args s1;
+        memset(&s1, 0, sizeof s1);
+        s1.batch = BS, s1.pool_slots = SLOTS;
+        s1.state = a.state, s1.idx = a.idx, s1.dt_bias = a.dt_bias, s1.A = a.A, s1.D = a.D;
+        s1.x = (ssu_view){(uint16_t *)d_xbc + t * ROW, SSU_BF16, 0, {K * ROW, P, 1, 0}};
+        s1.B = (ssu_view){(uint16_t *)d_xbc + t * ROW + H * P, SSU_BF16, 0, {K * ROW, N, 1, 0}};
+        s1.C = (ssu_view){(uint16_t *)d_xbc + t * ROW + H * P + G * N, SSU_BF16, 0, {K * ROW, N, 1, 0}};
+        s1.dt = (ssu_view){(uint16_t *)d_dt + t * H, SSU_BF16, 0, {K * H, 1, 0, 0}};
+        s1.out = (ssu_view){(uint16_t *)d_out + t * H * P, SSU_BF16, 0, {K * H * P, P, 1, 0}};
+        SSU_OK_(ssu_update(h, &s1, NULL));
+    }
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(pool_s, d_pool, sizeof pool, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(out_s, d_out, sizeof out_s, hipMemcpyDeviceToHost));
+    ssu_destroy(h);
+    int bad = (memcmp(pool_f, pool_s, sizeof pool) != 0) + (memcmp(out_f, out_s, sizeof out_f) != 0);
+    hipFree(d_pool), hipFree(d_idx), hipFree(d_xbc), hipFree(d_dt), hipFree(d_A), hipFree(d_D), hipFree(d_bias);
+    hipFree(d_out);
+    printf("tokens: %s\n", bad ? "fused and successive calls differ" : "fused = successive, bitwise");
+    return bad != 0;
+}
+
+/* ssu_copy_blocks over two tensors of different block sizes: destinations
+ * receive their sources' bytes, every other block keeps its own. */
+static int check_copy(void)
+{
+    enum { NB = 6, BYTES0 = 4096, BYTES1 = 640, STRIDE1 = 768 };
+    static uint8_t t0[NB * BYTES0], t1[NB * STRIDE1], g0[NB * BYTES0], g1[NB * STRIDE1];
+    for (int i = 0; i < NB * BYTES0; ++i)
+        t0[i] = (uint8_t)next();
+    for (int i = 0; i < NB * STRIDE1; ++i)
+        t1[i] = (uint8_t)next();
+    const int32_t src[3] = {0, 4, 2}, dst[3] = {5, 1, 2}; /* the last: src == dst, a no-op */
+    void *d0 = to_device(t0, sizeof t0), *d1 = to_device(t1, sizeof t1);
+    void *d_src = to_device(src, sizeof src), *d_dst = to_device(dst, sizeof dst);
+    const ssu_block_tensor ts[2] = {{d0, BYTES0, BYTES0, NB}, {d1, STRIDE1, BYTES1, NB}};
+    SSU_OK_(ssu_copy_blocks(ts, 2, d_src, d_dst, 3, -1, NULL));
+    HIP_OK(hipDeviceSynchronize());
+    HIP_OK(hipMemcpy(g0, d0, sizeof g0, hipMemcpyDeviceToHost));
+    HIP_OK(hipMemcpy(g1, d1, sizeof g1, hipMemcpyDeviceToHost));
+    for (int r = 0; r < 3; ++r) {
+        memcpy(t0 + (size_t)dst[r] * BYTES0, t0 + (size_t)src[r] * BYTES0, BYTES0);
+        memcpy(t1 + (size_t)dst[r] * STRIDE1, t1 + (size_t)src[r] * STRIDE1, BYTES1);
+    }
+    const int bad = (memcmp(g0, t0, sizeof t0) != 0) + (memcmp(g1, t1, sizeof t1) != 0);
+    hipFree(d0), hipFree(d1), hipFree(d_src), hipFree(d_dst);
+    printf("copy: %s\n", bad ? "blocks differ" : "blocks as expected");
+    return bad != 0;
+}
+
 int main(void)
 {
     int dev = 0;
@@ -254,6 +354,8 @@ int main(void)
     }
     int fail = check_decode();
     fail |= check_scan();
+    fail |= check_tokens();
+    fail |= check_copy();
     if (fail)
         return 1;
     printf("ok\n");
