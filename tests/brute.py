@@ -91,16 +91,18 @@ def _io(bits: int, io: str) -> float:
     return _f16(bits) if io == "f16" else _bf16(bits)
 
 
-def scan(state, u, delta, A, B, C, D, delta_bias, softplus, io):
+def scan(state, u, delta, A, B, C, D, delta_bias, softplus, io, want_tau=False):
     """state [bs][dim][N] floats; u, delta [bs][dim][L] io bits; B, C
     [bs][G][N][L] io bits; A [dim][N]; D, delta_bias [dim] or None.
 
-    Returns (h_final [bs][dim][N], y [bs][dim][L]) in fp64.
+    Returns (h_final [bs][dim][N], y [bs][dim][L]) in fp64, and with
+    ``want_tau`` also tau [bs][dim][L] = sum_n |C_t[n] h_t[n]| + |D u_t|.
     """
     bs, dim, L = len(u), len(u[0]), len(u[0][0])
     G, N = len(B[0]), len(B[0][0])
     h_out = [[[0.0] * N for _ in range(dim)] for _ in range(bs)]
     y_out = [[[0.0] * L for _ in range(dim)] for _ in range(bs)]
+    tau_out = [[[0.0] * L for _ in range(dim)] for _ in range(bs)]
     for b in range(bs):
         for d in range(dim):
             g = d // (dim // G)
@@ -121,7 +123,9 @@ def scan(state, u, delta, A, B, C, D, delta_bias, softplus, io):
                 return math.fsum(terms)
 
             for t in range(L):
-                y_out[b][d][t] = math.fsum([_io(C[b][g][n][t], io) * h_at(t, n) for n in range(N)] + [dd * us[t]])
+                terms = [_io(C[b][g][n][t], io) * h_at(t, n) for n in range(N)] + [dd * us[t]]
+                y_out[b][d][t] = math.fsum(terms)
+                tau_out[b][d][t] = math.fsum(abs(v) for v in terms)
             for n in range(N):
                 h_out[b][d][n] = h_at(L - 1, n) if L > 0 else float(state[b][d][n])
-    return h_out, y_out
+    return (h_out, y_out, tau_out) if want_tau else (h_out, y_out)

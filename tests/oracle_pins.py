@@ -468,12 +468,14 @@ def pin_scan_brute_force(o):
                 p.delta_bias = np.full(p.dim, 0.01, dtype=np.float32)
             D, bias = (p.D, p.delta_bias) if with_opt else (None, None)
             state, r = _scan_run(o, p, D=D, delta_bias=bias)
-            h, y = brute.scan(p.state.tolist(), p.u.tolist(), p.delta.tolist(), p.A.tolist(), p.B.tolist(),
-                              p.C.tolist(), None if D is None else D.tolist(),
-                              None if bias is None else bias.tolist(), softplus, io)
-            h, y = np.array(h), np.array(y)
+            h, y, tau = brute.scan(p.state.tolist(), p.u.tolist(), p.delta.tolist(), p.A.tolist(), p.B.tolist(),
+                                   p.C.tolist(), None if D is None else D.tolist(),
+                                   None if bias is None else bias.tolist(), softplus, io, want_tau=True)
+            h, y, tau = np.array(h), np.array(y), np.array(tau)
             assert np.allclose(r["state"], h, rtol=1e-12, atol=1e-14), (io, softplus, with_opt)
-            assert np.all(np.abs(r["y"] - y) <= 1e-12 * (np.abs(r["tau"]) + 1e-300)), (io, softplus, with_opt)
+            assert np.all(np.abs(r["y"] - y) <= 1e-12 * (tau + 1e-300)), (io, softplus, with_opt)
+            # tau exactly (both ways): sum_n |C h| + |D u| of the brute force's terms
+            assert np.all(np.abs(r["tau"] - tau) <= 1e-12 * tau + 1e-300), (io, softplus, with_opt)
             assert np.array_equal(state, h.astype(np.float32))
             assert np.array_equal(r["out"], _io_round(r["y"], io))
 
@@ -625,6 +627,95 @@ def pin_scan_error_scale(o):
     assert np.all(np.abs(h - r["state"]) <= 4 * eps * r["err"])
 
 
+def pin_scan_error_scale_closed_forms(o):
+    """The error scales equal their definitions, in closed form, from above and
+    below. With beta_t = Delta_t u_t B_t and a_t = exp(A Delta_t) per state:
+    M_t = a_t M_{t-1} + |beta_t|, E_t = a_t E_{t-1} + (1 + |A Delta_t|) a_t
+    M_{t-1} + M_t, M_{-1} = E_{-1} = |h_{-1}|, rho_t = sum_n |C_t| E_t,
+    tau_t = sum_n |h_t C_t| + |D u_t|.
+
+    * Constant inputs (a, beta, C the same at every token): M_s = k + (m0 - k)
+      a^(s+1) with k = |beta| / (1 - a), m0 = |h_{-1}|, and summing the two
+      geometric series in E gives
+      E_t = a^(t+1) m0 + (1 + c a) k (1 - a^(t+1)) / (1 - a)
+            + (1 + c) (m0 - k) (t + 1) a^(t+1),   c = 1 + |A Delta|.
+      Signed B, C and h_{-1}, so every absolute value matters.
+    * A = 0 with every input positive: no decay, M_t = h_t = h_{-1} +
+      cumsum(beta), and E_t = m0 + sum_{s<=t} (M_{s-1} + M_s) (numpy.cumsum).
+    * A -> -1e30 (memoryless): E_t = M_t = |beta_t|, so rho_t = sum_n |C_t|
+      |beta_t| and tau_t = sum_n |beta_t C_t| + |D u_t|.
+    Agreement to 1e-12 relative: an error scale inflated (or deflated) by any
+    factor fails."""
+    rel = 1e-12
+
+    def close(got, want):
+        return np.all(np.abs(got - want) <= rel * np.abs(want) + 1e-300)
+
+    # constant inputs, geometric series
+    L, N, dim = 40, 4, 3
+    p = _scan_problem(batch=1, dim=dim, N=N, G=1, L=L, seed=32, zero_state=False)
+    io = p.io
+    uval, dval = np.float32(0.75), np.float32(-0.5)
+    p.u = np.full_like(p.u, si.io_bits([uval], io)[0])
+    p.delta = np.full_like(p.delta, si.io_bits([dval], io)[0])
+    Bv = np.array([1.0, -2.0, 0.5, 3.0], dtype=np.float32)
+    Cv = np.array([1.5, -2.0, 0.25, -3.0], dtype=np.float32)
+    p.B = np.broadcast_to(si.io_bits(Bv, io)[None, None, :, None], p.B.shape).copy()
+    p.C = np.broadcast_to(si.io_bits(Cv, io)[None, None, :, None], p.C.shape).copy()
+    _, r = _scan_run(o, p)
+    t = np.arange(L, dtype=np.float64)[None, :]                       # [1, L]
+    Cd = Cv.astype(np.float64)[:, None]                               # [N, 1]
+    for d in range(dim):
+        delta = np.logaddexp(0.0, float(dval) + float(p.delta_bias[d]))
+        A = p.A[d].astype(np.float64)[:, None]
+        a = np.exp(A * delta)
+        beta = delta * float(uval) * Bv.astype(np.float64)[:, None]
+        h0 = p.state[0, d].astype(np.float64)[:, None]
+        m0, k, c = np.abs(h0), np.abs(beta) / (1 - a), 1 + np.abs(A * delta)
+        pw = a ** (t + 1)
+        h = pw * h0 + beta * (1 - pw) / (1 - a)
+        E = pw * m0 + (1 + c * a) * k * (1 - pw) / (1 - a) + (1 + c) * (m0 - k) * (t + 1) * pw
+        Du = abs(float(p.D[d]) * float(uval))
+        assert close(r["err"][0, d], E[:, -1]), ("E", d)
+        assert close(r["rho"][0, d], (np.abs(Cd) * E).sum(axis=0)), ("rho", d)
+        assert close(r["tau"][0, d], np.abs(h * Cd).sum(axis=0) + Du), ("tau", d)
+
+    # A = 0, all inputs positive: cumulative sums
+    p = _scan_problem(batch=2, dim=4, N=3, G=2, L=25, seed=33, zero_state=False)
+    io = p.io
+    p.A = np.zeros_like(p.A)
+    p.state = np.abs(p.state)
+    p.u = si.io_bits(np.abs(si.io_values(p.u, io)) + 0.25, io)
+    p.B = si.io_bits(np.abs(si.io_values(p.B, io)) + 0.25, io)
+    _, r = _scan_run(o, p)
+    delta = np.logaddexp(0.0, si.io_values(p.delta, io).astype(np.float64) + p.delta_bias[None, :, None])
+    u = si.io_values(p.u, io).astype(np.float64)
+    g = np.arange(p.dim) // (p.dim // p.ngroups)
+    B = si.io_values(p.B, io).astype(np.float64)[:, g]                # [b, dim, N, L]
+    C = si.io_values(p.C, io).astype(np.float64)[:, g]
+    h0 = p.state.astype(np.float64)[..., None]                        # [b, dim, N, 1]
+    h = h0 + np.cumsum((delta * u)[:, :, None, :] * B, axis=-1)       # = M
+    hprev = np.concatenate([h0, h[..., :-1]], axis=-1)
+    E = h0 + np.cumsum(hprev + h, axis=-1)
+    assert close(r["err"], E[..., -1]), "E (A = 0)"
+    assert close(r["rho"], (np.abs(C) * E).sum(axis=2)), "rho (A = 0)"
+    assert close(r["tau"], np.abs(h * C).sum(axis=2) + np.abs(p.D[None, :, None] * u)), "tau (A = 0)"
+
+    # memoryless
+    p = _scan_problem(batch=2, dim=4, N=3, G=2, L=13, seed=34, zero_state=False)
+    io = p.io
+    p.A = np.full_like(p.A, -1e30)
+    _, r = _scan_run(o, p)
+    delta = np.logaddexp(0.0, si.io_values(p.delta, io).astype(np.float64) + p.delta_bias[None, :, None])
+    u = si.io_values(p.u, io).astype(np.float64)
+    B = si.io_values(p.B, io).astype(np.float64)[:, g]
+    C = si.io_values(p.C, io).astype(np.float64)[:, g]
+    beta = (delta * u)[:, :, None, :] * B
+    assert close(r["err"], np.abs(beta[..., -1])), "E (memoryless)"
+    assert close(r["rho"], (np.abs(C) * np.abs(beta)).sum(axis=2)), "rho (memoryless)"
+    assert close(r["tau"], np.abs(beta * C).sum(axis=2) + np.abs(p.D[None, :, None] * u)), "tau (memoryless)"
+
+
 def pin_scan_infinite_step(o):
     """A step of -inf with softplus on has size softplus(-inf) = 0: decay 1,
     input 0, so the scan is exactly the scan of the sequence with that token
@@ -653,4 +744,5 @@ def pin_scan_infinite_step(o):
 
 
 PINS.extend([pin_f16_decode, pin_f16_rounding, pin_scan_brute_force, pin_scan_closed_form, pin_scan_no_decay,
-             pin_scan_memoryless, pin_scan_zero_step, pin_scan_split, pin_scan_error_scale, pin_scan_infinite_step])
+             pin_scan_memoryless, pin_scan_zero_step, pin_scan_split, pin_scan_error_scale, pin_scan_error_scale_closed_forms,
+             pin_scan_infinite_step])

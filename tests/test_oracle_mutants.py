@@ -84,6 +84,21 @@ MUTANTS = [
     ("scan_B_lagged", "grp * g->B_g + t * g->B_t", "grp * g->B_g + (t > 0 ? t - 1 : 0) * g->B_t"),
     ("scan_out_always_bf16", "io ? ssu_ref_f16_rne(yf) : ssu_ref_bf16_rne(yf)", "ssu_ref_bf16_rne(yf)"),
     ("scan_error_scale_no_carry", "E[n] = a * E[n] +", "E[n] = 0.0 * E[n] +"),
+    # error scales inflated or mis-formed (each loosens or skews the scan's tolerance)
+    ("scan_E_times4", "E[n] = a * E[n] + (1.0 + fabs(An * Delta)) * a * Mprev + M[n];",
+     "E[n] = 4.0 * (a * E[n] + (1.0 + fabs(An * Delta)) * a * Mprev + M[n]);"),
+    ("scan_err_out_times4", "g->err_ref[si] = E[n];", "g->err_ref[si] = 4.0 * E[n];"),
+    ("scan_E_new_term_times4", "* a * Mprev + M[n];", "* a * Mprev + 4.0 * M[n];"),
+    ("scan_E_decay_term_times4", "(1.0 + fabs(An * Delta)) * a * Mprev", "4.0 * (1.0 + fabs(An * Delta)) * a * Mprev"),
+    ("scan_E_no_step_term", "(1.0 + fabs(An * Delta)) * a * Mprev", "(1.0) * a * Mprev"),
+    ("scan_E_initial_times4", "M[n] = E[n] = fabs(h[n]);", "M[n] = fabs(h[n]);\n                E[n] = 4.0 * M[n];"),
+    ("scan_M_signed_input", "M[n] = a * M[n] + fabs(beta);", "M[n] = a * M[n] + beta;"),
+    ("scan_M_no_decay", "M[n] = a * M[n] + fabs(beta);", "M[n] = M[n] + fabs(beta);"),
+    ("scan_rho_times16", "rho += fabs(c) * E[n];", "rho += 16.0 * fabs(c) * E[n];"),
+    ("scan_rho_signed_C", "rho += fabs(c) * E[n];", "rho += c * E[n];"),
+    ("scan_tau_times16", "tau += fabs(h[n] * c);", "tau += 16.0 * fabs(h[n] * c);"),
+    ("scan_tau_signed", "tau += fabs(h[n] * c);", "tau += h[n] * c;"),
+    ("scan_tau_no_D", "tau += fabs(Dv * ut);", "tau += 0.0 * Dv * ut;"),
     ("f16_exponent_bias", "e - 25", "e - 24"),
     ("f16_subnormal_zero", "v = ldexp((double)m, -24);", "v = 0.0 * m;"),
     ("f16_implicit_bit", "(m | 0x400)", "(m)"),
