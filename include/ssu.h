@@ -115,6 +115,13 @@ typedef struct ssu_view {
  * pool may overlap any input (the kernel reads inputs through the read-only
  * scalar cache), out must not overlap the state, and the state rows of
  * distinct requests must not overlap.
+ *
+ * dt is read as the aligned 32-bit words that hold its elements (the scalar
+ * cache reads whole words), so reading the first or the last element of the
+ * view may also read the 2 bytes beside it, just outside the view. An aligned
+ * word never crosses a page, so such a read cannot fault wherever the element
+ * itself is mapped, and the 2 extra bytes are never used; the caller need not
+ * pad dt. A tool that tracks bytes (a sanitizer) may still report the read.
  */
 typedef struct ssu_args {
     int32_t batch;      /* >= 0; 0 is a no-op */

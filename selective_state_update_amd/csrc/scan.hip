@@ -365,13 +365,14 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_kernel(const ScanParam
     c.softplus = p.softplus != 0;
     float *st = p.state + b * p.st_b + d * p.st_d + n0;
 
-    // wave-uniform per-channel values
+    // wave-uniform per-channel values; the state is written by this kernel,
+    // so it is read with a plain load, never through the read-only path
     c.bias = p.bias ? load_ro(p.bias + d) : 0.0f;
     c.Dd = p.D ? load_ro(p.D + d) : 0.0f;
 #pragma unroll
     for (int n = 0; n < NSW; ++n) {
         const int r = FULL ? n : min(n, c.ns - 1);
-        const float hv = load_ro(st + r), av = load_ro(p.A + d * p.A_d + (n0 + r) * p.A_n);
+        const float hv = st[r], av = load_ro(p.A + d * p.A_d + (n0 + r) * p.A_n);
         c.h0[n] = (FULL || n < c.ns) ? hv : 0.0f;
         c.A2[n] = (FULL || n < c.ns) ? av * kLog2e : 0.0f;
     }

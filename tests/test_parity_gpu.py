@@ -124,6 +124,44 @@ def test_padding_and_int64_indices(ref):
     assert np.array_equal(dp2.pool.cpu().numpy().view(np.uint32), pool_gpu.view(np.uint32))
 
 
+@pytest.mark.parametrize("offset", [0, 1], ids=["first_low_half", "first_high_half"])
+def test_dt_at_the_edges_of_its_allocation(ref, offset):
+    """dt is read as the aligned words that hold its elements. A dt view that
+    fills its own allocation exactly, with an odd element count (batch 5 x 3
+    heads), has its last element in the low half of a word when it starts on a
+    word (offset 0) and its first element in the high half of a word when it
+    starts 2 bytes in (offset 1): the results match the oracle either way, for
+    the one-token and the K-token call."""
+    torch = gu.torch_mod()
+    p = si.make_problem(H=3, P=64, N=128, batch=5, pool_slots=11, seed=810)
+    dp = gu.DeviceProblem(p)
+    storage = torch.empty(p.batch * p.nheads + offset, dtype=torch.bfloat16, device="cuda")
+    storage[offset:] = gu.bf16_tensor(p.dt.ravel(), "cuda")
+    dt = storage[offset:].view(p.batch, p.nheads)
+    assert dt.data_ptr() % 4 == 2 * offset
+    h = dp.handle()
+    out = torch.empty_like(dp.out)
+    h.update(dp.pool, dp.idx, dp.x, dp.B, dp.C, dt, dp.A, dp.D, dp.dt_bias, out)
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), out, f"dt offset {offset}")
+    # a 3-token call whose dt [batch, 3, H] fills its allocation the same way
+    # equals three one-token calls bitwise
+    K = 3
+    dts = np.random.Generator(np.random.PCG64(811)).standard_normal((p.batch, K, p.nheads)).astype(np.float32)
+    storage = torch.empty(p.batch * K * p.nheads + offset, dtype=torch.bfloat16, device="cuda")
+    storage[offset:] = torch.from_numpy(dts.ravel()).to(torch.bfloat16).cuda()
+    dtk = storage[offset:].view(p.batch, K, p.nheads)
+    xk, Bk, Ck = (v[:, None].expand(v.shape[0], K, *v.shape[1:]) for v in (dp.x, dp.B, dp.C))
+    pool_k = torch.from_numpy(p.pool).cuda()
+    out_k = h.update_tokens(pool_k, dp.idx, xk, Bk, Ck, dtk, dp.A, dp.D, dp.dt_bias)
+    pool_s = torch.from_numpy(p.pool).cuda()
+    for t in range(K):
+        o = h.update(pool_s, dp.idx, dp.x, dp.B, dp.C, dtk[:, t], dp.A, dp.D, dp.dt_bias)
+        torch.cuda.synchronize()
+        assert torch.equal(out_k[:, t].view(torch.int16), o.view(torch.int16)), (offset, t)
+    assert torch.equal(pool_k.view(torch.int32), pool_s.view(torch.int32)), offset
+
+
 def test_request_permutation_bitwise(ref):
     """Requests are independent: permuting (idx, x, B, C, dt) together over
     the batch permutes out the same way, bitwise, and leaves the same pool,

@@ -69,6 +69,9 @@ def oracle_scan(ref, p, D=True, bias=True):
 
 
 def check(p, out, state, r, what=""):
+    rs, ro = tol.scan_error_ratios(out, state, r["y"], r["tau"], r["rho"], r["state"], r["err"], p.dstate, p.io)
+    print(f"  {what}: worst state error {rs:.3f} eps*E (bound {tol.SCAN_STATE_C:g}), "
+          f"worst out excess {ro:.4f} eps*(rho+N*tau) (bound {tol.SCAN_OUT_C:g})", flush=True)
     bad_o = tol.scan_out_violations(out, r["y"], r["tau"], r["rho"], p.dstate, p.io)
     bad_s = tol.scan_state_violations(state, r["state"], r["err"])
     if bad_o.any():

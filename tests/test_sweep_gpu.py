@@ -4,7 +4,9 @@ measurement", and the "Correctness Verification" table) checked that launch
 configurations give bitwise-identical output and state.
 
 At every point, in the launch configuration the library picks:
-  * sampled requests (all heads) against the CPU oracle, state and out;
+  * every request against the CPU oracle, state and out, at the points that
+    move at most 64 MiB of state per call (batch x heads <= 2048: 272 of the
+    920 points); three sampled requests (all heads) at the larger points;
   * untouched pool slots bitwise unchanged;
   * a rerun from the restored pool bitwise identical (determinism);
   * a run in a different launch configuration bitwise identical.
@@ -19,6 +21,8 @@ from . import gpu_util as gu
 pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BATCHES = sorted({bs for (_, bs) in si.sweep_points()})
+# (request, head) units up to which every request is compared with the oracle
+FULL_CHECK_UNITS = 2048
 
 
 @pytest.fixture(autouse=True)
@@ -43,7 +47,7 @@ def test_sweep_heads(ref, H):
     torch = gu.torch_mod()
     h_auto = ssu.Handle(H, 64, 128, 1, True, -1)
     h_alt = None
-    checked = 0
+    checked = full = 0
     for bs in BATCHES:
         seed = si.sweep_seed(H, bs)
         slots = 2 * bs
@@ -56,9 +60,13 @@ def test_sweep_heads(ref, H):
         out = dp.run(h_auto)
         torch.cuda.synchronize()
 
-        # sampled requests against the oracle
-        rng = np.random.Generator(np.random.PCG64(seed))
-        sample = np.sort(rng.choice(bs, size=min(bs, 3), replace=False))
+        # every request (or three sampled ones at the larger points) against the oracle
+        if bs * H <= FULL_CHECK_UNITS:
+            sample = np.arange(bs)
+            full += 1
+        else:
+            rng = np.random.Generator(np.random.PCG64(seed))
+            sample = np.sort(rng.choice(bs, size=min(bs, 3), replace=False))
         sl = idx_t[torch.from_numpy(sample).cuda()]
         before = backup[sl].cpu().numpy()
         after = pool[sl].cpu().numpy()
@@ -86,4 +94,7 @@ def test_sweep_heads(ref, H):
         checked += 1
         del pool, backup, dp, first_state
     torch.cuda.empty_cache()
+    print(f"H{H}: {checked} points, every request against the oracle at {full} "
+          f"(batch x heads <= {FULL_CHECK_UNITS}), three sampled requests at {checked - full}", flush=True)
     assert checked == len(BATCHES) == 184
+    assert full == sum(1 for bs in BATCHES if bs * H <= FULL_CHECK_UNITS)

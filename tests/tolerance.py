@@ -108,3 +108,18 @@ def scan_out_violations(out_bits, y_ref, tau_ref, rho_ref, dstate, io) -> np.nda
     y = np.asarray(y_ref, dtype=np.float64)
     tol = io_ulp(y, io) + SCAN_OUT_C * EPS32 * (np.asarray(rho_ref) + dstate * np.asarray(tau_ref))
     return ~(np.abs(g - y) <= tol)
+
+
+def scan_error_ratios(out_bits, state, y_ref, tau_ref, rho_ref, state_ref, err_ref, dstate, io):
+    """Worst observed errors in units of the scan's error scales:
+    (max |S - h| / (eps E), max over outputs of (|out - y| - ulp_io(y))^+ /
+    (eps (rho + N tau))). The acceptance constants are SCAN_STATE_C and
+    SCAN_OUT_C in these units."""
+    s = np.abs(np.asarray(state, dtype=np.float64) - np.asarray(state_ref)) / (EPS32 * np.asarray(err_ref) + 1e-300)
+    g = io_to_f64(out_bits, io)
+    y = np.asarray(y_ref, dtype=np.float64)
+    ex = np.maximum(np.abs(g - y) - io_ulp(y, io), 0.0)
+    o = ex / (EPS32 * (np.asarray(rho_ref) + dstate * np.asarray(tau_ref)) + 1e-300)
+    fin_s, fin_o = np.isfinite(s), np.isfinite(o)
+    return (float(s[fin_s].max()) if fin_s.any() else 0.0, float(o[fin_o].max()) if fin_o.any() else 0.0)
+
