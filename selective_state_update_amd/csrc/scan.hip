@@ -12,11 +12,29 @@
 //   y[t]  = sum_n h[n] * C[b,g,n,t] + D[d] * u[b,d,t]
 // with g = d / (dim / G), h read from and written back to the fp32 state.
 //
-// Work split. One wave per (request, channel). Tokens go in blocks of
-// 64 * SEG: lane l owns tokens l*SEG .. l*SEG+SEG-1 of a block, so a block's
-// activations are one coalesced vector load per lane. Per state n the
-// recurrence h -> a h + b is a composition of affine maps, and composition is
-// associative:
+// Two kernels compute it, with the same fp32 operations in the same order,
+// so every configuration of either gives the same bits:
+//
+//   direct (scan_t{SEG}_n{NSW}): one workgroup per (request, channel), one
+//     wave per NSW of its states; each wave loads its states' B and C rows
+//     straight into registers, all of a block's loads issued before any is
+//     used. Few instructions stand between a launch and its first result,
+//     which is what a small batch (a few thousand channels: latency bound)
+//     needs.
+//   staged (scan_t{SEG}_n{NSW}_w{W}_c{CPW}): a workgroup holds CPW channels of
+//     one (request, group), with W waves of NSW states each. The channels of
+//     a group share B and C, so the workgroup stages a block's B and C rows
+//     in LDS once, W * NSW states at a time (a round; d_state above that
+//     takes several rounds), and each wave reads the rows of the state it is
+//     working on just before it needs them, with the carried states and
+//     decay rates kept in LDS. Few registers are live, so four waves fit on
+//     each SIMD, and the B/C traffic falls by CPW: what a large batch
+//     (throughput bound) needs.
+//
+// Both split tokens into blocks of 64 * SEG: lane l owns tokens l*SEG ..
+// l*SEG+SEG-1 of a block, so a block's activations are one coalesced vector
+// load per lane. Per state n the recurrence h -> a h + b is a composition of
+// affine maps, and composition is associative:
 //   1. each lane composes its SEG pairs (a_j, b_j) into one map (P, Q);
 //   2. a 64-lane inclusive scan of the maps in a fixed tree (DPP row shifts
 //      1, 2, 4, 8, then row broadcasts 15 and 31) gives every lane the map
@@ -27,31 +45,29 @@
 //      applied to g, h_j = P_j g + Q_j (P_j, Q_j kept from step 1), computed
 //      for every j independently, and y_j += h_j C_j;
 //   4. lane 63's end state is the carried state for the next block.
-// The carried state is wave-uniform (one register per state), so blocks, and
-// launches that start on a block boundary, continue from exactly the value the
-// previous block ended with: chunkings whose chunks are multiples of 64 * SEG
-// give bitwise identical results.
-//
-// States per wave: NSW = 16 or 8 (a launch configuration). A channel's
-// workgroup has W = ceil(dstate / NSW) waves, NSW states each. More waves per
-// channel hide more latency at the price of computing the step sizes in every
-// wave; a one-wave instantiation has the whole register file to itself.
+// The carried state is wave-uniform, so blocks, and launches that start on a
+// block boundary, continue from exactly the value the previous block ended
+// with: chunkings whose chunks are multiples of 64 * SEG give bitwise
+// identical results.
 //
 // y is summed in one fixed order whatever the configuration: states in groups
 // of 8, each group's partial accumulated in state order (fma), the groups
-// added in group order (waves other than the first hand their groups' partials
-// over through LDS). With the same token segment, every configuration and
-// every chunking on block boundaries gives bitwise the same outputs.
+// added in group order (the channel's first wave adds the partials of the
+// other waves, handed over through LDS, after its own). With the same token
+// segment, every configuration and every chunking on block boundaries gives
+// bitwise the same outputs.
 //
-// Invalid tokens (past the end of a ragged last block) get Delta = 0 and u = 0:
-// their decay is exp2(0) = 1 and their input 0, the identity map, so they
-// leave every scan value unchanged.
+// Invalid tokens (past the end of a ragged last block) get Delta = 0, u = 0
+// and B = C = 0: their decay is exp2(0) = 1 and their input 0, the identity
+// map, so they leave every scan value unchanged. States past d_state get
+// A = 0, h = 0 and B = C = 0: the identity map and a zero contribution.
 
 #include <hip/hip_runtime.h>
 
 #include <algorithm>
 #include <cstdint>
 #include <cstdio>
+#include <type_traits>
 
 #include "internal.h"
 
@@ -70,7 +86,7 @@ struct ScanParams {
     const float *A, *D, *bias;
     int64_t u_b, u_d, dl_b, dl_d, B_b, B_g, B_n, C_b, C_g, C_n, o_b, o_d, st_b, st_d, A_d, A_n;
     int64_t t0, t1;
-    int32_t dim, dstate, ch_per_group, softplus, vec;
+    int32_t dim, dstate, ch_per_group, softplus, vec, rounds;
 };
 
 template <bool F16>
@@ -179,6 +195,15 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(SEG + 1) / 2], 
         "v_mul_f32_dpp %2, %2, %2 " DPPCTL "\n\t"                   \
         "v_mul_f32_dpp %3, %3, %3 " DPPCTL                           \
         : "+v"(Q0), "+v"(Q1), "+v"(P0), "+v"(P1))
+
+// The same step for one state: the s_nop gives the DPP read of Q the wait
+// states it needs after the previous step's write of Q (one instruction
+// between them).
+#define SSU_SCAN_STEP1(DPPCTL, Q0, P0)                              \
+    asm("s_nop 1\n\t"                                               \
+        "v_fmac_f32_dpp %0, %0, %1 " DPPCTL "\n\t"                  \
+        "v_mul_f32_dpp %1, %1, %1 " DPPCTL                           \
+        : "+v"(Q0), "+v"(P0))
 
 // DPP control of the one-lane shift of the whole wave (GFX9 encoding).
 constexpr int kWaveShr1 = 0x138;
@@ -336,7 +361,7 @@ struct Chan {
 };
 
 template <bool F16, int SEG, int NSW, int MAXW, bool FULL>
-__global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_kernel(const ScanParams p)
+__global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const ScanParams p)
 {
     using Ch = Chan<F16, SEG, NSW, FULL>;
     constexpr int BLOCK = Ch::BLOCK;
@@ -434,65 +459,416 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_kernel(const ScanParam
         st[lane] = mine;
 }
 
-using ScanFn = hipError_t (*)(const ScanParams &, int grid, int threads, hipStream_t);
 
-template <bool F16, int SEG, int NSW, int MAXW, bool FULL>
-hipError_t launch_scan(const ScanParams &p, int grid, int threads, hipStream_t stream)
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
+
+// SEG tokens of a row staged in LDS (16-bit values, packed two per word).
+template <int SEG>
+__device__ __forceinline__ void lds_seg(const uint16_t *p, uint32_t (&w)[(SEG + 1) / 2])
 {
-    hipLaunchKernelGGL((ssu_scan_kernel<F16, SEG, NSW, MAXW, FULL>), dim3(grid), dim3(threads), 0, stream, p);
+    if constexpr (SEG == 8) {
+        const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
+        w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
+    } else if constexpr (SEG == 4) {
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+        w[0] = x.x, w[1] = x.y;
+    } else if constexpr (SEG == 2) {
+        w[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        w[0] = *p;
+    }
+}
+
+// Layout of one workgroup's LDS (dynamic, 16-byte aligned):
+//   sBC [2 * RS][BLOCK] u16      the round's B rows, then its C rows;
+//   sY  [W - 1][GROUPS][CPW][BLOCK] f32  partials of y that waves 1 .. W-1
+//                                        of each channel hand to wave 0;
+//   sH  [CPW][rounds * RS] f32   the carried states (0 past d_state);
+//   sA  [CPW][rounds * RS] f32   A * log2(e) (0 past d_state).
+template <int SEG, int NSW, int W, int CPW>
+struct ScanShape {
+    static constexpr int BLOCK = kLanes * SEG;
+    static constexpr int WORDS = (SEG + 1) / 2;
+    static constexpr int RS = W * NSW;            // states per round
+    static constexpr int GROUPS = NSW / kGroup;
+    static constexpr int NT = kLanes * W * CPW;   // threads
+    static constexpr int CPR = BLOCK / 8;         // 16-byte pieces per staged row
+    static constexpr int PIECES = 2 * RS * CPR;   // per round
+    static constexpr int ITERS = (PIECES + NT - 1) / NT;
+    static constexpr size_t BC_BYTES = size_t(2) * RS * BLOCK * 2;
+    static constexpr size_t Y_BYTES = size_t(W - 1) * GROUPS * CPW * BLOCK * 4;
+    static size_t lds_bytes(int rounds) { return BC_BYTES + Y_BYTES + size_t(2) * CPW * rounds * RS * 4; }
+};
+
+template <bool F16, int SEG, int NSW, int W, int CPW, bool FULL>
+__global__ void __launch_bounds__(kLanes * W * CPW) __attribute__((amdgpu_waves_per_eu(4)))
+ssu_scan_staged_kernel(const ScanParams p)
+{
+    using S = ScanShape<SEG, NSW, W, CPW>;
+    constexpr int BLOCK = S::BLOCK, WORDS = S::WORDS, RS = S::RS, GROUPS = S::GROUPS, NT = S::NT;
+    constexpr bool kAllPieces = S::PIECES % NT == 0;  // every thread stages ITERS pieces
+    constexpr bool kSplitRows = kAllPieces && S::ITERS % 2 == 0 && NT % S::CPR == 0;
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *const sBC = reinterpret_cast<uint16_t *>(smem);
+    float *const sY = reinterpret_cast<float *>(smem + S::BC_BYTES);
+    float *const sH = reinterpret_cast<float *>(smem + S::BC_BYTES + S::Y_BYTES);
+    const int rounds = p.rounds;
+    const int HP = rounds * RS;
+    float *const sA = sH + CPW * HP;
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & (kLanes - 1);
+    const int wv = tid / kLanes;
+    const int c = wv / W;        // channel slot
+    const int w = wv - c * W;    // state slice
+    const int64_t bd0 = static_cast<int64_t>(blockIdx.x) * CPW;
+    const int64_t b = bd0 / p.dim;                 // every channel of the group shares it
+    const int d0 = static_cast<int>(bd0 - b * p.dim);
+    const int d = d0 + c;
+    const int grp = d0 / p.ch_per_group;
+    const int dstate = p.dstate;
+
+    const uint16_t *const Bbase = p.B + b * p.B_b + grp * p.B_g;
+    const uint16_t *const Cbase = p.C + b * p.C_b + grp * p.C_g;
+    const uint16_t *const u_row = p.u + b * p.u_b + d * p.u_d;
+    const uint16_t *const dl_row = p.delta + b * p.dl_b + d * p.dl_d;
+    const float bias = p.bias ? load_ro(p.bias + d) : 0.0f;
+    const float Dd = p.D ? load_ro(p.D + d) : 0.0f;
+    const bool softplus = p.softplus != 0;
+
+    // carried states into LDS (the state is written by this kernel, so it is
+    // read with plain loads, never through the read-only path)
+    // and the decay rates A * log2(e)
+    for (int i = tid; i < CPW * HP; i += NT) {
+        const int cc = i / HP, n = i - cc * HP;
+        const int nn = FULL ? n : min(n, dstate - 1);
+        const float *st = p.state + b * p.st_b + (d0 + cc) * p.st_d;
+        const float av = load_ro(p.A + (d0 + cc) * p.A_d + nn * p.A_n);
+        sH[i] = (FULL || n < dstate) ? st[nn] : 0.0f;
+        sA[i] = (FULL || n < dstate) ? av * kLog2e : 0.0f;
+    }
+
+    // One block of tokens. FAST: the block lies inside the chunk and every
+    // row is aligned for vector access, so every load is an unconditional
+    // vector load; otherwise each token is read from an address clamped into
+    // the chunk and tokens past its end read as 0.
+    auto block = [&](int64_t blk, auto fast_tag) {
+        constexpr bool fast = decltype(fast_tag)::value;
+        const int64_t tok = blk + lane * SEG;
+
+        // this lane's step sizes and inputs (requested before the staging waits)
+        uint32_t uw[WORDS], dw[WORDS];
+        load_seg<SEG, fast>(u_row, tok, p.t1, uw);
+        load_seg<SEG, fast>(dl_row, tok, p.t1, dw);
+        float dl[SEG], du[SEG], y[SEG];
+
+        // step sizes Delta_j and inputs Delta_j u_j of this lane's tokens
+        // (invalid tokens: the identity)
+        auto steps = [&]() {
+#pragma unroll
+            for (int j = 0; j < SEG; ++j) {
+                const float v = io_to_f32<F16>(half_of<SEG>(dw, j)) + bias;
+                float sv = softplus ? softplus_f32(v) : v;
+                sv = (fast || tok + j < p.t1) ? sv : 0.0f;
+                dl[j] = sv;
+                du[j] = sv * io_to_f32<F16>(half_of<SEG>(uw, j));
+            }
+        };
+
+        for (int r = 0; r < rounds; ++r) {
+            // stage the round's B and C rows into LDS (and, in the first
+            // round, compute the step sizes while the pieces are in flight).
+            // Fast blocks request all their 16-byte pieces (at most 8 per
+            // thread at a time) before writing any; ragged or unaligned
+            // blocks build each piece from clamped 16-bit reads, one at a time.
+            {
+                auto piece_src = [&](int q, bool &live) -> const uint16_t * {
+                    const int row = q / S::CPR, k = q - row * S::CPR;
+                    const bool isC = row >= RS;
+                    const int n = r * RS + (isC ? row - RS : row);
+                    const int nn = FULL ? n : min(n, dstate - 1);
+                    live = FULL || n < dstate;
+                    return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * k;
+                };
+                // When the pieces divide evenly (every thread stages the same
+                // number, half of them in B rows), a thread's piece `it` lies
+                // in row row0 + it * RSTEP of B (first half of the iterations)
+                // or of C (second half), at column piece `col`: its address is
+                // the thread's base plus a uniform step.
+                auto split_src = [&](int it, bool &live) -> const uint16_t * {
+                    constexpr int RSTEP = NT / S::CPR;
+                    const int row0 = tid / S::CPR, col = tid - row0 * S::CPR;
+                    const bool isC = it >= S::ITERS / 2;
+                    const int n = r * RS + row0 + (isC ? it - S::ITERS / 2 : it) * RSTEP;
+                    const int nn = FULL ? n : min(n, dstate - 1);
+                    live = FULL || n < dstate;
+                    return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * col;
+                };
+                bool stepped = false;
+                if constexpr (fast) {
+                    constexpr int BATCH = S::ITERS < 8 ? S::ITERS : 8;
+#pragma unroll
+                    for (int i0 = 0; i0 < S::ITERS; i0 += BATCH) {
+                        u32x4 v[BATCH];
+#pragma unroll
+                        for (int i = 0; i < BATCH; ++i) {
+                            const int q = tid + (i0 + i) * NT;
+                            v[i] = u32x4{0u, 0u, 0u, 0u};
+                            if (kAllPieces || q < S::PIECES) {
+                                bool live;
+                                const uint16_t *src = kSplitRows ? split_src(i0 + i, live) : piece_src(q, live);
+                                const u32x4 x = *reinterpret_cast<const u32x4 *>(src);
+                                v[i] = live ? x : u32x4{0u, 0u, 0u, 0u};
+                            }
+                        }
+                        if (r == 0 && i0 == 0) {
+                            steps();
+                            stepped = true;
+                        }
+#pragma unroll
+                        for (int i = 0; i < BATCH; ++i) {
+                            const int q = tid + (i0 + i) * NT;
+                            if (kAllPieces || q < S::PIECES)
+                                *reinterpret_cast<u32x4 *>(sBC + 8 * q) = v[i];
+                        }
+                    }
+                } else {
+#pragma unroll 1
+                    for (int q = tid; q < S::PIECES; q += NT) {
+                        bool live;
+                        const uint16_t *src = piece_src(q, live);
+                        const int64_t t8 = blk + 8 * (q % S::CPR);
+                        uint32_t e[8];
+#pragma unroll
+                        for (int j = 0; j < 8; ++j) {
+                            const int64_t t = t8 + j;
+                            const uint32_t h = src[(t < p.t1 ? t : p.t1 - 1) - t8];
+                            e[j] = (live && t < p.t1) ? h : 0u;
+                        }
+                        *reinterpret_cast<u32x4 *>(sBC + 8 * q) =
+                            u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+                    }
+                }
+                if (r == 0 && !stepped)
+                    steps();
+            }
+            __syncthreads();
+
+            // this wave's states of the round, in groups of 8 and pairs: the
+            // carried values and decay rates come from LDS, the B and C rows
+            // of the pair from the staged block, just before they are used
+            const int sbase = r * RS + w * NSW;
+            const uint16_t *const sB = sBC + (w * NSW) * BLOCK + lane * SEG;
+            const uint16_t *const sC = sBC + (RS + w * NSW) * BLOCK + lane * SEG;
+            float *const hrow = sH + c * HP + sbase;
+            const float *const arow = sA + c * HP + sbase;
+#pragma unroll
+            for (int gi = 0; gi < GROUPS; ++gi) {
+                float yy[SEG];
+#pragma unroll
+                for (int j = 0; j < SEG; ++j)
+                    yy[j] = 0.0f;
+#pragma unroll 1
+                for (int n = gi * kGroup; n < (gi + 1) * kGroup; ++n) {
+                    const float hv = hrow[n];
+                    const float av = arow[n];
+                    uint32_t B0[WORDS], C0[WORDS];
+                    lds_seg<SEG>(sB + n * BLOCK, B0);
+                    lds_seg<SEG>(sC + n * BLOCK, C0);
+                    float a0[SEG], b0[SEG];
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j) {
+                        a0[j] = __builtin_amdgcn_exp2f(dl[j] * av);
+                        b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B0, j)), 0.0f);
+                    }
+                    float P0[SEG], Q0[SEG];
+                    P0[0] = a0[0], Q0[0] = b0[0];
+#pragma unroll
+                    for (int j = 1; j < SEG; ++j) {
+                        Q0[j] = fmaf(a0[j], Q0[j - 1], b0[j]);
+                        P0[j] = P0[j - 1] * a0[j];
+                    }
+                    float SP0 = P0[SEG - 1], SQ0 = Q0[SEG - 1];
+                    SSU_SCAN_STEP1("row_shr:1 row_mask:0xf bank_mask:0xf", SQ0, SP0);
+                    SSU_SCAN_STEP1("row_shr:2 row_mask:0xf bank_mask:0xf", SQ0, SP0);
+                    SSU_SCAN_STEP1("row_shr:4 row_mask:0xf bank_mask:0xf", SQ0, SP0);
+                    SSU_SCAN_STEP1("row_shr:8 row_mask:0xf bank_mask:0xf", SQ0, SP0);
+                    SSU_SCAN_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf", SQ0, SP0);
+                    SSU_SCAN_STEP1("row_bcast:31 row_mask:0xc bank_mask:0xf", SQ0, SP0);
+                    const float e0 = fmaf(SP0, hv, SQ0);
+                    const float g0 = __int_as_float(__builtin_amdgcn_update_dpp(
+                        __float_as_int(hv), __float_as_int(e0), kWaveShr1, 0xf, 0xf, false));
+                    const float n0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
+                    if (lane == 0)
+                        hrow[n] = n0;
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j)
+                        yy[j] = fmaf(fmaf(P0[j], g0, Q0[j]), io_to_f32<F16>(half_of<SEG>(C0, j)), yy[j]);
+                }
+                // the group's partial: added by wave 0 in group order, handed
+                // over through LDS by the channel's other waves
+                if (w == 0) {
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j)
+                        y[j] = (r == 0 && gi == 0) ? yy[j] : y[j] + yy[j];
+                } else if constexpr (W > 1) {
+#pragma unroll
+                    for (int j = 0; j < SEG; ++j)
+                        sY[(((w - 1) * GROUPS + gi) * CPW + c) * BLOCK + lane * SEG + j] = yy[j];
+                }
+            }
+
+            // every wave is done with this round's rows (and has handed over
+            // its partials) before they are overwritten
+            if constexpr (NT > kLanes)
+                __syncthreads();
+            if constexpr (W > 1) {
+                if (w == 0) {
+                    for (int k = 0; k < (W - 1) * GROUPS; ++k)
+#pragma unroll
+                        for (int j = 0; j < SEG; ++j)
+                            y[j] += sY[(k * CPW + c) * BLOCK + lane * SEG + j];
+                }
+            }
+        }
+
+        if (w == 0) {
+            uint16_t o[SEG];
+#pragma unroll
+            for (int j = 0; j < SEG; ++j)
+                o[j] = f32_to_io<F16>(fmaf(Dd, io_to_f32<F16>(half_of<SEG>(uw, j)), y[j]));
+            store_seg<SEG, fast>(p.out + b * p.o_b + d * p.o_d, tok, p.t1, o);
+        }
+    };
+    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+        if (p.vec && blk + BLOCK <= p.t1)
+            block(blk, std::true_type{});
+        else
+            block(blk, std::false_type{});
+    }
+
+    // final states: every wave wrote its own to LDS
+    __syncthreads();
+    for (int i = tid; i < CPW * dstate; i += NT) {
+        const int cc = i / dstate, n = i - cc * dstate;
+        p.state[b * p.st_b + (d0 + cc) * p.st_d + n] = sH[cc * HP + n];
+    }
+}
+
+// Launchers: every configuration takes the channel count and sets its own
+// grid, workgroup size and LDS.
+using ScanFn = hipError_t (*)(const ScanParams &, int64_t channels, hipStream_t);
+
+template <bool F16, int SEG, int NSW, bool FULL>
+hipError_t launch_direct(const ScanParams &p, int64_t channels, hipStream_t stream)
+{
+    const int waves = (p.dstate + NSW - 1) / NSW;
+    if constexpr (NSW == 16) {
+        if (waves == 1) {  // the one-wave instantiation has the whole register file
+            hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, SEG, NSW, 1, FULL>), dim3(channels), dim3(kLanes), 0,
+                               stream, p);
+            return hipGetLastError();
+        }
+    }
+    hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, SEG, NSW, kMaxStates / NSW, FULL>), dim3(channels),
+                       dim3(waves * kLanes), 0, stream, p);
     return hipGetLastError();
 }
 
-// A launch configuration: SEG tokens per lane, NSW states per wave. fn[single
-// wave][dstate % NSW == 0][f16]; the single-wave entry is null where the
-// multi-wave instantiation serves every wave count.
-struct ScanTile {
-    int seg, nsw;
-    ScanFn fn[2][2][2];
-    char name[24];
-};
-
-template <int SEG, int NSW, int MAXW, bool FULL>
-void set_scan_fns(ScanTile &t)
+template <bool F16, int SEG, int NSW, int W, int CPW, bool FULL>
+hipError_t launch_staged(const ScanParams &p, int64_t channels, hipStream_t stream)
 {
-    t.fn[MAXW == 1][FULL][0] = &launch_scan<false, SEG, NSW, MAXW, FULL>;
-    t.fn[MAXW == 1][FULL][1] = &launch_scan<true, SEG, NSW, MAXW, FULL>;
+    using S = ScanShape<SEG, NSW, W, CPW>;
+    hipLaunchKernelGGL((ssu_scan_staged_kernel<F16, SEG, NSW, W, CPW, FULL>), dim3(channels / CPW), dim3(S::NT),
+                       S::lds_bytes(p.rounds), stream, p);
+    return hipGetLastError();
 }
 
+// A launch configuration: SEG tokens per lane, NSW states per wave; staged
+// ones also W waves per channel and CPW channels per workgroup. rs: states
+// per round (per wave for direct ones); ealign: the element alignment (of
+// every row start and chunk start) its vector loads need. fn[all rounds
+// full][f16].
+struct ScanTile {
+    int seg, nsw, waves, cpw, rs, ealign;
+    bool staged;
+    ScanFn fn[2][2];
+    char name[32];
+};
+
 template <int SEG, int NSW>
-ScanTile make_scan_tile()
+ScanTile direct_tile()
 {
     ScanTile t{};
-    t.seg = SEG;
-    t.nsw = NSW;
-    set_scan_fns<SEG, NSW, kMaxStates / NSW, false>(t);
-    set_scan_fns<SEG, NSW, kMaxStates / NSW, true>(t);
-    if constexpr (NSW == 16) {
-        set_scan_fns<SEG, NSW, 1, false>(t);
-        set_scan_fns<SEG, NSW, 1, true>(t);
-    }
+    t.seg = SEG, t.nsw = NSW, t.waves = 0, t.cpw = 1, t.rs = NSW, t.ealign = SEG, t.staged = false;
+    t.fn[0][0] = &launch_direct<false, SEG, NSW, false>;
+    t.fn[0][1] = &launch_direct<true, SEG, NSW, false>;
+    t.fn[1][0] = &launch_direct<false, SEG, NSW, true>;
+    t.fn[1][1] = &launch_direct<true, SEG, NSW, true>;
     std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d", SEG, NSW);
     return t;
 }
 
+template <int SEG, int NSW, int W, int CPW>
+ScanTile staged_tile()
+{
+    ScanTile t{};
+    t.seg = SEG, t.nsw = NSW, t.waves = W, t.cpw = CPW, t.rs = W * NSW, t.ealign = 8, t.staged = true;
+    t.fn[0][0] = &launch_staged<false, SEG, NSW, W, CPW, false>;
+    t.fn[0][1] = &launch_staged<true, SEG, NSW, W, CPW, false>;
+    t.fn[1][0] = &launch_staged<false, SEG, NSW, W, CPW, true>;
+    t.fn[1][1] = &launch_staged<true, SEG, NSW, W, CPW, true>;
+    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d_w%d_c%d", SEG, NSW, W, CPW);
+    return t;
+}
+
+template <int SEG>
+void add_scan_tiles(ScanTile *&t)
+{
+    *t++ = direct_tile<SEG, 16>();
+    *t++ = direct_tile<SEG, 8>();
+    *t++ = staged_tile<SEG, 16, 1, 4>();
+    *t++ = staged_tile<SEG, 16, 1, 8>();
+    *t++ = staged_tile<SEG, 16, 1, 2>();
+    *t++ = staged_tile<SEG, 8, 2, 4>();
+}
+
+constexpr int kScanTiles = 24;
+
 const ScanTile *scan_tiles(int *count)
 {
-    static const ScanTile table[] = {make_scan_tile<8, 16>(), make_scan_tile<4, 16>(), make_scan_tile<2, 16>(),
-                                     make_scan_tile<1, 16>(), make_scan_tile<8, 8>(),  make_scan_tile<4, 8>(),
-                                     make_scan_tile<2, 8>(),  make_scan_tile<1, 8>()};
-    *count = static_cast<int>(sizeof table / sizeof table[0]);
+    static ScanTile table[kScanTiles];
+    static const bool init = [] {
+        ScanTile *t = table;
+        add_scan_tiles<8>(t);
+        add_scan_tiles<4>(t);
+        add_scan_tiles<2>(t);
+        add_scan_tiles<1>(t);
+        return t == table + kScanTiles;
+    }();
+    (void)init;
+    *count = kScanTiles;
     return table;
 }
 
-// Default launch configuration, from a sweep of every configuration on
-// MI355X (batch 1, dim 1024, d_state 16, 4096 fp16 tokens, cold and warm
-// caches): the largest token segment that a launch still fills (64 lanes x SEG
-// tokens per block; chunks of 64, 128, 256 and 512 tokens are fastest at
-// SEG 1, 2, 4 and 8), with 8 states per wave: two waves per channel hide
-// latency that one wave cannot (59.4 us against 69.9 us per sequence at chunk
-// 512), and are within 1% of 16 states per wave when a launch covers the
-// whole sequence.
-int default_scan_tile(int64_t span)
+// Default launch configuration, from a sweep of the configurations on MI355X
+// (d_state 16, 4096 fp16 tokens per request, 1, 2, 4, 8 and 16 requests of
+// 1024 channels, static chunk 512 and one launch, cold caches): the largest
+// token segment that a launch still fills (64 lanes x SEG tokens per block);
+// then by the number of channels:
+//   up to 1024:  the direct kernel, two waves of 8 states per channel (at one
+//                request 59.95 us per sequence at chunk 512 against 64.03 for
+//                the best staged one: latency bound);
+//   up to 2048:  staged, two waves of 8 states per channel, four channels per
+//                workgroup (two requests: 85.6 against 108.4 us direct);
+//   above:       staged, one wave of 16 states per channel, four channels per
+//                workgroup (16 requests: 384.5 against 595.6 us direct, and
+//                355.4 against 479.4 us in one launch).
+// Where a group's channels do not split into fours, the direct kernel.
+constexpr int64_t kDirectChannels = 1024;
+constexpr int64_t kTwoWaveChannels = 2048;
+
+int default_scan_tile(int64_t span, int64_t channels, int ch_per_group)
 {
     int count = 0;
     const ScanTile *t = scan_tiles(&count);
@@ -502,9 +878,17 @@ int default_scan_tile(int64_t span)
             seg = sg;
             break;
         }
-    for (int i = 0; i < count; ++i)
-        if (t[i].seg == seg && t[i].nsw == 8)
+    const bool staged = channels > kDirectChannels && ch_per_group % 4 == 0;
+    const bool two_waves = channels <= kTwoWaveChannels;
+    for (int i = 0; i < count; ++i) {
+        const ScanTile &x = t[i];
+        if (x.seg != seg || x.staged != staged)
+            continue;
+        if (!staged && x.nsw == 8)
             return i;
+        if (staged && x.cpw == 4 && (two_waves ? (x.nsw == 8 && x.waves == 2) : (x.nsw == 16 && x.waves == 1)))
+            return i;
+    }
     return 0;
 }
 
@@ -604,10 +988,14 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
         }
     }
 
-    const int t = tile >= 0 ? tile : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L);
+    const int ch_per_group = dim / G;
+    const int64_t channels = static_cast<int64_t>(bs) * dim;
+    const int t = tile >= 0 ? tile : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, channels, ch_per_group);
     const ScanTile &T = tiles[t];
-    const int waves = (N + T.nsw - 1) / T.nsw;
-    const bool single = waves == 1 && T.fn[1][0][0] != nullptr;
+    if (ch_per_group % T.cpw)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: %s needs the channels of a group (%d) in multiples of %d", T.name,
+                    ch_per_group, T.cpw);
+    const int rounds = (N + T.rs - 1) / T.rs;
 
     ScanParams p{};
     p.u = static_cast<const uint16_t *>(a->u.ptr);
@@ -626,11 +1014,13 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
     p.o_b = a->out.stride[0], p.o_d = a->out.stride[1];
     p.st_b = a->state.stride[0], p.st_d = a->state.stride[1];
     p.A_d = a->A.stride[0], p.A_n = a->A.stride[1];
-    p.dim = dim, p.dstate = N, p.ch_per_group = dim / G, p.softplus = a->delta_softplus;
+    p.dim = dim, p.dstate = N, p.ch_per_group = ch_per_group, p.softplus = a->delta_softplus;
+    p.rounds = rounds;
 
-    // Vector loads need every row start and every chunk start aligned to
-    // 2 * SEG bytes.
-    const int64_t ealign = T.seg;  // in 16-bit elements
+    // Vector access (SEG tokens of a row per lane; for the staged kernel also
+    // 16-byte pieces of the B and C rows into LDS) needs every row start and
+    // every chunk start on a multiple of T.ealign elements.
+    const int64_t ealign = T.ealign;  // in 16-bit elements
     bool vec = true;
     if (L > 0) {
         for (const ssu_view *v : {&a->u, &a->delta, &a->out})
@@ -642,12 +1032,12 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
     }
     const int64_t step = (chunk > 0 && chunk < L) ? chunk : L;
     const bool f16 = a->u.dtype == SSU_F16;
-    const int grid = bs * dim;
+    const ScanFn fn = T.fn[N % T.rs == 0][f16];
     for (int64_t t0 = 0; t0 < L; t0 += step) {
         p.t0 = t0;
         p.t1 = std::min(L, t0 + step);
         p.vec = vec && (t0 % ealign == 0);
-        const hipError_t e = T.fn[single][N % T.nsw == 0][f16](p, grid, waves * kLanes, stream);
+        const hipError_t e = fn(p, channels, stream);
         if (e != hipSuccess)
             return fail(SSU_ERR_HIP, "launch of %s failed: %s", T.name, hipGetErrorString(e));
     }

@@ -504,7 +504,7 @@ def test_scan_other_rejections(ssu):
     assert _scan_call(ssu, a, chunk=-1) == 1
     assert _scan_call(ssu, a, tile=ssu._lib.ssu_scan_tile_count()) == 1
     assert _scan_call(ssu, a, tile=-2) == 1
-    assert ssu._lib.ssu_scan_tile_count() == len(ssu.scan_tiles()) == 8
+    assert ssu._lib.ssu_scan_tile_count() == len(ssu.scan_tiles()) == 24
     assert ssu._lib.ssu_scan_tile_name(0).decode().startswith("scan_")
     assert ssu._lib.ssu_scan_tile_name(99) == b""
 
