@@ -181,64 +181,174 @@ __device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(SEG + 1) / 2], 
     return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
 }
 
-// One step of the 64-lane scan for two states at once, as in-place DPP
-// operations: every lane combines its map (P, Q) with the map of the lane that
-// the DPP control names (the earlier tokens), Q += P * Q_src, then
-// P *= P_src. A lane without a source (shifted out of its row, or in a row
-// the row mask leaves out) is not written, which is the same as combining
-// with the identity map (1, 0). The leading s_nop gives the two wait states a
-// DPP read needs after a VALU write of its source register.
-#define SSU_SCAN_STEP2(DPPCTL, Q0, Q1, P0, P1)                      \
-    asm("s_nop 1\n\t"                                               \
-        "v_fmac_f32_dpp %0, %0, %2 " DPPCTL "\n\t"                  \
-        "v_fmac_f32_dpp %1, %1, %3 " DPPCTL "\n\t"                  \
-        "v_mul_f32_dpp %2, %2, %2 " DPPCTL "\n\t"                   \
-        "v_mul_f32_dpp %3, %3, %3 " DPPCTL                           \
+// The 64-lane inclusive scan of the lanes' maps (P, Q), for two states at
+// once or for one, as in-place DPP operations: at each level every lane
+// combines its map with the map of the lane that the DPP control names (the
+// earlier tokens), Q += P * Q_src, then P *= P_src. A lane without a source
+// (shifted out of its row, or in a row the row mask leaves out) is not
+// written, which is the same as combining with the identity map (1, 0). The
+// levels: shifts 1, 2, 4, 8 within rows of 16, then lane 15 of each row into
+// the next (rows 1, 3) and lane 31 into rows 2, 3. A DPP read needs two wait
+// states after a VALU write of its source register: the leading s_nop 1
+// covers the caller's last writes; between levels, two interleaved states
+// already put three instructions between a write and its next DPP read, and
+// one state needs an s_nop 0.
+#define SSU_SCAN_LEVEL2(CTL)                                        \
+    "v_fmac_f32_dpp %0, %0, %2 " CTL "\n\t"                         \
+    "v_fmac_f32_dpp %1, %1, %3 " CTL "\n\t"                         \
+    "v_mul_f32_dpp %2, %2, %2 " CTL "\n\t"                          \
+    "v_mul_f32_dpp %3, %3, %3 " CTL "\n\t"
+#define SSU_SCAN_TREE2(Q0, Q1, P0, P1)                                                  \
+    asm("s_nop 1\n\t" SSU_SCAN_LEVEL2("row_shr:1 row_mask:0xf bank_mask:0xf")          \
+            SSU_SCAN_LEVEL2("row_shr:2 row_mask:0xf bank_mask:0xf")                      \
+                SSU_SCAN_LEVEL2("row_shr:4 row_mask:0xf bank_mask:0xf")                  \
+                    SSU_SCAN_LEVEL2("row_shr:8 row_mask:0xf bank_mask:0xf")              \
+                        SSU_SCAN_LEVEL2("row_bcast:15 row_mask:0xa bank_mask:0xf")       \
+                            SSU_SCAN_LEVEL2("row_bcast:31 row_mask:0xc bank_mask:0xf")   \
         : "+v"(Q0), "+v"(Q1), "+v"(P0), "+v"(P1))
-
-// The same step for one state: the s_nop gives the DPP read of Q the wait
-// states it needs after the previous step's write of Q (one instruction
-// between them).
-#define SSU_SCAN_STEP1(DPPCTL, Q0, P0)                              \
-    asm("s_nop 1\n\t"                                               \
-        "v_fmac_f32_dpp %0, %0, %1 " DPPCTL "\n\t"                  \
-        "v_mul_f32_dpp %1, %1, %1 " DPPCTL                           \
+#define SSU_SCAN_LEVEL1(CTL)                                        \
+    "v_fmac_f32_dpp %0, %0, %1 " CTL "\n\t"                         \
+    "v_mul_f32_dpp %1, %1, %1 " CTL "\n\t"
+#define SSU_SCAN_TREE1(Q0, P0)                                                                      \
+    asm("s_nop 1\n\t" SSU_SCAN_LEVEL1("row_shr:1 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"          \
+            SSU_SCAN_LEVEL1("row_shr:2 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                      \
+                SSU_SCAN_LEVEL1("row_shr:4 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                  \
+                    SSU_SCAN_LEVEL1("row_shr:8 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"              \
+                        SSU_SCAN_LEVEL1("row_bcast:15 row_mask:0xa bank_mask:0xf") "s_nop 0\n\t"       \
+                            SSU_SCAN_LEVEL1("row_bcast:31 row_mask:0xc bank_mask:0xf")                   \
         : "+v"(Q0), "+v"(P0))
 
 // DPP control of the one-lane shift of the whole wave (GFX9 encoding).
 constexpr int kWaveShr1 = 0x138;
 
-constexpr float kLog2eLo = 1.925963033500011e-08f;  // log2(e) - (float)log2(e)
-constexpr float kLn2 = 0.693147180559945309f;
+constexpr float kLn2Hi = 0.693147182464599609375f;      // (float)ln 2
+constexpr float kLn2Lo = -1.904654323148236e-09f;       // ln 2 - kLn2Hi
 
 // softplus(v) = max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1], and
-// log1p(e) = 2 atanh(s), s = e / (2 + e) in (0, 1/3]: the odd series
-// 2 s (1 + s^2/3 + s^4/5 + ... + s^14/15) has terms shrinking by s^2 <= 1/9, so
-// eight of them reach fp32 precision. e is the hardware exp2 of
-// -|v| log2(e), with the rounding error of that product (exact by an fma)
-// and of the constant folded back in to first order. -|v| is clamped at -128,
-// where exp2 is already 0 in fp32, so that infinite v give e = 0 rather than
-// inf - inf; the positive part is a select that lets NaN through (fmaxf would
-// drop it): softplus(+inf) = +inf, softplus(-inf) = 0, softplus(NaN) = NaN,
-// and every finite v gives the same bits as without the clamp.
+// log1p(e) = 2 atanh(s) = s q(s^2), s = e / (2 + e) in (0, 1/3]. q is a
+// degree-4 polynomial fitted to 2 atanh(sqrt z) / sqrt z on z in [0, 1/9] by
+// the Remez exchange (relative error 4e-9, under a tenth of an fp32 ulp;
+// fit_softplus.py beside this file recomputes it). e is the hardware exp2 of
+// t = -|v| log2(e) in fp32, times exp(r) ~ 1 + r for the residual
+// r = -|v| - t ln 2 (ln 2 split in two, each product exact in an fma), so the
+// rounding of t costs nothing. -|v| is clamped at -128, where exp2 is already
+// 0 in fp32, so that infinite v give e = 0 rather than inf - inf; the
+// positive part is a select that lets NaN through (fmaxf would drop it):
+// softplus(+inf) = +inf, softplus(-inf) = 0, softplus(NaN) = NaN, and every
+// finite v gives the same bits as without the clamp.
 __device__ __forceinline__ float softplus_f32(float v)
 {
     const float x = __builtin_amdgcn_fmed3f(-fabsf(v), -128.0f, 0.0f);  // NaN: carried by the select below
     const float t = x * kLog2e;
-    const float r = fmaf(x, kLog2e, -t) + x * kLog2eLo;
-    const float e0 = __builtin_amdgcn_exp2f(t);
-    const float e = fmaf(e0 * kLn2, r, e0);
+    const float ex = __builtin_amdgcn_exp2f(t);
+    const float r = fmaf(-t, kLn2Lo, fmaf(-t, kLn2Hi, x));
+    const float e = fmaf(ex, r, ex);
     const float sv = e * __builtin_amdgcn_rcpf(2.0f + e);
-    const float s2 = sv * sv;
-    float q = 1.0f / 15.0f;
-    q = fmaf(q, s2, 1.0f / 13.0f);
-    q = fmaf(q, s2, 1.0f / 11.0f);
-    q = fmaf(q, s2, 1.0f / 9.0f);
-    q = fmaf(q, s2, 1.0f / 7.0f);
-    q = fmaf(q, s2, 1.0f / 5.0f);
-    q = fmaf(q, s2, 1.0f / 3.0f);
-    q = fmaf(q, s2, 1.0f);
-    return (v <= 0.0f ? 0.0f : v) + 2.0f * sv * q;
+    const float z = sv * sv;
+    float q = fmaf(2.817833424e-01f, z, 2.796060145e-01f);
+    q = fmaf(q, z, 4.002490938e-01f);
+    q = fmaf(q, z, 6.666631699e-01f);
+    q = fmaf(q, z, 2.0f);
+    return fmaf(sv, q, v <= 0.0f ? 0.0f : v);
+}
+
+// One state's scan over one block of 64 * SEG tokens, in this lane's SEG
+// tokens: dl their step sizes, du = dl * u their inputs, dls = the sum of dl
+// (in token order), Bw and Cw the state's B and C bits, A2 = A * log2(e), h
+// the carried state (wave uniform). Adds the state's h_j * C_j to yy[j] and
+// returns the carried state after the block.
+//   1. the lane's whole map: decay exp2(A2 * dls) (the product of its
+//      tokens' decays in one exponential), and the state Q reached from 0;
+//   2. the 64-lane inclusive scan of the maps;
+//   3. the lane's end state e (the map applied to h) and start state g (e
+//      shifted one lane up, lane 0 taking h); the lane's tokens are replayed
+//      from g, h_j = a_j h_{j-1} + b_j, and after its last token the state
+//      is e;
+//   4. lane 63's e is the carried state.
+template <bool F16, int SEG>
+__device__ __forceinline__ float scan_state(const float (&dl)[SEG], const float (&du)[SEG], float dls, float A2,
+                                            const uint32_t (&Bw)[(SEG + 1) / 2], const uint32_t (&Cw)[(SEG + 1) / 2],
+                                            float h, float (&yy)[SEG])
+{
+    float a[SEG], b[SEG];
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        a[j] = __builtin_amdgcn_exp2f(dl[j] * A2);
+        b[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw, j)), 0.0f);
+    }
+    float Q = b[0];
+#pragma unroll
+    for (int j = 1; j < SEG; ++j)
+        Q = fmaf(a[j], Q, b[j]);
+    float P = __builtin_amdgcn_exp2f(dls * A2);
+    SSU_SCAN_TREE1(Q, P);
+    const float e = fmaf(P, h, Q);
+    const float g = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(h), __float_as_int(e), kWaveShr1, 0xf, 0xf, false));
+    float hj = g;
+#pragma unroll
+    for (int j = 0; j < SEG - 1; ++j) {
+        hj = fmaf(a[j], hj, b[j]);
+        yy[j] = fmaf(hj, io_to_f32<F16>(half_of<SEG>(Cw, j)), yy[j]);
+    }
+    yy[SEG - 1] = fmaf(e, io_to_f32<F16>(half_of<SEG>(Cw, SEG - 1)), yy[SEG - 1]);
+    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), kLanes - 1));
+}
+
+// The same for two states n, n+1 at once (their dependent steps interleave),
+// with the same operations per state, so the same bits. y gets state n's
+// terms before state n+1's.
+template <bool F16, int SEG>
+__device__ __forceinline__ void scan_state2(const float (&dl)[SEG], const float (&du)[SEG], float dls, float A20,
+                                            float A21, const uint32_t (&B0)[(SEG + 1) / 2],
+                                            const uint32_t (&B1)[(SEG + 1) / 2], const uint32_t (&C0)[(SEG + 1) / 2],
+                                            const uint32_t (&C1)[(SEG + 1) / 2], float &h0, float &h1,
+                                            float (&yy)[SEG])
+{
+    float a0[SEG], b0[SEG], a1[SEG], b1[SEG];
+#pragma unroll
+    for (int j = 0; j < SEG; ++j) {
+        a0[j] = __builtin_amdgcn_exp2f(dl[j] * A20);
+        a1[j] = __builtin_amdgcn_exp2f(dl[j] * A21);
+        b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B0, j)), 0.0f);
+        b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B1, j)), 0.0f);
+    }
+    float Q0 = b0[0], Q1 = b1[0];
+#pragma unroll
+    for (int j = 1; j < SEG; ++j) {
+        Q0 = fmaf(a0[j], Q0, b0[j]);
+        Q1 = fmaf(a1[j], Q1, b1[j]);
+    }
+    float P0 = __builtin_amdgcn_exp2f(dls * A20), P1 = __builtin_amdgcn_exp2f(dls * A21);
+    SSU_SCAN_TREE2(Q0, Q1, P0, P1);
+    const float e0 = fmaf(P0, h0, Q0), e1 = fmaf(P1, h1, Q1);
+    const float g0 = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(h0), __float_as_int(e0), kWaveShr1, 0xf, 0xf, false));
+    const float g1 = __int_as_float(
+        __builtin_amdgcn_update_dpp(__float_as_int(h1), __float_as_int(e1), kWaveShr1, 0xf, 0xf, false));
+    float hj0 = g0, hj1 = g1;
+#pragma unroll
+    for (int j = 0; j < SEG - 1; ++j) {
+        hj0 = fmaf(a0[j], hj0, b0[j]);
+        hj1 = fmaf(a1[j], hj1, b1[j]);
+        yy[j] = fmaf(hj0, io_to_f32<F16>(half_of<SEG>(C0, j)), yy[j]);
+        yy[j] = fmaf(hj1, io_to_f32<F16>(half_of<SEG>(C1, j)), yy[j]);
+    }
+    yy[SEG - 1] = fmaf(e0, io_to_f32<F16>(half_of<SEG>(C0, SEG - 1)), yy[SEG - 1]);
+    yy[SEG - 1] = fmaf(e1, io_to_f32<F16>(half_of<SEG>(C1, SEG - 1)), yy[SEG - 1]);
+    h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
+    h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1), kLanes - 1));
+}
+
+// The sum of a lane's step sizes, in token order.
+template <int SEG>
+__device__ __forceinline__ float step_sum(const float (&dl)[SEG])
+{
+    float s = dl[0];
+#pragma unroll
+    for (int j = 1; j < SEG; ++j)
+        s += dl[j];
+    return s;
 }
 
 // One wave's share of one (request, channel): its 16 states' carried values
@@ -293,12 +403,14 @@ struct Chan {
         float dl[SEG], du[SEG];
 #pragma unroll
         for (int j = 0; j < SEG; ++j) {
-            const float v = io_to_f32<F16>(half_of<SEG>(dw, j)) + bias;
+            // (the f16 conversions fold into mixed-precision fmas; x * 1 + bias
+            // and sv * u + 0 round exactly as x + bias and sv * u)
+            const float v = fmaf(io_to_f32<F16>(half_of<SEG>(dw, j)), 1.0f, bias);
             float sv = softplus ? softplus_f32(v) : v;
             if (!FAST)
                 sv = tok + j < t1 ? sv : 0.0f;
             dl[j] = sv;
-            du[j] = sv * io_to_f32<F16>(half_of<SEG>(uw, j));
+            du[j] = fmaf(sv, io_to_f32<F16>(half_of<SEG>(uw, j)), 0.0f);
         }
 #pragma unroll
         for (int gi = 0; gi < GROUPS; ++gi)
@@ -306,57 +418,11 @@ struct Chan {
             for (int j = 0; j < SEG; ++j)
                 yg[gi][j] = 0.0f;
 
+        const float dls = step_sum<SEG>(dl);
 #pragma unroll
-        for (int n = 0; n < NSW; n += 2) {
-            // two states at a time, so that each one's dependent steps
-            // interleave with the other's
-            float a0[SEG], b0[SEG], a1[SEG], b1[SEG];
-#pragma unroll
-            for (int j = 0; j < SEG; ++j) {
-                a0[j] = __builtin_amdgcn_exp2f(dl[j] * A2[n]);
-                a1[j] = __builtin_amdgcn_exp2f(dl[j] * A2[n + 1]);
-                b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n], j)), 0.0f);
-                b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw[n + 1], j)), 0.0f);
-            }
-            // 1. this lane's maps from its first token to each of its tokens
-            // (the prefix products P_j of the decays and the states Q_j reached
-            // from 0), the last of which is the lane's whole map
-            float P0[SEG], Q0[SEG], P1[SEG], Q1[SEG];
-            P0[0] = a0[0], Q0[0] = b0[0], P1[0] = a1[0], Q1[0] = b1[0];
-#pragma unroll
-            for (int j = 1; j < SEG; ++j) {
-                Q0[j] = fmaf(a0[j], Q0[j - 1], b0[j]);
-                P0[j] = P0[j - 1] * a0[j];
-                Q1[j] = fmaf(a1[j], Q1[j - 1], b1[j]);
-                P1[j] = P1[j - 1] * a1[j];
-            }
-            // 2. inclusive scan of the lanes' whole maps over the 64 lanes:
-            // shifts 1, 2, 4, 8 within rows of 16, then lane 15 of each row into
-            // the next (rows 1, 3) and lane 31 into rows 2, 3
-            float SP0 = P0[SEG - 1], SQ0 = Q0[SEG - 1], SP1 = P1[SEG - 1], SQ1 = Q1[SEG - 1];
-            SSU_SCAN_STEP2("row_shr:1 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            SSU_SCAN_STEP2("row_shr:2 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            SSU_SCAN_STEP2("row_shr:4 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            SSU_SCAN_STEP2("row_shr:8 row_mask:0xf bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            SSU_SCAN_STEP2("row_bcast:15 row_mask:0xa bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            SSU_SCAN_STEP2("row_bcast:31 row_mask:0xc bank_mask:0xf", SQ0, SQ1, SP0, SP1);
-            const float e0 = fmaf(SP0, h0[n], SQ0), e1 = fmaf(SP1, h0[n + 1], SQ1);
-            // 3. start state of each lane (lane 0: the carried state); each of
-            // the lane's states is its prefix map applied to it, independently
-            const float g0 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n]), __float_as_int(e0),
-                                                                        kWaveShr1, 0xf, 0xf, false));
-            const float g1 = __int_as_float(__builtin_amdgcn_update_dpp(__float_as_int(h0[n + 1]), __float_as_int(e1),
-                                                                        kWaveShr1, 0xf, 0xf, false));
-            // 4. carried states
-            h0[n] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
-            h0[n + 1] = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1), kLanes - 1));
-#pragma unroll
-            for (int j = 0; j < SEG; ++j) {
-                float &y = yg[n / kGroup][j];
-                y = fmaf(fmaf(P0[j], g0, Q0[j]), io_to_f32<F16>(half_of<SEG>(Cw[n], j)), y);
-                y = fmaf(fmaf(P1[j], g1, Q1[j]), io_to_f32<F16>(half_of<SEG>(Cw[n + 1], j)), y);
-            }
-        }
+        for (int n = 0; n < NSW; n += 2)
+            scan_state2<F16, SEG>(dl, du, dls, A2[n], A2[n + 1], Bw[n], Bw[n + 1], Cw[n], Cw[n + 1], h0[n],
+                                  h0[n + 1], yg[n / kGroup]);
     }
 };
 
@@ -560,19 +626,20 @@ ssu_scan_staged_kernel(const ScanParams p)
         uint32_t uw[WORDS], dw[WORDS];
         load_seg<SEG, fast>(u_row, tok, p.t1, uw);
         load_seg<SEG, fast>(dl_row, tok, p.t1, dw);
-        float dl[SEG], du[SEG], y[SEG];
+        float dl[SEG], du[SEG], y[SEG], dls = 0.0f;
 
         // step sizes Delta_j and inputs Delta_j u_j of this lane's tokens
-        // (invalid tokens: the identity)
+        // (invalid tokens: the identity), and their sum
         auto steps = [&]() {
 #pragma unroll
             for (int j = 0; j < SEG; ++j) {
-                const float v = io_to_f32<F16>(half_of<SEG>(dw, j)) + bias;
+                const float v = fmaf(io_to_f32<F16>(half_of<SEG>(dw, j)), 1.0f, bias);
                 float sv = softplus ? softplus_f32(v) : v;
                 sv = (fast || tok + j < p.t1) ? sv : 0.0f;
                 dl[j] = sv;
-                du[j] = sv * io_to_f32<F16>(half_of<SEG>(uw, j));
+                du[j] = fmaf(sv, io_to_f32<F16>(half_of<SEG>(uw, j)), 0.0f);
             }
+            dls = step_sum<SEG>(dl);
         };
 
         for (int r = 0; r < rounds; ++r) {
@@ -668,43 +735,24 @@ ssu_scan_staged_kernel(const ScanParams p)
 #pragma unroll
                 for (int j = 0; j < SEG; ++j)
                     yy[j] = 0.0f;
+                // the group's carried states and decay rates, lane k holding
+                // state gi * 8 + k's, read out and written back per state
+                // with lane reads and writes
+                float hg = lane < kGroup ? hrow[gi * kGroup + lane] : 0.0f;
+                const float ag = lane < kGroup ? arow[gi * kGroup + lane] : 0.0f;
 #pragma unroll 1
-                for (int n = gi * kGroup; n < (gi + 1) * kGroup; ++n) {
-                    const float hv = hrow[n];
-                    const float av = arow[n];
+                for (int k = 0; k < kGroup; ++k) {
+                    const int n = gi * kGroup + k;
+                    const float hv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hg), k));
+                    const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ag), k));
                     uint32_t B0[WORDS], C0[WORDS];
                     lds_seg<SEG>(sB + n * BLOCK, B0);
                     lds_seg<SEG>(sC + n * BLOCK, C0);
-                    float a0[SEG], b0[SEG];
-#pragma unroll
-                    for (int j = 0; j < SEG; ++j) {
-                        a0[j] = __builtin_amdgcn_exp2f(dl[j] * av);
-                        b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B0, j)), 0.0f);
-                    }
-                    float P0[SEG], Q0[SEG];
-                    P0[0] = a0[0], Q0[0] = b0[0];
-#pragma unroll
-                    for (int j = 1; j < SEG; ++j) {
-                        Q0[j] = fmaf(a0[j], Q0[j - 1], b0[j]);
-                        P0[j] = P0[j - 1] * a0[j];
-                    }
-                    float SP0 = P0[SEG - 1], SQ0 = Q0[SEG - 1];
-                    SSU_SCAN_STEP1("row_shr:1 row_mask:0xf bank_mask:0xf", SQ0, SP0);
-                    SSU_SCAN_STEP1("row_shr:2 row_mask:0xf bank_mask:0xf", SQ0, SP0);
-                    SSU_SCAN_STEP1("row_shr:4 row_mask:0xf bank_mask:0xf", SQ0, SP0);
-                    SSU_SCAN_STEP1("row_shr:8 row_mask:0xf bank_mask:0xf", SQ0, SP0);
-                    SSU_SCAN_STEP1("row_bcast:15 row_mask:0xa bank_mask:0xf", SQ0, SP0);
-                    SSU_SCAN_STEP1("row_bcast:31 row_mask:0xc bank_mask:0xf", SQ0, SP0);
-                    const float e0 = fmaf(SP0, hv, SQ0);
-                    const float g0 = __int_as_float(__builtin_amdgcn_update_dpp(
-                        __float_as_int(hv), __float_as_int(e0), kWaveShr1, 0xf, 0xf, false));
-                    const float n0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
-                    if (lane == 0)
-                        hrow[n] = n0;
-#pragma unroll
-                    for (int j = 0; j < SEG; ++j)
-                        yy[j] = fmaf(fmaf(P0[j], g0, Q0[j]), io_to_f32<F16>(half_of<SEG>(C0, j)), yy[j]);
+                    const float hn = scan_state<F16, SEG>(dl, du, dls, av, B0, C0, hv, yy);
+                    hg = lane == k ? hn : hg;
                 }
+                if (lane < kGroup)
+                    hrow[gi * kGroup + lane] = hg;
                 // the group's partial: added by wave 0 in group order, handed
                 // over through LDS by the channel's other waves
                 if (w == 0) {
