@@ -380,7 +380,7 @@ def run_tile_sweep(a):
     print(f"# H{H} P{P} N{N} bs{bs}: {nbytes} B/call; auto tile {ssu.tiles()[auto]['name']}", file=out)
     print("tile name rows_per_group waves us_per_call GBps pct_peak", file=out, flush=True)
     for t in ssu.tiles():
-        if t["dstate"] != N or P % t["rows_per_group"]:
+        if t["dstate"] != N or not ssu.tile_fits(t, H, P):
             continue
         h = ssu.Handle(H, P, N, G, True, t["id"])
         args = rot.args(h)
@@ -425,7 +425,7 @@ def run_shapes(a):
         ids = [auto]
         if a.tile_sweep:
             ids += [t["id"] for t in ssu.tiles()
-                    if t["dstate"] == N and P % t["rows_per_group"] == 0 and t["id"] != auto]
+                    if t["dstate"] == N and ssu.tile_fits(t, H, P) and t["id"] != auto]
         for tid in ids:
             h = ssu.Handle(H, P, N, G, True, tid)
             args = rot.args(h)

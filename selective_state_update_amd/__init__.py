@@ -36,6 +36,7 @@ __all__ = [
     "selective_scan",
     "scan_launch",
     "scan_tiles",
+    "tile_fits",
     "tiles",
     "library_path",
     "abi_version",
@@ -179,6 +180,16 @@ def tiles():
                         rows_per_group=d.rows_per_group, nontemporal=d.nontemporal,
                         xcd_remap=d.xcd_remap, groups_per_cu=d.groups_per_cu, name=d.name.decode()))
     return out
+
+
+def tile_fits(t, nheads: int, headdim: int) -> bool:
+    """Whether launch configuration `t` (a dict from tiles()) serves H heads of
+    headdim P: its rows per group divide P, or each of its waves covers one
+    whole head and its waves split the heads evenly (the library's rule)."""
+    rg, rw = t["rows_per_group"], t["rows_per_wave"]
+    if headdim % rg == 0:
+        return True
+    return rw == headdim and rg % headdim == 0 and nheads % (rg // headdim) == 0
 
 
 def _torch():

@@ -280,14 +280,18 @@ struct Work {
             return;
         }
         const int g = p.xcd_remap ? xcd_order(graw, p.total_groups) : graw;
-        const int t = g % p.ptiles;
-        const int bh = g / p.ptiles;
+        // ptiles == 0: a wave covers a whole head (rows_per_wave == headdim)
+        // and the group's waves take consecutive heads of one request;
+        // otherwise the group's rows are tile t of one head
+        const bool per_head = p.ptiles == 0;
+        const int t = per_head ? 0 : g % p.ptiles;
+        const int bh = per_head ? g * (rows_group / ROWS_WAVE) + wave : g / p.ptiles;
         h = bh % p.nheads;
         b = bh / p.nheads;
         grp = h / p.heads_per_group;
         c = lane % LPR;    // column chunk
         sub = lane / LPR;  // row within one instruction
-        wrow = t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
+        wrow = per_head ? 0 : t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
         p0 = wrow + sub;
 
         // B and C do not depend on the slot: requested first (vector-memory
@@ -658,6 +662,17 @@ using ssu::fail;
 
 bool valid_dstate(int n) { return n == 16 || n == 32 || n == 64 || n == 128 || n == 256; }
 
+// A launch configuration fits H heads of headdim P if its rows per group
+// divide P (a group covers part of one head), or if each of its waves covers
+// exactly one head and its waves split the heads evenly (a group covers
+// several whole heads of one request).
+bool tile_fits(const ssu_tile_desc &d, int H, int P)
+{
+    if (P % d.rows_per_group == 0)
+        return true;
+    return d.rows_per_wave == P && d.rows_per_group % P == 0 && H % (d.rows_per_group / P) == 0;
+}
+
 // The launch configuration for `batch` requests, from tile sweeps on MI355X
 // (every compiled configuration, H16 P64 N128, batches 8 to 512, cold state).
 // Non-temporal access and XCD-ordered workgroups win everywhere. What matters
@@ -812,12 +827,10 @@ ssu_status ssu_create(const ssu_config *cfg, ssu_handle **out)
             forced = static_cast<int32_t>(v);
         }
     }
-    if (forced >= 0) {
-        const ssu_tile_desc &d = ssu::tiles()[forced].d;
-        if (d.dstate != c.dstate || c.headdim % d.rows_per_group != 0)
-            return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: tile %s does not fit N=%d P=%d", d.name, c.dstate,
-                        c.headdim);
-    }
+    if (forced >= 0 &&
+        (ssu::tiles()[forced].d.dstate != c.dstate || !tile_fits(ssu::tiles()[forced].d, c.nheads, c.headdim)))
+        return fail(SSU_ERR_INVALID_ARGUMENT, "ssu_create: tile %s does not fit N=%d H=%d P=%d",
+                    ssu::tiles()[forced].d.name, c.dstate, c.nheads, c.headdim);
     ssu_handle *h = new (std::nothrow) ssu_handle;
     if (!h)
         return fail(SSU_ERR_NO_MEMORY, "ssu_create: out of host memory");
@@ -948,8 +961,12 @@ ssu_status run(const ssu_handle *hd, const Operands &a, hipStream_t stream)
     if (tile < 0)
         return fail(SSU_ERR_UNSUPPORTED, "no launch configuration for N=%d P=%d", c.dstate, c.headdim);
     const ssu::Tile &T = ssu::tiles()[tile];
-    const int ptiles = c.headdim / T.d.rows_per_group;
-    const int64_t groups = static_cast<int64_t>(a.batch) * c.nheads * ptiles;
+    // a group covers rows_per_group rows of one head, or (when its waves each
+    // cover a whole head) rows_per_group / headdim heads of one request
+    const bool per_head = T.d.rows_per_group > c.headdim;
+    const int ptiles = per_head ? 0 : c.headdim / T.d.rows_per_group;
+    const int64_t groups = per_head ? static_cast<int64_t>(a.batch) * c.nheads / (T.d.rows_per_group / c.headdim)
+                                    : static_cast<int64_t>(a.batch) * c.nheads * ptiles;
     if (groups > 0x7fffffff)
         return fail(SSU_ERR_UNSUPPORTED, "batch * heads too large for one launch");
 

@@ -142,8 +142,29 @@ def test_select_tile_fits_shape(ssu, N, P):
     for bs in (1, 8, 128, 512, 1024):
         i = ssu._lib.ssu_select_tile(h, bs)
         assert i >= 0
-        assert t[i]["dstate"] == N and P % t[i]["rows_per_group"] == 0
+        assert t[i]["dstate"] == N and ssu.tile_fits(t[i], 16, P)
     ssu._lib.ssu_destroy(h)
+
+
+@pytest.mark.parametrize("H", [1, 4, 12, 16])
+@pytest.mark.parametrize("N,P", [(16, 64), (32, 64), (16, 128), (128, 64)])
+def test_forced_tile_accepted_iff_it_fits(ssu, H, N, P):
+    """ssu_create takes a forced launch configuration exactly when tile_fits
+    says it serves H heads of headdim P (rows per group dividing P, or waves
+    of one whole head each that split the heads evenly)."""
+    t = ssu.tiles()
+    multi = 0
+    for x in t:
+        if x["dstate"] != N:
+            continue
+        st, h = _create(ssu, nheads=H, headdim=P, dstate=N, tile=x["id"])
+        fits = ssu.tile_fits(x, H, P)
+        assert (st == 0) == fits, (x["name"], H, P, st)
+        multi += fits and x["rows_per_group"] > P
+        if st == 0:
+            ssu._lib.ssu_destroy(h)
+    if (N, P, H) in ((16, 64, 16), (32, 64, 16)):
+        assert multi > 0  # groups of several whole heads exist for these shapes
 
 
 @pytest.mark.parametrize("bs,K,name", [
@@ -172,7 +193,7 @@ def test_select_tile_tokens_fits_shape(ssu, N, P):
         for K in (2, 4, 8, 16, 64):
             i = ssu._lib.ssu_select_tile_tokens(h, bs, K)
             assert i >= 0
-            assert t[i]["dstate"] == N and P % t[i]["rows_per_group"] == 0
+            assert t[i]["dstate"] == N and ssu.tile_fits(t[i], 16, P)
     ssu._lib.ssu_destroy(h)
 
 

@@ -67,11 +67,40 @@ def test_every_tile_bitwise_identical(ref, N, P):
     torch.cuda.synchronize()
     gu.compare_full(ref, dp, p.pool.copy(), base_out, f"N{N} P{P} auto")
     base_pool = dp.pool.clone()
-    ids = [t["id"] for t in ssu.tiles() if t["dstate"] == N and P % t["rows_per_group"] == 0]
+    ids = [t["id"] for t in ssu.tiles() if t["dstate"] == N and ssu.tile_fits(t, 4, P)]
     assert ids
     for tid in ids:
         dp.pool.copy_(backup)
         o = dp.run(tile=tid, out=torch.empty_like(base_out))
+        torch.cuda.synchronize()
+        assert torch.equal(o.view(torch.int16), base_out.view(torch.int16)), f"tile {tid} out differs"
+        assert torch.equal(dp.pool.view(torch.int32), base_pool.view(torch.int32)), f"tile {tid} state differs"
+
+
+@pytest.mark.parametrize("N", [16, 32])
+def test_multihead_tiles_bitwise_identical(ref, N):
+    """Groups whose waves each take a whole head of one request (2 to 16 heads
+    per group at H = 16, P = 64) give the same bits as the library's choice,
+    which matches the oracle; padding entries skip all of a group's heads."""
+    import selective_state_update_amd as ssu
+
+    torch = gu.torch_mod()
+    H, P = 16, 64
+    p = si.make_problem(H=H, P=P, N=N, G=2, batch=5, pool_slots=11, seed=530 + N)
+    idx = p.idx.copy()
+    idx[3] = -1
+    p.idx = idx
+    dp = gu.DeviceProblem(p)
+    backup = dp.pool.clone()
+    base_out = dp.run(tile=-1).clone()
+    torch.cuda.synchronize()
+    gu.compare_full(ref, dp, p.pool.copy(), base_out, f"N{N} multi-head auto")
+    base_pool = dp.pool.clone()
+    ids = [t["id"] for t in ssu.tiles() if t["dstate"] == N and ssu.tile_fits(t, H, P) and t["rows_per_group"] > P]
+    assert len(ids) >= 4
+    for tid in ids:
+        dp.pool.copy_(backup)
+        o = dp.run(tile=tid, out=base_out.clone())
         torch.cuda.synchronize()
         assert torch.equal(o.view(torch.int16), base_out.view(torch.int16)), f"tile {tid} out differs"
         assert torch.equal(dp.pool.view(torch.int32), base_pool.view(torch.int32)), f"tile {tid} state differs"
@@ -517,7 +546,7 @@ def test_random_shapes(ref, case):
     p.idx = idx
     tile = -1
     if rng.integers(0, 10) < 3:
-        fits = [t["id"] for t in ssu.tiles() if t["dstate"] == N and P % t["rows_per_group"] == 0]
+        fits = [t["id"] for t in ssu.tiles() if t["dstate"] == N and ssu.tile_fits(t, H, P)]
         tile = int(rng.choice(fits))
     what = (f"case {case}: N {N} P {P} H {H} G {G} bs {bs} slots {slots} softplus {softplus} "
             f"bias {use_bias} D {use_D} tile {tile}")

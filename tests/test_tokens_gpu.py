@@ -111,7 +111,7 @@ def test_tokens_every_tile_bitwise(ref, N):
     torch = gu.torch_mod()
     tp = TokenProblem(4, 64, N, 1, 6, 13, 3, seed=3100 + N)
     base = None
-    ids = [x for x in ssu.tiles() if x["dstate"] == N and 64 % x["rows_per_group"] == 0]
+    ids = [x for x in ssu.tiles() if x["dstate"] == N and ssu.tile_fits(x, 4, 64)]
     assert ids
     for t in ids:
         h = ssu.Handle(4, 64, N, 1, True, t["id"])
