@@ -955,6 +955,76 @@ same run.
     print(text)
 
 
+def run_floors(a):
+    """Per-call floors of the decode step at H16 P64 N128, at each batch of
+    --batches (default 8 and 128), same rotation and graph method as the
+    headline (cold sets, max(20, K) launches per graph, median of 5 x 10
+    replays):
+      (1) a graph launch of a 1-element kernel: the launch floor;
+      (2) ssu_update with every slot id padding: the launch, the id reads and
+          the small operands, no state traffic;
+      (3) ssu_update on one request (512 KiB of state): the launch plus one
+          dependent idx -> state round trip;
+      (4) a device copy of the call's state bytes (read and written,
+          contiguous, rotating buffers over >= 768 MiB): the bare stream;
+      (5) ssu_update at the batch."""
+    import torch
+
+    import selective_state_update_amd as ssu
+
+    out = open(a.out, "w") if a.out else sys.stdout
+    batches = [int(b) for b in (a.batches or "8,128").split(",")]
+    H, P, N, G = 16, 64, 128, 1
+    print("batch us_per_call what", file=out, flush=True)
+
+    def timed(fn, calls):
+        g = torch.cuda.CUDAGraph()
+        side = torch.cuda.Stream()
+        side.wait_stream(torch.cuda.current_stream())
+        with torch.cuda.stream(side):
+            fn(0)
+        torch.cuda.current_stream().wait_stream(side)
+        torch.cuda.synchronize()
+        with torch.cuda.graph(g):
+            for i in range(calls):
+                fn(i)
+        g.replay()
+        torch.cuda.synchronize()
+        us = statistics.median([time_graph(g, 10) / (10 * calls) for _ in range(5)]) * 1e6
+        del g
+        return us
+
+    for bs in batches:
+        rot = Rotation(H, P, N, G, bs, seed=9100 + bs)
+        one = Rotation(H, P, N, G, 1, seed=9200 + bs)
+        calls = max(20, rot.K)
+        h = ssu.Handle(H, P, N, G, True, a.tile)
+        args = rot.args(h)
+        pad = torch.full((bs,), -1, dtype=torch.int32, device="cuda")
+        pad_args = [h.make_args(rot.pool, pad, s["x"], s["B"], s["C"], s["dt"], rot.A, rot.D, rot.dt_bias, s["out"])
+                    for s in rot.sets]
+        one_args = one.args(h)
+        nbytes = bs * H * P * N * 4
+        pairs = max(2, -(-ROTATION_BYTES // (2 * nbytes)))
+        bufs = [(torch.empty(nbytes // 4, device="cuda"), torch.empty(nbytes // 4, device="cuda"))
+                for _ in range(pairs)]
+        tiny = torch.zeros(1, device="cuda")
+        rows = [
+            ("launch of a 1-element kernel", lambda i: tiny.add_(1.0), calls),
+            ("ssu_update, every slot id padding (no state traffic)", lambda i: h.launch(pad_args[i % rot.K]), calls),
+            ("ssu_update on one request (512 KiB of state)", lambda i: h.launch(one_args[i % one.K]),
+             max(20, one.K)),
+            (f"device copy of the call's state bytes ({nbytes >> 20} MiB read + written, {pairs} rotating pairs)",
+             lambda i: bufs[i % pairs][1].copy_(bufs[i % pairs][0]), max(20, pairs)),
+            (f"ssu_update ({ssu.tiles()[h.selected_tile(bs)]['name']})", lambda i: h.launch(args[i % rot.K]), calls),
+        ]
+        for what, fn, n in rows:
+            us = timed(fn, n)
+            print(f"{bs} {us:.3f} {what}", file=out, flush=True)
+        del rot, one, bufs
+        torch.cuda.empty_cache()
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -972,6 +1042,7 @@ def main():
     ap.add_argument("--tile-sweep", action="store_true")
     ap.add_argument("--shapes", default="", help="comma list of HxPxNxGxBATCH decode shapes")
     ap.add_argument("--copy-ceiling", action="store_true")
+    ap.add_argument("--floors", action="store_true", help="per-call floors of the decode step (--batches)")
     ap.add_argument("--tokens", default="", help="comma list of tokens per call (ssu_update_tokens)")
     ap.add_argument("--copy-blocks", default="", help="comma list of request counts (ssu_copy_blocks)")
     ap.add_argument("--scan", default="", help="comma list of scan configs (ssu_scan), e.g. 1,2,3")
@@ -1004,6 +1075,8 @@ def main():
         run_tile_sweep(a)
     elif a.copy_ceiling:
         run_copy_ceiling(a)
+    elif a.floors:
+        run_floors(a)
     elif a.tokens:
         run_tokens(a)
     elif a.copy_blocks:
