@@ -787,6 +787,8 @@ def run_scan_counters(a):
     chunk = cfg.pop("chunk")
     if a.chunks:
         chunk = int(a.chunks.split(",")[0])
+    if a.scan_batch:
+        cfg["batch"] = a.scan_batch
     dt = torch.float16 if cfg["io"] == "f16" else torch.bfloat16
     sets = []
     for i in range(4):
@@ -807,8 +809,8 @@ def run_scan_counters(a):
         ssu.scan_launch(sets[i % 4]["args"], chunk, a.tile)
     torch.cuda.synchronize()
     n = _copy_reference()
-    print(f"# scan counters pass: {a.steps} sequences of config {k} at chunk {chunk}, 4 copies of {n} bytes",
-          flush=True)
+    print(f"# scan counters pass: {a.steps} sequences of config {k} (batch {cfg['batch']}) at chunk {chunk}, "
+          f"4 copies of {n} bytes", flush=True)
 
 
 def run_counters(a):
@@ -852,8 +854,12 @@ def summarize_scan_counters(a):
     """Counter summary for the scan kernel (see run_scan_counters)."""
     fetch_dir, write_dir = a.summarize_scan_counters.split(",")
     fetch, write = _load_counter(fetch_dir, "FETCH_SIZE"), _load_counter(write_dir, "WRITE_SIZE")
-    fs = [v for k, v in fetch if "ssu_scan_kernel" in k]
-    ws = [v for k, v in write if "ssu_scan_kernel" in k]
+    def is_scan(k):
+        return "ssu_scan_direct_kernel" in k or "ssu_scan_staged_kernel" in k
+
+    fs = [v for k, v in fetch if is_scan(k)]
+    ws = [v for k, v in write if is_scan(k)]
+    kernels = sorted({k for k, v in fetch if is_scan(k)})
     fc = [v for k, v in fetch if "MulFunctor" in k]
     wc = [v for k, v in write if "MulFunctor" in k]
     if not fs or not ws or not fc or not wc:
@@ -867,7 +873,7 @@ def summarize_scan_counters(a):
     f_b = statistics.median(fs) * 1024 * f_scale
     w_b = statistics.median(ws) * 1024 * w_scale
     cmd = f"python3 bench.py --scan {k} --scan-counters --steps {a.steps}"
-    text = f"""# rocprofv3 HBM counters: ssu_scan_kernel, {c['name']}
+    text = f"""# rocprofv3 HBM counters: the selective scan, {c['name']}
 
 Commands (run from the repository root on one MI355X):
 
@@ -881,6 +887,7 @@ Each dispatch is one chunk of {c['chunk']} tokens; the Infinity Cache is
 flushed between sequences.
 
 - scan_code_digest: `{scan_source_digest()}`
+- kernel: `{"`, `".join(kernels)}`
 - scan_dispatches: {len(fs)}
 - fetch_kib_median: {statistics.median(fs):.1f}
 - write_kib_median: {statistics.median(ws):.1f}

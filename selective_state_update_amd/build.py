@@ -50,5 +50,22 @@ def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
     return out
 
 
+PROBE_SRC = os.path.join(HERE, "csrc", "valu_rate_probe.hip")
+PROBE = os.path.join(HERE, "valu_rate_probe")
+
+
+def build_probe(out: str = PROBE) -> str:
+    """The VALU issue-rate probe (a standalone program, same code-generation
+    flags as the library)."""
+    flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
+    cmd = [HIPCC, *flags, "-o", out + ".tmp", PROBE_SRC]
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError("probe build failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
+    os.replace(out + ".tmp", out)
+    return out
+
+
 if __name__ == "__main__":
     print(build(verbose=True))
+    print(build_probe())
