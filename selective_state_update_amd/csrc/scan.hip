@@ -12,50 +12,61 @@
 //   y[t]  = sum_n h[n] * C[b,g,n,t] + D[d] * u[b,d,t]
 // with g = d / (dim / G), h read from and written back to the fp32 state.
 //
-// Two kernels compute it, with the same fp32 operations in the same order,
-// so every configuration of either gives the same bits:
+// Tokens go in blocks of 32 * T (T = 16, 8, 4 or 2 tokens per lane; 512
+// tokens at T = 16). Both halves of a wave (lanes 0-31 and 32-63) see the
+// same block: lane i of either half holds the segment of T tokens starting at
+// i * T, and the two halves scan two different states, so every wave
+// instruction advances two states at once. Per state the recurrence
+// h -> a h + b is a composition of affine maps, and composition is
+// associative:
+//   1. each lane composes its T pairs (a_j, b_j) into one map (P, Q);
+//   2. a 32-lane inclusive scan of the maps in a fixed tree (DPP row shifts
+//      1, 2, 4, 8, then lane 15 of each half into the half's second row)
+//      gives every lane the map from the block's start to its last token;
+//      applied to the carried state it is the state after that token;
+//   3. shifted one lane up within the half (the half's first lane takes the
+//      carried state) it is each lane's start state g; the lane's state after
+//      its token j is its prefix map applied to g, computed by replaying its
+//      tokens from g, h_j = a_j h_{j-1} + b_j, and y_j += h_j C_j;
+//   4. the half's last lane's end state is the carried state for the next
+//      block.
+// The carried state is uniform over the half, so blocks, and launches that
+// start on a block boundary, continue from exactly the value the previous
+// block ended with: chunkings whose chunks are multiples of 32 * T give
+// bitwise identical results.
 //
-//   direct (scan_t{SEG}_n{NSW}): one workgroup per (request, channel), one
-//     wave per NSW of its states; each wave loads its states' B and C rows
-//     straight into registers, all of a block's loads issued before any is
-//     used. Few instructions stand between a launch and its first result,
-//     which is what a small batch (a few thousand channels: latency bound)
-//     needs.
-//   staged (scan_t{SEG}_n{NSW}_w{W}_c{CPW}): a workgroup holds CPW channels of
-//     one (request, group), with W waves of NSW states each. The channels of
-//     a group share B and C, so the workgroup stages a block's B and C rows
-//     in LDS once, W * NSW states at a time (a round; d_state above that
-//     takes several rounds), and each wave reads the rows of the state it is
-//     working on just before it needs them, with the carried states and
-//     decay rates kept in LDS. Few registers are live, so four waves fit on
-//     each SIMD, and the B/C traffic falls by CPW: what a large batch
-//     (throughput bound) needs.
-//
-// Both split tokens into blocks of 64 * SEG: lane l owns tokens l*SEG ..
-// l*SEG+SEG-1 of a block, so a block's activations are one coalesced vector
-// load per lane. Per state n the recurrence h -> a h + b is a composition of
-// affine maps, and composition is associative:
-//   1. each lane composes its SEG pairs (a_j, b_j) into one map (P, Q);
-//   2. a 64-lane inclusive scan of the maps in a fixed tree (DPP row shifts
-//      1, 2, 4, 8, then row broadcasts 15 and 31) gives every lane the map
-//      from the block's start to its last token; applied to the carried state
-//      it is the state after that token;
-//   3. shifted one lane up (lane 0 takes the carried state) it is each lane's
-//      start state g; the lane's state after its token j is its prefix map
-//      applied to g, h_j = P_j g + Q_j (P_j, Q_j kept from step 1), computed
-//      for every j independently, and y_j += h_j C_j;
-//   4. lane 63's end state is the carried state for the next block.
-// The carried state is wave-uniform, so blocks, and launches that start on a
-// block boundary, continue from exactly the value the previous block ended
-// with: chunkings whose chunks are multiples of 64 * SEG give bitwise
-// identical results.
+// Work on tokens alone (the step sizes and their softplus, the inputs
+// Delta u, the output's D u term and its rounding) is not repeated in both
+// halves: of each segment the lower half's lane owns the first T/2 tokens and
+// the upper half's lane the last T/2; each computes its own tokens' values and
+// the two trade what the other needs with one v_permlane32_swap per value.
 //
 // y is summed in one fixed order whatever the configuration: states in groups
-// of 8, each group's partial accumulated in state order (fma), the groups
-// added in group order (the channel's first wave adds the partials of the
-// other waves, handed over through LDS, after its own). With the same token
-// segment, every configuration and every chunking on block boundaries gives
+// of 4, each group's partial accumulated in state order (fma), the groups
+// added in group order. A wave takes its states in passes of 8: in each pass
+// the lower half scans the first group and the upper half the second, one
+// state of each per step. After a pass the halves trade partials so that each
+// lane holds both groups' partials for the tokens it owns, and adds them in
+// order; partials of a channel's other waves are handed over through LDS. With
+// the same T, every configuration and every chunking on block boundaries gives
 // bitwise the same outputs.
+//
+// Two kernels compute it, with the same fp32 operations in the same order:
+//
+//   direct (scan_t{T}_n{NSW}): one workgroup per (request, channel), one wave
+//     per NSW of its states; each wave loads its states' B and C rows straight
+//     into registers, all of a block's loads issued before any is used. Few
+//     instructions stand between a launch and its first result, which is what
+//     a small batch (a few thousand channels: latency bound) needs.
+//   staged (scan_t{T}_n{NSW}_w{W}_c{CPW}): a workgroup holds CPW channels of
+//     one (request, group), with W waves of NSW states each. The channels of a
+//     group share B and C, so the workgroup stages a block's B and C rows in
+//     LDS once, W * NSW states at a time (a round; d_state above that takes
+//     several rounds), and each wave reads the rows of the state it is working
+//     on just before it needs them, with the carried states and decay rates
+//     kept in LDS. Few registers are live, so four waves fit on each SIMD, and
+//     the B/C traffic falls by CPW: what a large batch (throughput bound)
+//     needs.
 //
 // Invalid tokens (past the end of a ragged last block) get Delta = 0, u = 0
 // and B = C = 0: their decay is exp2(0) = 1 and their input 0, the identity
@@ -75,9 +86,13 @@ namespace ssu {
 namespace {
 
 constexpr int kLanes = 64;
+constexpr int kHalf = 32;
 constexpr int kMaxStates = 64;
-constexpr int kGroup = 8;  // states per partial sum of y
+constexpr int kGroup = 4;          // states per partial sum of y
+constexpr int kPass = 2 * kGroup;  // states per pass of a wave: a group per half
 constexpr float kLog2e = 1.44269504088896340736f;
+
+using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
 struct ScanParams {
     const uint16_t *u, *delta, *B, *C;
@@ -112,114 +127,155 @@ __device__ __forceinline__ uint16_t f32_to_io(float f)
     }
 }
 
-// Tokens tok .. tok+SEG-1 of a row, packed two per word. FAST: all of them
-// lie before t1 and the row is aligned for one vector load. Otherwise each is
-// read from an address clamped into [0, t1) (always valid) and tokens at or
-// past t1 read as 0; the loads stay unconditional, so they issue back to back.
-template <int SEG, bool FAST>
-__device__ __forceinline__ void load_seg(const uint16_t *row, int64_t tok, int64_t t1, uint32_t (&w)[(SEG + 1) / 2])
+// Tokens tok .. tok+N-1 of a row, packed two per word. FAST: all of them lie
+// before t1 and the row is aligned for vector loads. Otherwise each is read
+// from an address clamped into [0, t1) (always valid) and tokens at or past t1
+// read as 0; the loads stay unconditional, so they issue back to back.
+template <int N, bool FAST>
+__device__ __forceinline__ void load_seg(const uint16_t *row, int64_t tok, int64_t t1, uint32_t (&w)[(N + 1) / 2])
 {
     if constexpr (FAST) {
         const uint16_t *p = row + tok;
-        if constexpr (SEG == 8) {
-            const auto x = *reinterpret_cast<const uint32_t __attribute__((ext_vector_type(4))) *>(p);
-            w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
-        } else if constexpr (SEG == 4) {
+        if constexpr (N >= 8) {
+#pragma unroll
+            for (int q = 0; q < N / 8; ++q) {
+                const u32x4 x = *reinterpret_cast<const u32x4 *>(p + 8 * q);
+                w[4 * q] = x.x, w[4 * q + 1] = x.y, w[4 * q + 2] = x.z, w[4 * q + 3] = x.w;
+            }
+        } else if constexpr (N == 4) {
             const auto x = *reinterpret_cast<const u32x2 *>(p);
             w[0] = x.x, w[1] = x.y;
-        } else if constexpr (SEG == 2) {
+        } else if constexpr (N == 2) {
             w[0] = *reinterpret_cast<const uint32_t *>(p);
         } else {
             w[0] = *p;
         }
     } else {
-        uint32_t v[SEG];
+        uint32_t v[N];
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) {
+        for (int j = 0; j < N; ++j) {
             const int64_t t = tok + j;
             const uint32_t x = row[t < t1 ? t : t1 - 1];
             v[j] = t < t1 ? x : 0u;
         }
 #pragma unroll
-        for (int k = 0; k < (SEG + 1) / 2; ++k)
-            w[k] = v[2 * k] | ((2 * k + 1 < SEG) ? (v[2 * k + 1] << 16) : 0u);
+        for (int k = 0; k < (N + 1) / 2; ++k)
+            w[k] = v[2 * k] | ((2 * k + 1 < N) ? (v[2 * k + 1] << 16) : 0u);
     }
 }
 
-// Store tokens tok .. tok+SEG-1 of a row (those before t1).
-template <int SEG, bool FAST>
-__device__ __forceinline__ void store_seg(uint16_t *row, int64_t tok, int64_t t1, const uint16_t (&v)[SEG])
+// Store tokens tok .. tok+N-1 of a row (those before t1).
+template <int N, bool FAST>
+__device__ __forceinline__ void store_seg(uint16_t *row, int64_t tok, int64_t t1, const uint16_t (&v)[N])
 {
     if constexpr (FAST) {
         uint16_t *p = row + tok;
-        uint32_t w[(SEG + 1) / 2];
+        uint32_t w[(N + 1) / 2];
 #pragma unroll
-        for (int k = 0; k < (SEG + 1) / 2; ++k)
-            w[k] = v[2 * k] | ((2 * k + 1 < SEG) ? (static_cast<uint32_t>(v[2 * k + 1]) << 16) : 0u);
-        if constexpr (SEG == 8) {
-            uint32_t __attribute__((ext_vector_type(4))) x = {w[0], w[1], w[2], w[3]};
-            *reinterpret_cast<uint32_t __attribute__((ext_vector_type(4))) *>(p) = x;
-        } else if constexpr (SEG == 4) {
+        for (int k = 0; k < (N + 1) / 2; ++k)
+            w[k] = v[2 * k] | ((2 * k + 1 < N) ? (static_cast<uint32_t>(v[2 * k + 1]) << 16) : 0u);
+        if constexpr (N == 8) {
+            u32x4 x = {w[0], w[1], w[2], w[3]};
+            *reinterpret_cast<u32x4 *>(p) = x;
+        } else if constexpr (N == 4) {
             u32x2 x = {w[0], w[1]};
             *reinterpret_cast<u32x2 *>(p) = x;
-        } else if constexpr (SEG == 2) {
+        } else if constexpr (N == 2) {
             *reinterpret_cast<uint32_t *>(p) = w[0];
         } else {
             *p = v[0];
         }
     } else {
 #pragma unroll
-        for (int j = 0; j < SEG; ++j)
+        for (int j = 0; j < N; ++j)
             if (tok + j < t1)
                 row[tok + j] = v[j];
     }
 }
 
-template <int SEG>
-__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(SEG + 1) / 2], int j)
+// N tokens of a row staged in LDS (16-bit values, packed two per word).
+template <int N>
+__device__ __forceinline__ void lds_seg(const uint16_t *p, uint32_t (&w)[(N + 1) / 2])
+{
+    if constexpr (N >= 8) {
+#pragma unroll
+        for (int q = 0; q < N / 8; ++q) {
+            const u32x4 x = *reinterpret_cast<const u32x4 *>(p + 8 * q);
+            w[4 * q] = x.x, w[4 * q + 1] = x.y, w[4 * q + 2] = x.z, w[4 * q + 3] = x.w;
+        }
+    } else if constexpr (N == 4) {
+        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
+        w[0] = x.x, w[1] = x.y;
+    } else {
+        w[0] = *reinterpret_cast<const uint32_t *>(p);
+    }
+}
+
+template <int N>
+__device__ __forceinline__ uint32_t half_of(const uint32_t (&w)[(N + 1) / 2], int j)
 {
     return (j & 1) ? (w[j >> 1] >> 16) : (w[j >> 1] & 0xffffu);
 }
 
-// The 64-lane inclusive scan of the lanes' maps (P, Q), for two states at
-// once or for one, as in-place DPP operations: at each level every lane
-// combines its map with the map of the lane that the DPP control names (the
-// earlier tokens), Q += P * Q_src, then P *= P_src. A lane without a source
-// (shifted out of its row, or in a row the row mask leaves out) is not
-// written, which is the same as combining with the identity map (1, 0). The
-// levels: shifts 1, 2, 4, 8 within rows of 16, then lane 15 of each row into
-// the next (rows 1, 3) and lane 31 into rows 2, 3. A DPP read needs two wait
-// states after a VALU write of its source register: the leading s_nop 1
-// covers the caller's last writes; between levels, two interleaved states
-// already put three instructions between a write and its next DPP read, and
-// one state needs an s_nop 0.
-#define SSU_SCAN_LEVEL2(CTL)                                        \
-    "v_fmac_f32_dpp %0, %0, %2 " CTL "\n\t"                         \
-    "v_fmac_f32_dpp %1, %1, %3 " CTL "\n\t"                         \
-    "v_mul_f32_dpp %2, %2, %2 " CTL "\n\t"                          \
+// The 32-lane inclusive scan of the lanes' maps (P, Q) in each half of the
+// wave, for two states at once or for one, as in-place DPP operations: at each
+// level every lane combines its map with the map of the lane that the DPP
+// control names (the earlier tokens), Q += P * Q_src, then P *= P_src. A lane
+// without a source (shifted out of its row, or in a row the row mask leaves
+// out) is not written, which is the same as combining with the identity map
+// (1, 0). The levels: shifts 1, 2, 4, 8 within rows of 16, then lane 15 of
+// each row into the next row, for rows 1 and 3 only (lane 15 into row 1,
+// lane 47 into row 3), so that nothing crosses from one half into the other.
+// A DPP read needs two wait states after a VALU write of its source register:
+// the leading s_nop 1 covers the caller's last writes; between levels, two
+// interleaved states already put three instructions between a write and its
+// next DPP read, and one state needs an s_nop 0.
+#define SSU_SCAN_LEVEL2(CTL)                \
+    "v_fmac_f32_dpp %0, %0, %2 " CTL "\n\t" \
+    "v_fmac_f32_dpp %1, %1, %3 " CTL "\n\t" \
+    "v_mul_f32_dpp %2, %2, %2 " CTL "\n\t"  \
     "v_mul_f32_dpp %3, %3, %3 " CTL "\n\t"
-#define SSU_SCAN_TREE2(Q0, Q1, P0, P1)                                                  \
-    asm("s_nop 1\n\t" SSU_SCAN_LEVEL2("row_shr:1 row_mask:0xf bank_mask:0xf")          \
-            SSU_SCAN_LEVEL2("row_shr:2 row_mask:0xf bank_mask:0xf")                      \
-                SSU_SCAN_LEVEL2("row_shr:4 row_mask:0xf bank_mask:0xf")                  \
-                    SSU_SCAN_LEVEL2("row_shr:8 row_mask:0xf bank_mask:0xf")              \
-                        SSU_SCAN_LEVEL2("row_bcast:15 row_mask:0xa bank_mask:0xf")       \
-                            SSU_SCAN_LEVEL2("row_bcast:31 row_mask:0xc bank_mask:0xf")   \
+#define SSU_SCAN_TREE2(Q0, Q1, P0, P1)                                              \
+    asm("s_nop 1\n\t" SSU_SCAN_LEVEL2("row_shr:1 row_mask:0xf bank_mask:0xf")      \
+            SSU_SCAN_LEVEL2("row_shr:2 row_mask:0xf bank_mask:0xf")                  \
+                SSU_SCAN_LEVEL2("row_shr:4 row_mask:0xf bank_mask:0xf")              \
+                    SSU_SCAN_LEVEL2("row_shr:8 row_mask:0xf bank_mask:0xf")          \
+                        SSU_SCAN_LEVEL2("row_bcast:15 row_mask:0xa bank_mask:0xf")   \
         : "+v"(Q0), "+v"(Q1), "+v"(P0), "+v"(P1))
-#define SSU_SCAN_LEVEL1(CTL)                                        \
-    "v_fmac_f32_dpp %0, %0, %1 " CTL "\n\t"                         \
+#define SSU_SCAN_LEVEL1(CTL)                \
+    "v_fmac_f32_dpp %0, %0, %1 " CTL "\n\t" \
     "v_mul_f32_dpp %1, %1, %1 " CTL "\n\t"
-#define SSU_SCAN_TREE1(Q0, P0)                                                                      \
-    asm("s_nop 1\n\t" SSU_SCAN_LEVEL1("row_shr:1 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"          \
-            SSU_SCAN_LEVEL1("row_shr:2 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                      \
-                SSU_SCAN_LEVEL1("row_shr:4 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                  \
-                    SSU_SCAN_LEVEL1("row_shr:8 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"              \
-                        SSU_SCAN_LEVEL1("row_bcast:15 row_mask:0xa bank_mask:0xf") "s_nop 0\n\t"       \
-                            SSU_SCAN_LEVEL1("row_bcast:31 row_mask:0xc bank_mask:0xf")                   \
-        : "+v"(Q0), "+v"(P0))
+#define SSU_SCAN_TREE1_TEXT                                                                    \
+    "s_nop 1\n\t" SSU_SCAN_LEVEL1("row_shr:1 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"            \
+        SSU_SCAN_LEVEL1("row_shr:2 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                        \
+            SSU_SCAN_LEVEL1("row_shr:4 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                    \
+                SSU_SCAN_LEVEL1("row_shr:8 row_mask:0xf bank_mask:0xf") "s_nop 0\n\t"                \
+                    SSU_SCAN_LEVEL1("row_bcast:15 row_mask:0xa bank_mask:0xf")
+#define SSU_SCAN_TREE1(Q0, P0) asm(SSU_SCAN_TREE1_TEXT : "+v"(Q0), "+v"(P0))
+// The same, and no memory access moves across it (the caller's loads after
+// it stay after it, so their registers are not live during the scan).
+#define SSU_SCAN_TREE1_FENCED(Q0, P0) asm(SSU_SCAN_TREE1_TEXT : "+v"(Q0), "+v"(P0) : : "memory")
 
 // DPP control of the one-lane shift of the whole wave (GFX9 encoding).
 constexpr int kWaveShr1 = 0x138;
+
+// v_permlane32_swap: lanes 32..63 of x trade places with lanes 0..31 of y.
+// With x and y the same per-lane values, the lower half keeps its own value
+// in x and receives the upper half's in y; the upper half receives the lower
+// half's in x and keeps its own in y.
+__device__ __forceinline__ void swap_halves(float &x, float &y)
+{
+    const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(x), __float_as_uint(y), false, false);
+    x = __uint_as_float(r[0]);
+    y = __uint_as_float(r[1]);
+}
+
+// The value of the last lane of this lane's half (lane 31 or lane 63), in
+// every lane of the half.
+__device__ __forceinline__ float half_last(float v, int lane)
+{
+    return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & kHalf) | (kHalf - 1)) << 2, __float_as_int(v)));
+}
 
 constexpr float kLn2Hi = 0.693147182464599609375f;      // (float)ln 2
 constexpr float kLn2Lo = -1.904654323148236e-09f;       // ln 2 - kLn2Hi
@@ -252,309 +308,333 @@ __device__ __forceinline__ float softplus_f32(float v)
     return fmaf(sv, q, v <= 0.0f ? 0.0f : v);
 }
 
-// One state's scan over one block of 64 * SEG tokens, in this lane's SEG
-// tokens: dl their step sizes, du = dl * u their inputs, dls = the sum of dl
-// (in token order), Bw and Cw the state's B and C bits, A2 = A * log2(e), h
-// the carried state (wave uniform). Adds the state's h_j * C_j to yy[j] and
-// returns the carried state after the block.
+// One state per half over one block of 32 * T tokens, in this lane's segment
+// of T tokens: dl their step sizes, du = dl * u their inputs, dls = the sum of
+// dl (in token order), Bw and Cw the state's B and C bits, A2 = A * log2(e), h
+// the carried state (uniform over the half), first_upper: this lane is
+// lane 32. Adds the state's h_j * C_j to yy[j] and returns the lane's end
+// state e (the half's last lane holds the carried state after the block).
 //   1. the lane's whole map: decay exp2(A2 * dls) (the product of its
 //      tokens' decays in one exponential), and the state Q reached from 0;
-//   2. the 64-lane inclusive scan of the maps;
+//   2. the 32-lane inclusive scan of the maps;
 //   3. the lane's end state e (the map applied to h) and start state g (e
-//      shifted one lane up, lane 0 taking h); the lane's tokens are replayed
-//      from g, h_j = a_j h_{j-1} + b_j, and after its last token the state
-//      is e;
-//   4. lane 63's e is the carried state.
-template <bool F16, int SEG>
-__device__ __forceinline__ float scan_state(const float (&dl)[SEG], const float (&du)[SEG], float dls, float A2,
-                                            const uint32_t (&Bw)[(SEG + 1) / 2], const uint32_t (&Cw)[(SEG + 1) / 2],
-                                            float h, float (&yy)[SEG])
+//      shifted one lane up, the half's first lane taking h); the lane's tokens
+//      are replayed from g, h_j = a_j h_{j-1} + b_j, and after its last token
+//      the state is e.
+// after_scan() is called once the step no longer needs A2, Bw and h (after
+// the 32-lane scan, which no memory access crosses when FENCED): a caller
+// that reads the next step's operands from LDS there has them in flight
+// while this step's tokens are replayed, in the registers this step's have
+// just freed.
+template <bool F16, int T, bool FENCED = false, typename AfterScan>
+__device__ __forceinline__ float scan_step(const float (&dl)[T], const float (&du)[T], float dls, float A2,
+                                           const uint32_t (&Bw)[(T + 1) / 2], const uint32_t (&Cw)[(T + 1) / 2],
+                                           float h, bool first_upper, float (&yy)[T], AfterScan after_scan)
 {
-    float a[SEG], b[SEG];
+    float a[T], b[T];
 #pragma unroll
-    for (int j = 0; j < SEG; ++j) {
+    for (int j = 0; j < T; ++j) {
         a[j] = __builtin_amdgcn_exp2f(dl[j] * A2);
-        b[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(Bw, j)), 0.0f);
+        b[j] = fmaf(du[j], io_to_f32<F16>(half_of<T>(Bw, j)), 0.0f);
     }
     float Q = b[0];
 #pragma unroll
-    for (int j = 1; j < SEG; ++j)
+    for (int j = 1; j < T; ++j)
         Q = fmaf(a[j], Q, b[j]);
     float P = __builtin_amdgcn_exp2f(dls * A2);
-    SSU_SCAN_TREE1(Q, P);
+    if constexpr (FENCED)
+        SSU_SCAN_TREE1_FENCED(Q, P);
+    else
+        SSU_SCAN_TREE1(Q, P);
     const float e = fmaf(P, h, Q);
-    const float g = __int_as_float(
+    float g = __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(h), __float_as_int(e), kWaveShr1, 0xf, 0xf, false));
+    g = first_upper ? h : g;
+    if constexpr (FENCED)
+        asm volatile("" : "+v"(g) : : "memory");  // h is dead before after_scan's reads
+    after_scan();
     float hj = g;
 #pragma unroll
-    for (int j = 0; j < SEG - 1; ++j) {
+    for (int j = 0; j < T - 1; ++j) {
         hj = fmaf(a[j], hj, b[j]);
-        yy[j] = fmaf(hj, io_to_f32<F16>(half_of<SEG>(Cw, j)), yy[j]);
+        yy[j] = fmaf(hj, io_to_f32<F16>(half_of<T>(Cw, j)), yy[j]);
     }
-    yy[SEG - 1] = fmaf(e, io_to_f32<F16>(half_of<SEG>(Cw, SEG - 1)), yy[SEG - 1]);
-    return __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e), kLanes - 1));
+    yy[T - 1] = fmaf(e, io_to_f32<F16>(half_of<T>(Cw, T - 1)), yy[T - 1]);
+    return e;
 }
 
-// The same for two states n, n+1 at once (their dependent steps interleave),
-// with the same operations per state, so the same bits. y gets state n's
-// terms before state n+1's.
-template <bool F16, int SEG>
-__device__ __forceinline__ void scan_state2(const float (&dl)[SEG], const float (&du)[SEG], float dls, float A20,
-                                            float A21, const uint32_t (&B0)[(SEG + 1) / 2],
-                                            const uint32_t (&B1)[(SEG + 1) / 2], const uint32_t (&C0)[(SEG + 1) / 2],
-                                            const uint32_t (&C1)[(SEG + 1) / 2], float &h0, float &h1,
-                                            float (&yy)[SEG])
+// The same for two states per half at once (their dependent steps
+// interleave), with the same operations per state, so the same bits. y gets
+// the first state's terms before the second's.
+template <bool F16, int T>
+__device__ __forceinline__ void scan_step2(const float (&dl)[T], const float (&du)[T], float dls, float A20,
+                                           float A21, const uint32_t (&B0)[(T + 1) / 2],
+                                           const uint32_t (&B1)[(T + 1) / 2], const uint32_t (&C0)[(T + 1) / 2],
+                                           const uint32_t (&C1)[(T + 1) / 2], float h0, float h1, bool first_upper,
+                                           float (&yy)[T], float &e0, float &e1)
 {
-    float a0[SEG], b0[SEG], a1[SEG], b1[SEG];
+    float a0[T], b0[T], a1[T], b1[T];
 #pragma unroll
-    for (int j = 0; j < SEG; ++j) {
+    for (int j = 0; j < T; ++j) {
         a0[j] = __builtin_amdgcn_exp2f(dl[j] * A20);
         a1[j] = __builtin_amdgcn_exp2f(dl[j] * A21);
-        b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B0, j)), 0.0f);
-        b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<SEG>(B1, j)), 0.0f);
+        b0[j] = fmaf(du[j], io_to_f32<F16>(half_of<T>(B0, j)), 0.0f);
+        b1[j] = fmaf(du[j], io_to_f32<F16>(half_of<T>(B1, j)), 0.0f);
     }
     float Q0 = b0[0], Q1 = b1[0];
 #pragma unroll
-    for (int j = 1; j < SEG; ++j) {
+    for (int j = 1; j < T; ++j) {
         Q0 = fmaf(a0[j], Q0, b0[j]);
         Q1 = fmaf(a1[j], Q1, b1[j]);
     }
     float P0 = __builtin_amdgcn_exp2f(dls * A20), P1 = __builtin_amdgcn_exp2f(dls * A21);
     SSU_SCAN_TREE2(Q0, Q1, P0, P1);
-    const float e0 = fmaf(P0, h0, Q0), e1 = fmaf(P1, h1, Q1);
-    const float g0 = __int_as_float(
+    e0 = fmaf(P0, h0, Q0);
+    e1 = fmaf(P1, h1, Q1);
+    float g0 = __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(h0), __float_as_int(e0), kWaveShr1, 0xf, 0xf, false));
-    const float g1 = __int_as_float(
+    float g1 = __int_as_float(
         __builtin_amdgcn_update_dpp(__float_as_int(h1), __float_as_int(e1), kWaveShr1, 0xf, 0xf, false));
+    g0 = first_upper ? h0 : g0;
+    g1 = first_upper ? h1 : g1;
     float hj0 = g0, hj1 = g1;
 #pragma unroll
-    for (int j = 0; j < SEG - 1; ++j) {
+    for (int j = 0; j < T - 1; ++j) {
         hj0 = fmaf(a0[j], hj0, b0[j]);
         hj1 = fmaf(a1[j], hj1, b1[j]);
-        yy[j] = fmaf(hj0, io_to_f32<F16>(half_of<SEG>(C0, j)), yy[j]);
-        yy[j] = fmaf(hj1, io_to_f32<F16>(half_of<SEG>(C1, j)), yy[j]);
+        yy[j] = fmaf(hj0, io_to_f32<F16>(half_of<T>(C0, j)), yy[j]);
+        yy[j] = fmaf(hj1, io_to_f32<F16>(half_of<T>(C1, j)), yy[j]);
     }
-    yy[SEG - 1] = fmaf(e0, io_to_f32<F16>(half_of<SEG>(C0, SEG - 1)), yy[SEG - 1]);
-    yy[SEG - 1] = fmaf(e1, io_to_f32<F16>(half_of<SEG>(C1, SEG - 1)), yy[SEG - 1]);
-    h0 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e0), kLanes - 1));
-    h1 = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(e1), kLanes - 1));
+    yy[T - 1] = fmaf(e0, io_to_f32<F16>(half_of<T>(C0, T - 1)), yy[T - 1]);
+    yy[T - 1] = fmaf(e1, io_to_f32<F16>(half_of<T>(C1, T - 1)), yy[T - 1]);
 }
 
-// The sum of a lane's step sizes, in token order.
-template <int SEG>
-__device__ __forceinline__ float step_sum(const float (&dl)[SEG])
+// The sum of a segment's step sizes, in token order.
+template <int T>
+__device__ __forceinline__ float step_sum(const float (&dl)[T])
 {
     float s = dl[0];
 #pragma unroll
-    for (int j = 1; j < SEG; ++j)
+    for (int j = 1; j < T; ++j)
         s += dl[j];
     return s;
 }
 
-// One wave's share of one (request, channel): its 16 states' carried values
-// and decay rates (wave-uniform) and the rows it reads and writes.
-template <bool F16, int SEG, int NSW, bool FULL>
-struct Chan {
-    static constexpr int BLOCK = kLanes * SEG;
-    static constexpr int WORDS = (SEG + 1) / 2;
-
-    const uint16_t *u_row, *dl_row, *B_row, *C_row;
-    uint16_t *o_row;
-    int64_t B_n, C_n;
-    float bias, Dd;
-    int ns, lane;
-    bool softplus;
-    float h0[NSW], A2[NSW];
-
-    static constexpr int GROUPS = NSW / kGroup;
-
-    // One block of 64 * SEG tokens starting at blk: the scan of every state
-    // of this wave; yg returns the partial of y over each group of 8 states.
-    // FAST: the block lies inside the chunk and every row is aligned for
-    // vector access, so all loads are unconditional vector loads.
-    template <bool FAST>
-    __device__ __forceinline__ void block(int64_t blk, int64_t t1, float (&yg)[GROUPS][SEG], uint32_t (&uw)[WORDS])
-    {
-        const int64_t tok = blk + lane * SEG;
-
-        // every load of the block first, so that one wait covers them all
-        uint32_t dw[WORDS], Bw[NSW][WORDS], Cw[NSW][WORDS];
-        load_seg<SEG, FAST>(u_row, tok, t1, uw);
-        load_seg<SEG, FAST>(dl_row, tok, t1, dw);
+// Step sizes Delta and inputs Delta u of the T/2 tokens this lane owns (from
+// their delta and u bits dw, uw; tokens at or past t1: the identity), traded
+// between the halves into the whole segment's dl[T], du[T].
+template <bool F16, int T, bool FAST>
+__device__ __forceinline__ void segment_steps(const uint32_t (&dw)[(T / 2 + 1) / 2],
+                                              const uint32_t (&uw)[(T / 2 + 1) / 2], float bias, bool softplus,
+                                              int64_t own, int64_t t1, float (&dl)[T], float (&du)[T])
+{
+    constexpr int TH = T / 2;
 #pragma unroll
-        for (int n = 0; n < NSW; ++n) {
-            const int r = FULL ? n : min(n, ns - 1);  // rows past dstate: read a valid row, zeroed below
-            load_seg<SEG, FAST>(B_row + r * B_n, tok, t1, Bw[n]);
-            load_seg<SEG, FAST>(C_row + r * C_n, tok, t1, Cw[n]);
-        }
-        if constexpr (!FULL) {
-            // states past dstate: B = C = 0 (and A2 = 0), the identity map and a
-            // zero contribution
-#pragma unroll
-            for (int n = 0; n < NSW; ++n)
-#pragma unroll
-                for (int k = 0; k < WORDS; ++k) {
-                    Bw[n][k] = n < ns ? Bw[n][k] : 0u;
-                    Cw[n][k] = n < ns ? Cw[n][k] : 0u;
-                }
-        }
-
-        // step sizes Delta_j and inputs Delta_j u_j; invalid tokens: identity
-        float dl[SEG], du[SEG];
-#pragma unroll
-        for (int j = 0; j < SEG; ++j) {
-            // (the f16 conversions fold into mixed-precision fmas; x * 1 + bias
-            // and sv * u + 0 round exactly as x + bias and sv * u)
-            const float v = fmaf(io_to_f32<F16>(half_of<SEG>(dw, j)), 1.0f, bias);
-            float sv = softplus ? softplus_f32(v) : v;
-            if (!FAST)
-                sv = tok + j < t1 ? sv : 0.0f;
-            dl[j] = sv;
-            du[j] = fmaf(sv, io_to_f32<F16>(half_of<SEG>(uw, j)), 0.0f);
-        }
-#pragma unroll
-        for (int gi = 0; gi < GROUPS; ++gi)
-#pragma unroll
-            for (int j = 0; j < SEG; ++j)
-                yg[gi][j] = 0.0f;
-
-        const float dls = step_sum<SEG>(dl);
-#pragma unroll
-        for (int n = 0; n < NSW; n += 2)
-            scan_state2<F16, SEG>(dl, du, dls, A2[n], A2[n + 1], Bw[n], Bw[n + 1], Cw[n], Cw[n + 1], h0[n],
-                                  h0[n + 1], yg[n / kGroup]);
+    for (int j = 0; j < TH; ++j) {
+        // (the f16 conversions fold into mixed-precision fmas; x * 1 + bias
+        // and sv * u + 0 round exactly as x + bias and sv * u)
+        const float v = fmaf(io_to_f32<F16>(half_of<TH>(dw, j)), 1.0f, bias);
+        float sv = softplus ? softplus_f32(v) : v;
+        if (!FAST)
+            sv = own + j < t1 ? sv : 0.0f;
+        float x = sv, y = sv;
+        swap_halves(x, y);
+        dl[j] = x, dl[TH + j] = y;
+        float xu = fmaf(sv, io_to_f32<F16>(half_of<TH>(uw, j)), 0.0f), yu = xu;
+        swap_halves(xu, yu);
+        du[j] = xu, du[TH + j] = yu;
     }
-};
+}
 
-template <bool F16, int SEG, int NSW, int MAXW, bool FULL>
+// After a pass, yy holds the lower group's partial in the lower half and the
+// upper group's in the upper half, over the whole segment. Trade them so
+// that each lane holds both partials of its own T/2 tokens, and add them to
+// y in group order.
+template <int T>
+__device__ __forceinline__ void pass_partials(const float (&yy)[T], float (&lo)[T / 2], float (&hi)[T / 2])
+{
+    constexpr int TH = T / 2;
+#pragma unroll
+    for (int j = 0; j < TH; ++j) {
+        float x = yy[j], z = yy[TH + j];
+        swap_halves(x, z);
+        lo[j] = x, hi[j] = z;
+    }
+}
+
+template <bool F16, int T, int NSW, int MAXW, bool FULL, bool ALLFAST>
 __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const ScanParams p)
 {
-    using Ch = Chan<F16, SEG, NSW, FULL>;
-    constexpr int BLOCK = Ch::BLOCK;
-    constexpr int GROUPS = Ch::GROUPS;
-    // group partials of waves 1 .. W-1
+    constexpr int TH = T / 2, BLOCK = kHalf * T, WT = (T + 1) / 2, WH = (TH + 1) / 2;
+    constexpr int STEPS = NSW / 2;          // states per half of the wave
+    constexpr int GROUPS = NSW / kGroup;
+    // group partials of waves 1 .. W-1, by own token
     __shared__ float ypart[MAXW > 1 ? (MAXW - 1) * GROUPS : 1][MAXW > 1 ? BLOCK : 1];
 
     const int lane = static_cast<int>(threadIdx.x) & (kLanes - 1);
-    const int wave = MAXW > 1 ? static_cast<int>(threadIdx.x) / kLanes : 0;
+    const int li = lane & (kHalf - 1), hl = lane >> 5;
+    const bool first_upper = lane == kHalf;
+    const int wave = MAXW > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kLanes) : 0;
     const int nwaves = MAXW > 1 ? static_cast<int>(blockDim.x) / kLanes : 1;
     const int64_t bd = blockIdx.x;
     const int64_t b = bd / p.dim;
     const int d = static_cast<int>(bd - b * p.dim);
     const int grp = d / p.ch_per_group;
     const int n0 = wave * NSW;
+    const int dstate = p.dstate;
 
-    Ch c;
-    c.lane = lane;
-    c.ns = FULL ? NSW : min(NSW, p.dstate - n0);
-    c.u_row = p.u + b * p.u_b + d * p.u_d;
-    c.dl_row = p.delta + b * p.dl_b + d * p.dl_d;
-    c.B_row = p.B + b * p.B_b + grp * p.B_g + n0 * p.B_n;
-    c.C_row = p.C + b * p.C_b + grp * p.C_g + n0 * p.C_n;
-    c.o_row = p.out + b * p.o_b + d * p.o_d;
-    c.B_n = p.B_n, c.C_n = p.C_n;
-    c.softplus = p.softplus != 0;
-    float *st = p.state + b * p.st_b + d * p.st_d + n0;
+    const uint16_t *const u_row = p.u + b * p.u_b + d * p.u_d;
+    const uint16_t *const dl_row = p.delta + b * p.dl_b + d * p.dl_d;
+    const uint16_t *const B_row = p.B + b * p.B_b + grp * p.B_g;
+    const uint16_t *const C_row = p.C + b * p.C_b + grp * p.C_g;
+    uint16_t *const o_row = p.out + b * p.o_b + d * p.o_d;
+    float *const st = p.state + b * p.st_b + d * p.st_d;
+    const float bias = p.bias ? load_ro(p.bias + d) : 0.0f;
+    const float Dd = p.D ? load_ro(p.D + d) : 0.0f;
+    const bool softplus = p.softplus != 0;
 
-    // wave-uniform per-channel values; the state is written by this kernel,
-    // so it is read with a plain load, never through the read-only path
-    c.bias = p.bias ? load_ro(p.bias + d) : 0.0f;
-    c.Dd = p.D ? load_ro(p.D + d) : 0.0f;
+    // this half's state of step s: n0 + 8 (s / 4) + 4 hl + s % 4; its carried
+    // value (read with a plain load: the state is written by this kernel) and
+    // decay rate A * log2(e), both uniform over the half, read in the first
+    // block after its rows are requested (one memory wait, not two in a row)
+    int row[STEPS];
+    bool live[STEPS];
+    float hv[STEPS], A2[STEPS];
 #pragma unroll
-    for (int n = 0; n < NSW; ++n) {
-        const int r = FULL ? n : min(n, c.ns - 1);
-        const float hv = st[r], av = load_ro(p.A + d * p.A_d + (n0 + r) * p.A_n);
-        c.h0[n] = (FULL || n < c.ns) ? hv : 0.0f;
-        c.A2[n] = (FULL || n < c.ns) ? av * kLog2e : 0.0f;
+    for (int s = 0; s < STEPS; ++s) {
+        const int n = n0 + kPass * (s / kGroup) + kGroup * hl + s % kGroup;
+        live[s] = FULL || n < dstate;
+        row[s] = FULL ? n : min(n, dstate - 1);  // rows past dstate: read a valid row, zeroed below
+        hv[s] = A2[s] = 0.0f;
     }
     const bool vec = p.vec != 0;
 
-    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
-        float yg[GROUPS][SEG];
-        uint32_t uw[Ch::WORDS];
-        const bool fast = vec && blk + BLOCK <= p.t1;
-        if (fast)
-            c.template block<true>(blk, p.t1, yg, uw);
-        else
-            c.template block<false>(blk, p.t1, yg, uw);
+    auto block = [&](int64_t blk, auto fast_tag) {
+        constexpr bool fast = decltype(fast_tag)::value;
+        const int64_t seg = blk + li * T, own = seg + hl * TH;
 
-        // y: the group partials added in group order
-        float y[SEG];
+        // every load of the block first, so that one wait covers them all
+        uint32_t uw[WH], dw[WH], Bw[STEPS][WT], Cw[STEPS][WT];
+        load_seg<TH, fast>(u_row, own, p.t1, uw);
+        load_seg<TH, fast>(dl_row, own, p.t1, dw);
 #pragma unroll
-        for (int j = 0; j < SEG; ++j) {
-            y[j] = yg[0][j];
+        for (int s = 0; s < STEPS; ++s) {
+            load_seg<T, fast>(B_row + row[s] * p.B_n, seg, p.t1, Bw[s]);
+            load_seg<T, fast>(C_row + row[s] * p.C_n, seg, p.t1, Cw[s]);
+        }
+        if (blk == p.t0) {
 #pragma unroll
-            for (int gi = 1; gi < GROUPS; ++gi)
-                y[j] += yg[gi][j];
+            for (int s = 0; s < STEPS; ++s) {
+                const float h = st[row[s]], av = load_ro(p.A + d * p.A_d + row[s] * p.A_n);
+                hv[s] = live[s] ? h : 0.0f;
+                A2[s] = live[s] ? av * kLog2e : 0.0f;
+            }
+        }
+        if constexpr (!FULL) {
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s)
+#pragma unroll
+                for (int k = 0; k < WT; ++k) {
+                    Bw[s][k] = live[s] ? Bw[s][k] : 0u;
+                    Cw[s][k] = live[s] ? Cw[s][k] : 0u;
+                }
+        }
+
+        float dl[T], du[T];
+        segment_steps<F16, T, fast>(dw, uw, bias, softplus, own, p.t1, dl, du);
+        const float dls = step_sum<T>(dl);
+
+        // y of the tokens this lane owns: starting from -0 (which adds exactly),
+        // the groups' partials added in group order
+        float y[TH];
+#pragma unroll
+        for (int j = 0; j < TH; ++j)
+            y[j] = -0.0f;
+#pragma unroll
+        for (int ps = 0; ps < STEPS; ps += kGroup) {
+            float yy[T];
+#pragma unroll
+            for (int j = 0; j < T; ++j)
+                yy[j] = 0.0f;
+            if constexpr (NSW == 8 && (T <= 8 || ALLFAST)) {  // (the ragged-block code leaves no room for two at T = 16)
+#pragma unroll
+                for (int s = ps; s < ps + kGroup; s += 2) {
+                    float e0, e1;
+                    scan_step2<F16, T>(dl, du, dls, A2[s], A2[s + 1], Bw[s], Bw[s + 1], Cw[s], Cw[s + 1], hv[s],
+                                       hv[s + 1], first_upper, yy, e0, e1);
+                    hv[s] = half_last(e0, lane);
+                    hv[s + 1] = half_last(e1, lane);
+                }
+            } else {
+#pragma unroll
+                for (int s = ps; s < ps + kGroup; ++s) {
+                    const float e =
+                        scan_step<F16, T>(dl, du, dls, A2[s], Bw[s], Cw[s], hv[s], first_upper, yy, [] {});
+                    hv[s] = half_last(e, lane);
+                }
+            }
+            float lo[TH], hi[TH];
+            pass_partials<T>(yy, lo, hi);
+            const int gi = 2 * (ps / kGroup);  // the pass's first group within the wave
+#pragma unroll
+            for (int j = 0; j < TH; ++j) {
+                if (wave == 0) {
+                    y[j] = (y[j] + lo[j]) + hi[j];
+                } else if constexpr (MAXW > 1) {
+                    ypart[(wave - 1) * GROUPS + gi][li * T + hl * TH + j] = lo[j];
+                    ypart[(wave - 1) * GROUPS + gi + 1][li * T + hl * TH + j] = hi[j];
+                }
+            }
         }
         if constexpr (MAXW > 1) {
-            if (wave > 0) {
-#pragma unroll
-                for (int gi = 0; gi < GROUPS; ++gi)
-#pragma unroll
-                    for (int j = 0; j < SEG; ++j)
-                        ypart[(wave - 1) * GROUPS + gi][lane * SEG + j] = yg[gi][j];
-            }
             __syncthreads();
             if (wave == 0) {
                 for (int k = 0; k < (nwaves - 1) * GROUPS; ++k)
 #pragma unroll
-                    for (int j = 0; j < SEG; ++j)
-                        y[j] += ypart[k][lane * SEG + j];
+                    for (int j = 0; j < TH; ++j)
+                        y[j] += ypart[k][li * T + hl * TH + j];
             }
             __syncthreads();
         }
         if (wave == 0) {
-            uint16_t o[SEG];
+            uint16_t o[TH];
 #pragma unroll
-            for (int j = 0; j < SEG; ++j)
-                o[j] = f32_to_io<F16>(fmaf(c.Dd, io_to_f32<F16>(half_of<SEG>(uw, j)), y[j]));
-            if (fast)
-                store_seg<SEG, true>(c.o_row, blk + lane * SEG, p.t1, o);
+            for (int j = 0; j < TH; ++j)
+                o[j] = f32_to_io<F16>(fmaf(Dd, io_to_f32<F16>(half_of<TH>(uw, j)), y[j]));
+            store_seg<TH, fast>(o_row, own, p.t1, o);
+        }
+    };
+    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+        if constexpr (ALLFAST) {
+            block(blk, std::true_type{});
+        } else {
+            if (vec && blk + BLOCK <= p.t1)
+                block(blk, std::true_type{});
             else
-                store_seg<SEG, false>(c.o_row, blk + lane * SEG, p.t1, o);
+                block(blk, std::false_type{});
         }
     }
 
-    // final state: lane n of the wave writes state n0 + n
-    float mine = 0.0f;
+    // final states: the first lane of each half writes its half's
+    if (li == 0) {
 #pragma unroll
-    for (int n = 0; n < NSW; ++n)
-        mine = lane == n ? c.h0[n] : mine;
-    if (lane < c.ns)
-        st[lane] = mine;
-}
-
-
-using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
-
-// SEG tokens of a row staged in LDS (16-bit values, packed two per word).
-template <int SEG>
-__device__ __forceinline__ void lds_seg(const uint16_t *p, uint32_t (&w)[(SEG + 1) / 2])
-{
-    if constexpr (SEG == 8) {
-        const u32x4 x = *reinterpret_cast<const u32x4 *>(p);
-        w[0] = x.x, w[1] = x.y, w[2] = x.z, w[3] = x.w;
-    } else if constexpr (SEG == 4) {
-        const u32x2 x = *reinterpret_cast<const u32x2 *>(p);
-        w[0] = x.x, w[1] = x.y;
-    } else if constexpr (SEG == 2) {
-        w[0] = *reinterpret_cast<const uint32_t *>(p);
-    } else {
-        w[0] = *p;
+        for (int s = 0; s < STEPS; ++s)
+            if (live[s])
+                st[row[s]] = hv[s];
     }
 }
 
 // Layout of one workgroup's LDS (dynamic, 16-byte aligned):
 //   sBC [2 * RS][BLOCK] u16      the round's B rows, then its C rows;
-//   sY  [W - 1][GROUPS][CPW][BLOCK] f32  partials of y that waves 1 .. W-1
-//                                        of each channel hand to wave 0;
+//   sY  [W - 1][GROUPS][CPW][BLOCK] f32  partials of y (by own token) that
+//                                        waves 1 .. W-1 of each channel hand
+//                                        to wave 0;
 //   sH  [CPW][rounds * RS] f32   the carried states (0 past d_state);
-//   sA  [CPW][rounds * RS] f32   A * log2(e) (0 past d_state).
-template <int SEG, int NSW, int W, int CPW>
+//   sA  [CPW][rounds * RS] f32   A * log2(e) (0 past d_state);
+//   16 bytes of padding (read, never used).
+template <int T, int NSW, int W, int CPW>
 struct ScanShape {
-    static constexpr int BLOCK = kLanes * SEG;
-    static constexpr int WORDS = (SEG + 1) / 2;
+    static constexpr int BLOCK = kHalf * T;
     static constexpr int RS = W * NSW;            // states per round
     static constexpr int GROUPS = NSW / kGroup;
     static constexpr int NT = kLanes * W * CPW;   // threads
@@ -563,15 +643,17 @@ struct ScanShape {
     static constexpr int ITERS = (PIECES + NT - 1) / NT;
     static constexpr size_t BC_BYTES = size_t(2) * RS * BLOCK * 2;
     static constexpr size_t Y_BYTES = size_t(W - 1) * GROUPS * CPW * BLOCK * 4;
-    static size_t lds_bytes(int rounds) { return BC_BYTES + Y_BYTES + size_t(2) * CPW * rounds * RS * 4; }
+    // (+16: a step reads the next state's operands one past the last)
+    static size_t lds_bytes(int rounds) { return BC_BYTES + Y_BYTES + size_t(2) * CPW * rounds * RS * 4 + 16; }
 };
 
-template <bool F16, int SEG, int NSW, int W, int CPW, bool FULL>
-__global__ void __launch_bounds__(kLanes * W * CPW) __attribute__((amdgpu_waves_per_eu(4)))
+template <bool F16, int T, int NSW, int W, int CPW, bool FULL, bool ALLFAST>
+__global__ void __launch_bounds__(kLanes * W * CPW) __attribute__((amdgpu_waves_per_eu(T >= 16 ? 3 : 4)))
 ssu_scan_staged_kernel(const ScanParams p)
 {
-    using S = ScanShape<SEG, NSW, W, CPW>;
-    constexpr int BLOCK = S::BLOCK, WORDS = S::WORDS, RS = S::RS, GROUPS = S::GROUPS, NT = S::NT;
+    using S = ScanShape<T, NSW, W, CPW>;
+    constexpr int TH = T / 2, BLOCK = S::BLOCK, WT = (T + 1) / 2, WH = (TH + 1) / 2;
+    constexpr int RS = S::RS, GROUPS = S::GROUPS, NT = S::NT;
     constexpr bool kAllPieces = S::PIECES % NT == 0;  // every thread stages ITERS pieces
     constexpr bool kSplitRows = kAllPieces && S::ITERS % 2 == 0 && NT % S::CPR == 0;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
@@ -584,7 +666,9 @@ ssu_scan_staged_kernel(const ScanParams p)
 
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & (kLanes - 1);
-    const int wv = tid / kLanes;
+    const int li = lane & (kHalf - 1), hl = lane >> 5;
+    const bool first_upper = lane == kHalf;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kLanes);  // uniform: pointers below stay scalar
     const int c = wv / W;        // channel slot
     const int w = wv - c * W;    // state slice
     const int64_t bd0 = static_cast<int64_t>(blockIdx.x) * CPW;
@@ -603,16 +687,28 @@ ssu_scan_staged_kernel(const ScanParams p)
     const bool softplus = p.softplus != 0;
 
     // carried states into LDS (the state is written by this kernel, so it is
-    // read with plain loads, never through the read-only path)
-    // and the decay rates A * log2(e)
-    for (int i = tid; i < CPW * HP; i += NT) {
-        const int cc = i / HP, n = i - cc * HP;
-        const int nn = FULL ? n : min(n, dstate - 1);
-        const float *st = p.state + b * p.st_b + (d0 + cc) * p.st_d;
-        const float av = load_ro(p.A + (d0 + cc) * p.A_d + nn * p.A_n);
-        sH[i] = (FULL || n < dstate) ? st[nn] : 0.0f;
-        sA[i] = (FULL || n < dstate) ? av * kLog2e : 0.0f;
-    }
+    // read with plain loads, never through the read-only path) and the decay
+    // rates A * log2(e); in the first block, after its staging loads are
+    // requested (one memory wait, not two in a row)
+    auto load_states = [&]() {
+        for (int i = tid; i < CPW * HP; i += NT) {
+            const int cc = i / HP, n = i - cc * HP;
+            const int nn = FULL ? n : min(n, dstate - 1);
+            const float *st = p.state + b * p.st_b + (d0 + cc) * p.st_d;
+            const float av = load_ro(p.A + (d0 + cc) * p.A_d + nn * p.A_n);
+            sH[i] = (FULL || n < dstate) ? st[nn] : 0.0f;
+            sA[i] = (FULL || n < dstate) ? av * kLog2e : 0.0f;
+        }
+    };
+
+    // Byte offset of a thread's staging pieces from the row of the first
+    // thread (rows row0 = tid / CPR, column piece tid % CPR), when the pieces
+    // split evenly; the host keeps RS row strides below 2^30 elements.
+    const uint32_t split_offB = static_cast<uint32_t>(
+        ((tid / S::CPR) * p.B_n + 8 * (tid % S::CPR)) * 2);
+    const uint32_t split_offC = static_cast<uint32_t>(
+        ((tid / S::CPR) * p.C_n + 8 * (tid % S::CPR)) * 2);
+    const int lown = li * T + hl * TH;  // this lane's own tokens, from the block's start
 
     // One block of tokens. FAST: the block lies inside the chunk and every
     // row is aligned for vector access, so every load is an unconditional
@@ -620,26 +716,25 @@ ssu_scan_staged_kernel(const ScanParams p)
     // the chunk and tokens past its end read as 0.
     auto block = [&](int64_t blk, auto fast_tag) {
         constexpr bool fast = decltype(fast_tag)::value;
-        const int64_t tok = blk + lane * SEG;
+        const int64_t own = blk + lown;
 
         // this lane's step sizes and inputs (requested before the staging waits)
-        uint32_t uw[WORDS], dw[WORDS];
-        load_seg<SEG, fast>(u_row, tok, p.t1, uw);
-        load_seg<SEG, fast>(dl_row, tok, p.t1, dw);
-        float dl[SEG], du[SEG], y[SEG], dls = 0.0f;
-
-        // step sizes Delta_j and inputs Delta_j u_j of this lane's tokens
-        // (invalid tokens: the identity), and their sum
-        auto steps = [&]() {
+        uint32_t uw[WH], dw[WH];
+        if constexpr (fast) {
+            load_seg<TH, true>(u_row + blk, lown, 0, uw);
+            load_seg<TH, true>(dl_row + blk, lown, 0, dw);
+        } else {
+            load_seg<TH, false>(u_row, own, p.t1, uw);
+            load_seg<TH, false>(dl_row, own, p.t1, dw);
+        }
+        float dl[T], du[T], y[TH], dls = 0.0f;
 #pragma unroll
-            for (int j = 0; j < SEG; ++j) {
-                const float v = fmaf(io_to_f32<F16>(half_of<SEG>(dw, j)), 1.0f, bias);
-                float sv = softplus ? softplus_f32(v) : v;
-                sv = (fast || tok + j < p.t1) ? sv : 0.0f;
-                dl[j] = sv;
-                du[j] = fmaf(sv, io_to_f32<F16>(half_of<SEG>(uw, j)), 0.0f);
-            }
-            dls = step_sum<SEG>(dl);
+        for (int j = 0; j < TH; ++j)
+            y[j] = -0.0f;
+
+        auto steps = [&]() {
+            segment_steps<F16, T, fast>(dw, uw, bias, softplus, own, p.t1, dl, du);
+            dls = step_sum<T>(dl);
         };
 
         for (int r = 0; r < rounds; ++r) {
@@ -664,12 +759,21 @@ ssu_scan_staged_kernel(const ScanParams p)
                 // the thread's base plus a uniform step.
                 auto split_src = [&](int it, bool &live) -> const uint16_t * {
                     constexpr int RSTEP = NT / S::CPR;
-                    const int row0 = tid / S::CPR, col = tid - row0 * S::CPR;
                     const bool isC = it >= S::ITERS / 2;
-                    const int n = r * RS + row0 + (isC ? it - S::ITERS / 2 : it) * RSTEP;
-                    const int nn = FULL ? n : min(n, dstate - 1);
-                    live = FULL || n < dstate;
-                    return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * col;
+                    const int nb = r * RS + (isC ? it - S::ITERS / 2 : it) * RSTEP;  // the piece's row for row0 = 0
+                    if constexpr (FULL) {
+                        // a uniform row pointer plus the thread's fixed byte offset
+                        live = true;
+                        const uint16_t *rowp = (isC ? Cbase + nb * p.C_n : Bbase + nb * p.B_n) + blk;
+                        return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(rowp) +
+                                                                  (isC ? split_offC : split_offB));
+                    } else {
+                        const int row0 = tid / S::CPR, col = tid - row0 * S::CPR;
+                        const int n = nb + row0;
+                        const int nn = min(n, dstate - 1);
+                        live = n < dstate;
+                        return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * col;
+                    }
                 };
                 bool stepped = false;
                 if constexpr (fast) {
@@ -689,6 +793,8 @@ ssu_scan_staged_kernel(const ScanParams p)
                             }
                         }
                         if (r == 0 && i0 == 0) {
+                            if (blk == p.t0)
+                                load_states();
                             steps();
                             stepped = true;
                         }
@@ -716,53 +822,64 @@ ssu_scan_staged_kernel(const ScanParams p)
                             u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
                     }
                 }
-                if (r == 0 && !stepped)
+                if (r == 0 && !stepped) {
+                    if (blk == p.t0)
+                        load_states();
                     steps();
+                }
             }
             __syncthreads();
 
-            // this wave's states of the round, in groups of 8 and pairs: the
+            // this wave's states of the round, in passes of two groups: the
             // carried values and decay rates come from LDS, the B and C rows
-            // of the pair from the staged block, just before they are used
-            const int sbase = r * RS + w * NSW;
-            const uint16_t *const sB = sBC + (w * NSW) * BLOCK + lane * SEG;
-            const uint16_t *const sC = sBC + (RS + w * NSW) * BLOCK + lane * SEG;
-            float *const hrow = sH + c * HP + sbase;
-            const float *const arow = sA + c * HP + sbase;
+            // from the staged block, just before they are used
+            const int sbase = w * NSW + kGroup * hl;  // this half's first state of the wave's first pass
+            const uint16_t *const sB = sBC + li * T;
+            const uint16_t *const sC = sBC + RS * BLOCK + li * T;
+            float *const hrow = sH + c * HP + r * RS;
+            const float *const arow = sA + c * HP + r * RS;
+#pragma unroll 1
+            for (int ps = 0; ps < NSW; ps += kPass) {
+                float yy[T];
 #pragma unroll
-            for (int gi = 0; gi < GROUPS; ++gi) {
-                float yy[SEG];
-#pragma unroll
-                for (int j = 0; j < SEG; ++j)
+                for (int j = 0; j < T; ++j)
                     yy[j] = 0.0f;
-                // the group's carried states and decay rates, lane k holding
-                // state gi * 8 + k's, read out and written back per state
-                // with lane reads and writes
-                float hg = lane < kGroup ? hrow[gi * kGroup + lane] : 0.0f;
-                const float ag = lane < kGroup ? arow[gi * kGroup + lane] : 0.0f;
+                // a step's carried value, decay rate and B row are read from
+                // LDS while the step before replays its tokens; its C row at
+                // its own start
+                const int n0 = sbase + ps;
+                float hv = hrow[n0], av = arow[n0];
+                uint32_t Bw[WT];
+                lds_seg<T>(sB + n0 * BLOCK, Bw);
 #pragma unroll 1
                 for (int k = 0; k < kGroup; ++k) {
-                    const int n = gi * kGroup + k;
-                    const float hv = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(hg), k));
-                    const float av = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(ag), k));
-                    uint32_t B0[WORDS], C0[WORDS];
-                    lds_seg<SEG>(sB + n * BLOCK, B0);
-                    lds_seg<SEG>(sC + n * BLOCK, C0);
-                    const float hn = scan_state<F16, SEG>(dl, du, dls, av, B0, C0, hv, yy);
-                    hg = lane == k ? hn : hg;
+                    const int n = n0 + k;  // this half's state, within the round
+                    const int nx = n + 1;  // past the pass's last: read, unused (LDS has a padding word)
+                    uint32_t Cw[WT];
+                    lds_seg<T>(sC + n * BLOCK, Cw);
+                    const float e = scan_step<F16, T, true>(dl, du, dls, av, Bw, Cw, hv, first_upper, yy, [&] {
+                        hv = hrow[nx];
+                        av = arow[nx];
+                        lds_seg<T>(sB + nx * BLOCK, Bw);
+                    });
+                    if (li == kHalf - 1)
+                        hrow[n] = e;
                 }
-                if (lane < kGroup)
-                    hrow[gi * kGroup + lane] = hg;
-                // the group's partial: added by wave 0 in group order, handed
+                // the pass's partials: added by wave 0 in group order, handed
                 // over through LDS by the channel's other waves
+                float lo[TH], hi[TH];
+                pass_partials<T>(yy, lo, hi);
+                const int gi = 2 * (ps / kPass);
                 if (w == 0) {
 #pragma unroll
-                    for (int j = 0; j < SEG; ++j)
-                        y[j] = (r == 0 && gi == 0) ? yy[j] : y[j] + yy[j];
+                    for (int j = 0; j < TH; ++j)
+                        y[j] = (y[j] + lo[j]) + hi[j];
                 } else if constexpr (W > 1) {
 #pragma unroll
-                    for (int j = 0; j < SEG; ++j)
-                        sY[(((w - 1) * GROUPS + gi) * CPW + c) * BLOCK + lane * SEG + j] = yy[j];
+                    for (int j = 0; j < TH; ++j) {
+                        sY[(((w - 1) * GROUPS + gi) * CPW + c) * BLOCK + li * T + hl * TH + j] = lo[j];
+                        sY[(((w - 1) * GROUPS + gi + 1) * CPW + c) * BLOCK + li * T + hl * TH + j] = hi[j];
+                    }
                 }
             }
 
@@ -774,25 +891,39 @@ ssu_scan_staged_kernel(const ScanParams p)
                 if (w == 0) {
                     for (int k = 0; k < (W - 1) * GROUPS; ++k)
 #pragma unroll
-                        for (int j = 0; j < SEG; ++j)
-                            y[j] += sY[(k * CPW + c) * BLOCK + lane * SEG + j];
+                        for (int j = 0; j < TH; ++j)
+                            y[j] += sY[(k * CPW + c) * BLOCK + li * T + hl * TH + j];
                 }
             }
         }
 
         if (w == 0) {
-            uint16_t o[SEG];
+            // u again for the D u term (read at the block's start, not kept
+            // in registers across the scan)
+            uint32_t uo[WH];
+            uint16_t o[TH];
+            if constexpr (fast)
+                load_seg<TH, true>(u_row + blk, lown, 0, uo);
+            else
+                load_seg<TH, false>(u_row, own, p.t1, uo);
 #pragma unroll
-            for (int j = 0; j < SEG; ++j)
-                o[j] = f32_to_io<F16>(fmaf(Dd, io_to_f32<F16>(half_of<SEG>(uw, j)), y[j]));
-            store_seg<SEG, fast>(p.out + b * p.o_b + d * p.o_d, tok, p.t1, o);
+            for (int j = 0; j < TH; ++j)
+                o[j] = f32_to_io<F16>(fmaf(Dd, io_to_f32<F16>(half_of<TH>(uo, j)), y[j]));
+            if constexpr (fast)
+                store_seg<TH, true>(p.out + b * p.o_b + d * p.o_d + blk, lown, 0, o);
+            else
+                store_seg<TH, false>(p.out + b * p.o_b + d * p.o_d, own, p.t1, o);
         }
     };
     for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
-        if (p.vec && blk + BLOCK <= p.t1)
+        if constexpr (ALLFAST) {
             block(blk, std::true_type{});
-        else
-            block(blk, std::false_type{});
+        } else {
+            if (p.vec && blk + BLOCK <= p.t1)
+                block(blk, std::true_type{});
+            else
+                block(blk, std::false_type{});
+        }
     }
 
     // final states: every wave wrote its own to LDS
@@ -807,78 +938,95 @@ ssu_scan_staged_kernel(const ScanParams p)
 // grid, workgroup size and LDS.
 using ScanFn = hipError_t (*)(const ScanParams &, int64_t channels, hipStream_t);
 
-template <bool F16, int SEG, int NSW, bool FULL>
+template <bool F16, int T, int NSW, bool FULL, bool ALLFAST>
 hipError_t launch_direct(const ScanParams &p, int64_t channels, hipStream_t stream)
 {
     const int waves = (p.dstate + NSW - 1) / NSW;
     if constexpr (NSW == 16) {
         if (waves == 1) {  // the one-wave instantiation has the whole register file
-            hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, SEG, NSW, 1, FULL>), dim3(channels), dim3(kLanes), 0,
-                               stream, p);
+            hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, T, NSW, 1, FULL, ALLFAST>), dim3(channels), dim3(kLanes),
+                               0, stream, p);
             return hipGetLastError();
         }
     }
-    hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, SEG, NSW, kMaxStates / NSW, FULL>), dim3(channels),
+
+    hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, T, NSW, kMaxStates / NSW, FULL, ALLFAST>), dim3(channels),
                        dim3(waves * kLanes), 0, stream, p);
     return hipGetLastError();
 }
 
-template <bool F16, int SEG, int NSW, int W, int CPW, bool FULL>
+template <bool F16, int T, int NSW, int W, int CPW, bool FULL, bool ALLFAST>
 hipError_t launch_staged(const ScanParams &p, int64_t channels, hipStream_t stream)
 {
-    using S = ScanShape<SEG, NSW, W, CPW>;
-    hipLaunchKernelGGL((ssu_scan_staged_kernel<F16, SEG, NSW, W, CPW, FULL>), dim3(channels / CPW), dim3(S::NT),
-                       S::lds_bytes(p.rounds), stream, p);
+    using S = ScanShape<T, NSW, W, CPW>;
+    hipLaunchKernelGGL((ssu_scan_staged_kernel<F16, T, NSW, W, CPW, FULL, ALLFAST>), dim3(channels / CPW),
+                       dim3(S::NT), S::lds_bytes(p.rounds), stream, p);
     return hipGetLastError();
 }
 
-// A launch configuration: SEG tokens per lane, NSW states per wave; staged
-// ones also W waves per channel and CPW channels per workgroup. rs: states
-// per round (per wave for direct ones); ealign: the element alignment (of
-// every row start and chunk start) its vector loads need. fn[all rounds
-// full][f16].
+// A launch configuration: T tokens per lane, NSW states per wave; staged ones
+// also W waves per channel and CPW channels per workgroup. rs: states per
+// round (per wave for direct ones); ealign: the element alignment (of every
+// row start and chunk start) its vector loads need. fn[all rounds
+// full][f16][every block whole and aligned]: the last kernel has no code
+// for ragged or unaligned blocks, so fewer registers.
 struct ScanTile {
     int seg, nsw, waves, cpw, rs, ealign;
     bool staged;
-    ScanFn fn[2][2];
+    ScanFn fn[2][2][2];
     char name[32];
 };
 
-template <int SEG, int NSW>
+template <bool FULL, bool F16, bool ALLFAST, int T, int NSW>
+void set_direct(ScanTile &t)
+{
+    t.fn[FULL][F16][ALLFAST] = &launch_direct<F16, T, NSW, FULL, ALLFAST>;
+}
+
+template <bool FULL, bool F16, bool ALLFAST, int T, int NSW, int W, int CPW>
+void set_staged(ScanTile &t)
+{
+    t.fn[FULL][F16][ALLFAST] = &launch_staged<F16, T, NSW, W, CPW, FULL, ALLFAST>;
+}
+
+// Direct loads: a lane's own T/2 tokens of u, delta and out, its T-token
+// segment of each B and C row (16-byte vectors at most). Staged ones copy
+// 16-byte pieces of B and C.
+template <int T, int NSW>
 ScanTile direct_tile()
 {
     ScanTile t{};
-    t.seg = SEG, t.nsw = NSW, t.waves = 0, t.cpw = 1, t.rs = NSW, t.ealign = SEG, t.staged = false;
-    t.fn[0][0] = &launch_direct<false, SEG, NSW, false>;
-    t.fn[0][1] = &launch_direct<true, SEG, NSW, false>;
-    t.fn[1][0] = &launch_direct<false, SEG, NSW, true>;
-    t.fn[1][1] = &launch_direct<true, SEG, NSW, true>;
-    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d", SEG, NSW);
+    t.seg = T, t.nsw = NSW, t.waves = 0, t.cpw = 1, t.rs = NSW, t.ealign = T < 8 ? T : 8, t.staged = false;
+    set_direct<false, false, false, T, NSW>(t), set_direct<false, false, true, T, NSW>(t);
+    set_direct<false, true, false, T, NSW>(t), set_direct<false, true, true, T, NSW>(t);
+    set_direct<true, false, false, T, NSW>(t), set_direct<true, false, true, T, NSW>(t);
+    set_direct<true, true, false, T, NSW>(t), set_direct<true, true, true, T, NSW>(t);
+    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d", T, NSW);
     return t;
 }
 
-template <int SEG, int NSW, int W, int CPW>
+template <int T, int NSW, int W, int CPW>
 ScanTile staged_tile()
 {
     ScanTile t{};
-    t.seg = SEG, t.nsw = NSW, t.waves = W, t.cpw = CPW, t.rs = W * NSW, t.ealign = 8, t.staged = true;
-    t.fn[0][0] = &launch_staged<false, SEG, NSW, W, CPW, false>;
-    t.fn[0][1] = &launch_staged<true, SEG, NSW, W, CPW, false>;
-    t.fn[1][0] = &launch_staged<false, SEG, NSW, W, CPW, true>;
-    t.fn[1][1] = &launch_staged<true, SEG, NSW, W, CPW, true>;
-    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d_w%d_c%d", SEG, NSW, W, CPW);
+    t.seg = T, t.nsw = NSW, t.waves = W, t.cpw = CPW, t.rs = W * NSW, t.ealign = 8, t.staged = true;
+    set_staged<false, false, false, T, NSW, W, CPW>(t), set_staged<false, false, true, T, NSW, W, CPW>(t);
+    set_staged<false, true, false, T, NSW, W, CPW>(t), set_staged<false, true, true, T, NSW, W, CPW>(t);
+    set_staged<true, false, false, T, NSW, W, CPW>(t), set_staged<true, false, true, T, NSW, W, CPW>(t);
+    set_staged<true, true, false, T, NSW, W, CPW>(t), set_staged<true, true, true, T, NSW, W, CPW>(t);
+    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d_w%d_c%d", T, NSW, W, CPW);
     return t;
 }
 
-template <int SEG>
+template <int T>
 void add_scan_tiles(ScanTile *&t)
 {
-    *t++ = direct_tile<SEG, 16>();
-    *t++ = direct_tile<SEG, 8>();
-    *t++ = staged_tile<SEG, 16, 1, 4>();
-    *t++ = staged_tile<SEG, 16, 1, 8>();
-    *t++ = staged_tile<SEG, 16, 1, 2>();
-    *t++ = staged_tile<SEG, 8, 2, 4>();
+    *t++ = direct_tile<T, 16>();
+    *t++ = direct_tile<T, 8>();
+    *t++ = staged_tile<T, 16, 1, 4>();
+    *t++ = staged_tile<T, 16, 1, 8>();
+    *t++ = staged_tile<T, 16, 1, 2>();
+    *t++ = staged_tile<T, 8, 2, 4>();
 }
 
 constexpr int kScanTiles = 24;
@@ -888,10 +1036,10 @@ const ScanTile *scan_tiles(int *count)
     static ScanTile table[kScanTiles];
     static const bool init = [] {
         ScanTile *t = table;
+        add_scan_tiles<16>(t);
         add_scan_tiles<8>(t);
         add_scan_tiles<4>(t);
         add_scan_tiles<2>(t);
-        add_scan_tiles<1>(t);
         return t == table + kScanTiles;
     }();
     (void)init;
@@ -900,41 +1048,45 @@ const ScanTile *scan_tiles(int *count)
 }
 
 // Default launch configuration, from a sweep of the configurations on MI355X
-// (d_state 16, 4096 fp16 tokens per request, 1, 2, 4, 8 and 16 requests of
-// 1024 channels, static chunk 512 and one launch, cold caches): the largest
-// token segment that a launch still fills (64 lanes x SEG tokens per block);
-// then by the number of channels:
-//   up to 1024:  the direct kernel, two waves of 8 states per channel (at one
-//                request 59.95 us per sequence at chunk 512 against 64.03 for
-//                the best staged one: latency bound);
-//   up to 2048:  staged, two waves of 8 states per channel, four channels per
-//                workgroup (two requests: 85.6 against 108.4 us direct);
+// (d_state 16, 4096 fp16 tokens per request, 1, 2, 4 and 16 requests of 1024
+// channels, static chunk 512 and one launch, cold caches): the largest token
+// segment that a launch still fills (32 lanes x T tokens per block); then by
+// the number of channels:
+//   up to 2048:  the direct kernel, one wave of 16 states per channel (one
+//                request: 59.8 us per sequence at chunk 512 and 33.4 in one
+//                launch, against 64.6 and 35.7 with two waves of 8 states
+//                and 61.8 and 39.7 staged; two requests: 79.9 and 50.3,
+//                against 78.4 and 55.5 staged);
 //   above:       staged, one wave of 16 states per channel, four channels per
-//                workgroup (16 requests: 384.5 against 595.6 us direct, and
-//                355.4 against 479.4 us in one launch).
+//                workgroup (16 requests: 357.0 and 330.7 us, against 390.5
+//                and 335.2 direct; eight channels per workgroup 499.7 and
+//                422.4, two 506.7 and 464.5: fewer waves fit).
 // Where a group's channels do not split into fours, the direct kernel.
-constexpr int64_t kDirectChannels = 1024;
-constexpr int64_t kTwoWaveChannels = 2048;
+constexpr int64_t kDirectChannels = 2048;
 
-int default_scan_tile(int64_t span, int64_t channels, int ch_per_group)
+// Staged kernels address a thread's staging pieces as a 32-bit byte offset
+// from a row pointer, over at most kMaxStates rows of B and of C.
+bool staged_rows_fit(int64_t B_n, int64_t C_n)
+{
+    return std::max(B_n, C_n) < (int64_t(1) << 30) / kMaxStates;
+}
+
+int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool staged_ok)
 {
     int count = 0;
     const ScanTile *t = scan_tiles(&count);
-    int seg = 1;
-    for (int sg : {8, 4, 2})
-        if (span >= int64_t(kLanes) * sg) {
+    int seg = 2;
+    for (int sg : {16, 8, 4})
+        if (span >= int64_t(kHalf) * sg) {
             seg = sg;
             break;
         }
-    const bool staged = channels > kDirectChannels && ch_per_group % 4 == 0;
-    const bool two_waves = channels <= kTwoWaveChannels;
+    const bool staged = staged_ok && channels > kDirectChannels && ch_per_group % 4 == 0;
     for (int i = 0; i < count; ++i) {
         const ScanTile &x = t[i];
-        if (x.seg != seg || x.staged != staged)
+        if (x.seg != seg || x.staged != staged || x.nsw != 16)
             continue;
-        if (!staged && x.nsw == 8)
-            return i;
-        if (staged && x.cpw == 4 && (two_waves ? (x.nsw == 8 && x.waves == 2) : (x.nsw == 16 && x.waves == 1)))
+        if (!staged || (x.cpw == 4 && x.waves == 1))
             return i;
     }
     return 0;
@@ -1038,11 +1190,16 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
 
     const int ch_per_group = dim / G;
     const int64_t channels = static_cast<int64_t>(bs) * dim;
-    const int t = tile >= 0 ? tile : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, channels, ch_per_group);
+    const bool staged_ok = staged_rows_fit(a->B.stride[2], a->C.stride[2]);
+    const int t = tile >= 0 ? tile
+                            : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, channels, ch_per_group, staged_ok);
     const ScanTile &T = tiles[t];
     if (ch_per_group % T.cpw)
         return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: %s needs the channels of a group (%d) in multiples of %d", T.name,
                     ch_per_group, T.cpw);
+    if (T.staged && !staged_ok)
+        return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: %s needs the B and C state strides below %lld elements", T.name,
+                    static_cast<long long>((int64_t(1) << 30) / kMaxStates));
     const int rounds = (N + T.rs - 1) / T.rs;
 
     ScanParams p{};
@@ -1065,7 +1222,7 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
     p.dim = dim, p.dstate = N, p.ch_per_group = ch_per_group, p.softplus = a->delta_softplus;
     p.rounds = rounds;
 
-    // Vector access (SEG tokens of a row per lane; for the staged kernel also
+    // Vector access (a lane's tokens of each row; for the staged kernel also
     // 16-byte pieces of the B and C rows into LDS) needs every row start and
     // every chunk start on a multiple of T.ealign elements.
     const int64_t ealign = T.ealign;  // in 16-bit elements
@@ -1080,14 +1237,30 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
     }
     const int64_t step = (chunk > 0 && chunk < L) ? chunk : L;
     const bool f16 = a->u.dtype == SSU_F16;
-    const ScanFn fn = T.fn[N % T.rs == 0][f16];
-    for (int64_t t0 = 0; t0 < L; t0 += step) {
-        p.t0 = t0;
-        p.t1 = std::min(L, t0 + step);
-        p.vec = vec && (t0 % ealign == 0);
-        const hipError_t e = fn(p, channels, stream);
+    const bool full = N % T.rs == 0;
+    const int64_t block = int64_t(kHalf) * T.seg;
+    // Each chunk: its whole, aligned blocks in one launch of the kernel
+    // without the ragged-block code, then what is left (a ragged tail, or a
+    // chunk that is not aligned) in one launch of the general kernel. The
+    // state is carried between the two as between chunks, and the blocks are
+    // the same, so the split changes no bit of the result.
+    auto launch = [&](int64_t t0, int64_t t1, bool v, bool allfast) -> ssu_status {
+        p.t0 = t0, p.t1 = t1, p.vec = v;
+        const hipError_t e = T.fn[full][f16][allfast](p, channels, stream);
         if (e != hipSuccess)
             return fail(SSU_ERR_HIP, "launch of %s failed: %s", T.name, hipGetErrorString(e));
+        return SSU_OK;
+    };
+    for (int64_t t0 = 0; t0 < L; t0 += step) {
+        const int64_t t1 = std::min(L, t0 + step);
+        const bool v = vec && (t0 % ealign == 0);
+        const int64_t tf = v ? t0 + (t1 - t0) / block * block : t0;  // end of the whole blocks
+        if (tf > t0)
+            if (const ssu_status st = launch(t0, tf, true, true); st != SSU_OK)
+                return st;
+        if (t1 > tf)
+            if (const ssu_status st = launch(tf, t1, v, false); st != SSU_OK)
+                return st;
     }
     return SSU_OK;
 }

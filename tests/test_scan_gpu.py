@@ -116,9 +116,9 @@ def test_scan_configs(k, zero_state):
 
 def test_scan_chunk_invariance():
     """Chunks that are multiples of 512 tokens give bitwise the results of one
-    launch, in the default configuration and in every configuration with 8
-    tokens per lane; other chunk sizes (including ragged ones) stay within
-    tolerance."""
+    launch, in the default configuration and in every configuration with 16
+    tokens per lane (blocks of 512); other chunk sizes (including ragged ones)
+    stay within tolerance."""
     import selective_state_update_amd as ssu
 
     name, _, p = _config_case(1, False)
@@ -128,7 +128,7 @@ def test_scan_chunk_invariance():
         o, s = ds.run(chunk=chunk)
         assert np.array_equal(o, o0) and np.array_equal(s, s0), chunk
     for tile, tname in enumerate(ssu.scan_tiles()):
-        if tname.startswith("scan_t8_"):
+        if tname.startswith("scan_t16_"):
             for chunk in (512, 0):
                 o, s = ds.run(chunk=chunk, tile=tile)
                 assert np.array_equal(o, o0) and np.array_equal(s, s0), (tname, chunk)
