@@ -530,6 +530,20 @@ def test_scan_other_rejections(ssu):
     assert ssu._lib.ssu_scan_tile_name(99) == b""
 
 
+def test_scan_staged_needs_32bit_row_offsets(ssu):
+    """A staged launch configuration addresses its staging pieces as 32-bit
+    byte offsets from a row pointer: B or C state strides of 2^30 / 64 elements
+    or more are refused for it before any launch (the default then picks the
+    direct kernel, which takes 64-bit addresses)."""
+    names = ssu.scan_tiles()
+    staged = next(i for i, n in enumerate(names) if n.startswith("scan_t16_n16_w1_c4"))
+    a = _scan_args(ssu, dim=32)
+    a.B.stride[2] = (1 << 30) // 64
+    assert _scan_call(ssu, a, tile=staged) == 2
+    err = ssu._lib.ssu_last_error().decode()
+    assert err.startswith("ssu_scan") and "strides" in err
+
+
 def test_scan_empty_is_a_noop(ssu):
     """batch 0, or a sequence of length 0, returns OK without any HIP call."""
     a = _scan_args(ssu, batch=0)
