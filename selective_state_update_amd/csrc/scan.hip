@@ -326,7 +326,9 @@ __device__ __forceinline__ float softplus_f32(float v)
 // that reads the next step's operands from LDS there has them in flight
 // while this step's tokens are replayed, in the registers this step's have
 // just freed.
-template <bool F16, int T, bool FENCED = false, typename AfterScan>
+// FIRST: the pass's first state, whose terms start yy (yy[j] = h_j C_j + 0,
+// the same bits as adding them to yy = +0).
+template <bool F16, int T, bool FENCED = false, bool FIRST = false, typename AfterScan>
 __device__ __forceinline__ float scan_step(const float (&dl)[T], const float (&du)[T], float dls, float A2,
                                            const uint32_t (&Bw)[(T + 1) / 2], const uint32_t (&Cw)[(T + 1) / 2],
                                            float h, bool first_upper, float (&yy)[T], AfterScan after_scan)
@@ -357,9 +359,9 @@ __device__ __forceinline__ float scan_step(const float (&dl)[T], const float (&d
 #pragma unroll
     for (int j = 0; j < T - 1; ++j) {
         hj = fmaf(a[j], hj, b[j]);
-        yy[j] = fmaf(hj, io_to_f32<F16>(half_of<T>(Cw, j)), yy[j]);
+        yy[j] = fmaf(hj, io_to_f32<F16>(half_of<T>(Cw, j)), FIRST ? 0.0f : yy[j]);
     }
-    yy[T - 1] = fmaf(e, io_to_f32<F16>(half_of<T>(Cw, T - 1)), yy[T - 1]);
+    yy[T - 1] = fmaf(e, io_to_f32<F16>(half_of<T>(Cw, T - 1)), FIRST ? 0.0f : yy[T - 1]);
     return e;
 }
 
@@ -840,31 +842,32 @@ ssu_scan_staged_kernel(const ScanParams p)
             const float *const arow = sA + c * HP + r * RS;
 #pragma unroll 1
             for (int ps = 0; ps < NSW; ps += kPass) {
-                float yy[T];
-#pragma unroll
-                for (int j = 0; j < T; ++j)
-                    yy[j] = 0.0f;
                 // a step's carried value, decay rate and B row are read from
                 // LDS while the step before replays its tokens; its C row at
                 // its own start
+                float yy[T];
                 const int n0 = sbase + ps;
                 float hv = hrow[n0], av = arow[n0];
                 uint32_t Bw[WT];
                 lds_seg<T>(sB + n0 * BLOCK, Bw);
-#pragma unroll 1
-                for (int k = 0; k < kGroup; ++k) {
+                auto step = [&](int k, auto first_tag) {
                     const int n = n0 + k;  // this half's state, within the round
                     const int nx = n + 1;  // past the pass's last: read, unused (LDS has a padding word)
                     uint32_t Cw[WT];
                     lds_seg<T>(sC + n * BLOCK, Cw);
-                    const float e = scan_step<F16, T, true>(dl, du, dls, av, Bw, Cw, hv, first_upper, yy, [&] {
-                        hv = hrow[nx];
-                        av = arow[nx];
-                        lds_seg<T>(sB + nx * BLOCK, Bw);
-                    });
+                    const float e = scan_step<F16, T, true, decltype(first_tag)::value>(
+                        dl, du, dls, av, Bw, Cw, hv, first_upper, yy, [&] {
+                            hv = hrow[nx];
+                            av = arow[nx];
+                            lds_seg<T>(sB + nx * BLOCK, Bw);
+                        });
                     if (li == kHalf - 1)
                         hrow[n] = e;
-                }
+                };
+                step(0, std::true_type{});
+#pragma unroll 1
+                for (int k = 1; k < kGroup; ++k)
+                    step(k, std::false_type{});
                 // the pass's partials: added by wave 0 in group order, handed
                 // over through LDS by the channel's other waves
                 float lo[TH], hi[TH];
