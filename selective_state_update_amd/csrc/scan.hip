@@ -310,17 +310,18 @@ __device__ __forceinline__ float softplus_f32(float v)
 
 // One state per half over one block of 32 * T tokens, in this lane's segment
 // of T tokens: dl their step sizes, du = dl * u their inputs, dls = the sum of
-// dl (in token order), Bw and Cw the state's B and C bits, A2 = A * log2(e), h
-// the carried state (uniform over the half), first_upper: this lane is
-// lane 32. Adds the state's h_j * C_j to yy[j] and returns the lane's end
-// state e (the half's last lane holds the carried state after the block).
+// dl (in token order), Bw and Cw the state's B and C bits, A2 = A * log2(e),
+// h the carried state (uniform over the half), half_first: this lane is its
+// half's first (lane 0 or 32). Adds the state's h_j * C_j to yy[j] and
+// returns the lane's end state e (the half's last lane holds the carried
+// state after the block).
 //   1. the lane's whole map: decay exp2(A2 * dls) (the product of its
 //      tokens' decays in one exponential), and the state Q reached from 0;
 //   2. the 32-lane inclusive scan of the maps;
 //   3. the lane's end state e (the map applied to h) and start state g (e
-//      shifted one lane up, the half's first lane taking h); the lane's tokens
-//      are replayed from g, h_j = a_j h_{j-1} + b_j, and after its last token
-//      the state is e.
+//      shifted one lane up; the half's first lane takes h instead); the
+//      lane's tokens are replayed from g, h_j = a_j h_{j-1} + b_j, and after
+//      its last token the state is e.
 // after_scan() is called once the step no longer needs A2, Bw and h (after
 // the 32-lane scan, which no memory access crosses when FENCED): a caller
 // that reads the next step's operands from LDS there has them in flight
@@ -331,7 +332,7 @@ __device__ __forceinline__ float softplus_f32(float v)
 template <bool F16, int T, bool FENCED = false, bool FIRST = false, typename AfterScan>
 __device__ __forceinline__ float scan_step(const float (&dl)[T], const float (&du)[T], float dls, float A2,
                                            const uint32_t (&Bw)[(T + 1) / 2], const uint32_t (&Cw)[(T + 1) / 2],
-                                           float h, bool first_upper, float (&yy)[T], AfterScan after_scan)
+                                           float h, bool half_first, float (&yy)[T], AfterScan after_scan)
 {
     float a[T], b[T];
 #pragma unroll
@@ -349,9 +350,8 @@ __device__ __forceinline__ float scan_step(const float (&dl)[T], const float (&d
     else
         SSU_SCAN_TREE1(Q, P);
     const float e = fmaf(P, h, Q);
-    float g = __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(h), __float_as_int(e), kWaveShr1, 0xf, 0xf, false));
-    g = first_upper ? h : g;
+    float g = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e), kWaveShr1, 0xf, 0xf, true));
+    g = half_first ? h : g;
     if constexpr (FENCED)
         asm volatile("" : "+v"(g) : : "memory");  // h is dead before after_scan's reads
     after_scan();
@@ -372,7 +372,7 @@ template <bool F16, int T>
 __device__ __forceinline__ void scan_step2(const float (&dl)[T], const float (&du)[T], float dls, float A20,
                                            float A21, const uint32_t (&B0)[(T + 1) / 2],
                                            const uint32_t (&B1)[(T + 1) / 2], const uint32_t (&C0)[(T + 1) / 2],
-                                           const uint32_t (&C1)[(T + 1) / 2], float h0, float h1, bool first_upper,
+                                           const uint32_t (&C1)[(T + 1) / 2], float h0, float h1, bool half_first,
                                            float (&yy)[T], float &e0, float &e1)
 {
     float a0[T], b0[T], a1[T], b1[T];
@@ -393,12 +393,10 @@ __device__ __forceinline__ void scan_step2(const float (&dl)[T], const float (&d
     SSU_SCAN_TREE2(Q0, Q1, P0, P1);
     e0 = fmaf(P0, h0, Q0);
     e1 = fmaf(P1, h1, Q1);
-    float g0 = __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(h0), __float_as_int(e0), kWaveShr1, 0xf, 0xf, false));
-    float g1 = __int_as_float(
-        __builtin_amdgcn_update_dpp(__float_as_int(h1), __float_as_int(e1), kWaveShr1, 0xf, 0xf, false));
-    g0 = first_upper ? h0 : g0;
-    g1 = first_upper ? h1 : g1;
+    float g0 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e0), kWaveShr1, 0xf, 0xf, true));
+    float g1 = __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(e1), kWaveShr1, 0xf, 0xf, true));
+    g0 = half_first ? h0 : g0;
+    g1 = half_first ? h1 : g1;
     float hj0 = g0, hj1 = g1;
 #pragma unroll
     for (int j = 0; j < T - 1; ++j) {
@@ -475,7 +473,7 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
 
     const int lane = static_cast<int>(threadIdx.x) & (kLanes - 1);
     const int li = lane & (kHalf - 1), hl = lane >> 5;
-    const bool first_upper = lane == kHalf;
+    const bool half_first = li == 0;
     const int wave = MAXW > 1 ? __builtin_amdgcn_readfirstlane(static_cast<int>(threadIdx.x) / kLanes) : 0;
     const int nwaves = MAXW > 1 ? static_cast<int>(blockDim.x) / kLanes : 1;
     const int64_t bd = blockIdx.x;
@@ -563,7 +561,7 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
                 for (int s = ps; s < ps + kGroup; s += 2) {
                     float e0, e1;
                     scan_step2<F16, T>(dl, du, dls, A2[s], A2[s + 1], Bw[s], Bw[s + 1], Cw[s], Cw[s + 1], hv[s],
-                                       hv[s + 1], first_upper, yy, e0, e1);
+                                       hv[s + 1], half_first, yy, e0, e1);
                     hv[s] = half_last(e0, lane);
                     hv[s + 1] = half_last(e1, lane);
                 }
@@ -571,7 +569,7 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
 #pragma unroll
                 for (int s = ps; s < ps + kGroup; ++s) {
                     const float e =
-                        scan_step<F16, T>(dl, du, dls, A2[s], Bw[s], Cw[s], hv[s], first_upper, yy, [] {});
+                        scan_step<F16, T>(dl, du, dls, A2[s], Bw[s], Cw[s], hv[s], half_first, yy, [] {});
                     hv[s] = half_last(e, lane);
                 }
             }
@@ -669,7 +667,7 @@ ssu_scan_staged_kernel(const ScanParams p)
     const int tid = static_cast<int>(threadIdx.x);
     const int lane = tid & (kLanes - 1);
     const int li = lane & (kHalf - 1), hl = lane >> 5;
-    const bool first_upper = lane == kHalf;
+    const bool half_first = li == 0;
     const int wv = __builtin_amdgcn_readfirstlane(tid / kLanes);  // uniform: pointers below stay scalar
     const int c = wv / W;        // channel slot
     const int w = wv - c * W;    // state slice
@@ -856,7 +854,7 @@ ssu_scan_staged_kernel(const ScanParams p)
                     uint32_t Cw[WT];
                     lds_seg<T>(sC + n * BLOCK, Cw);
                     const float e = scan_step<F16, T, true, decltype(first_tag)::value>(
-                        dl, du, dls, av, Bw, Cw, hv, first_upper, yy, [&] {
+                        dl, du, dls, av, Bw, Cw, hv, half_first, yy, [&] {
                             hv = hrow[nx];
                             av = arow[nx];
                             lds_seg<T>(sB + nx * BLOCK, Bw);
