@@ -1,14 +1,14 @@
 #!/usr/bin/env python3
 """Benchmark of libssu's decode-step selective_state_update on one MI355X.
 
-Method (sglang PR #41223, "[Perf] Mamba2 selective_state_update up to 2x
-faster on B200 via 8x1 launch config for dstate 128", section "Kernel
-measurement"): many calls captured in one graph, each call reading a different
-set of state slots; the sets are disjoint and together hold at least three
-times the last-level cache, so every call streams its state from HBM, as in
-real decode where each layer's state is touched once per step. Here the graph
-is a HIP graph and the last-level cache is MI355X's 256 MB Infinity Cache, so
-the sets total >= 768 MiB.
+Method: the measurement set-up of sglang PR #41223, "[Perf] Mamba2
+selective_state_update up to 2x faster on B200 via 8x1 launch config for
+dstate 128", section "Kernel measurement". One graph holds many calls;
+consecutive calls work on disjoint sets of state slots, and all the sets
+together exceed the last-level cache three times over, so no call finds its
+state in cache. (A decoding model's layer meets its state cold in the same
+way: once per generated token.) Here the graph is a HIP graph and the
+last-level cache is MI355X's 256 MB Infinity Cache: the sets total >= 768 MiB.
 
 A "step" is one ssu_update call over one batch. The default workload is the
 headline one: H=16, P=64, N=128, batch 512, fp32 state, bf16 x/B/C as strided
