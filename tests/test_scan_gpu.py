@@ -72,6 +72,9 @@ def check(p, out, state, r, what=""):
     rs, ro = tol.scan_error_ratios(out, state, r["y"], r["tau"], r["rho"], r["state"], r["err"], p.dstate, p.io)
     print(f"  {what}: worst state error {rs:.3f} eps*E (bound {tol.SCAN_STATE_C:g}), "
           f"worst out excess {ro:.4f} eps*(rho+N*tau) (bound {tol.SCAN_OUT_C:g})", flush=True)
+    assert rs <= tol.SCAN_STATE_WATCH and ro <= tol.SCAN_OUT_WATCH, (
+        f"{what}: error ratios {rs:.3f} / {ro:.4f} past the regression watch "
+        f"{tol.SCAN_STATE_WATCH:g} / {tol.SCAN_OUT_WATCH:g}")
     bad_o = tol.scan_out_violations(out, r["y"], r["tau"], r["rho"], p.dstate, p.io)
     bad_s = tol.scan_state_violations(state, r["state"], r["err"])
     if bad_o.any():
@@ -151,6 +154,33 @@ def test_scan_every_tile():
         for chunk in (0, 200):
             o, s = ds.run(chunk=chunk, tile=tile)
             check(p, o, s, r, f"{name} chunk {chunk}")
+
+
+@pytest.mark.parametrize("N", [17, 32, 48, 64])
+def test_scan_every_tile_more_states(N):
+    """Every launch configuration at d_state above one wave's 16 states (the
+    staged configurations then stage their rows in several rounds, the direct
+    ones run several waves per channel), with a ragged tail and a chunk that
+    splits blocks: within tolerance of the oracle, and the configurations with
+    the same token segment bitwise equal to each other."""
+    import oracle
+    import selective_state_update_amd as ssu
+
+    p = si.make_scan_problem(2, 32, N, 700, 2, io="bf16", seed=70 + N, zero_state=False)
+    r = oracle_scan(oracle.get(), p)
+    ds = DeviceScan(p)
+    first = {}
+    for tile, name in enumerate(ssu.scan_tiles()):
+        seg = name.split("_")[1]
+        for chunk in (0, 256):
+            o, s = ds.run(chunk=chunk, tile=tile)
+            check(p, o, s, r, f"N={N} {name} chunk {chunk}")
+            key = (seg, chunk)
+            if key not in first:
+                first[key] = (name, o, s)
+            else:
+                n0, o0, s0 = first[key]
+                assert np.array_equal(o, o0) and np.array_equal(s, s0), (name, n0, chunk)
 
 
 @pytest.mark.parametrize("L", [1, 7, 63, 64, 65, 511, 513, 1000])
