@@ -297,12 +297,16 @@ typedef struct ssu_scan_args {
     ssu_view out;           /* [batch, dim, L], u's dtype, written; stride[2] == 1 */
 } ssu_scan_args;
 
-/* Enqueue the scan of `args` on `stream` in ceil(L / chunk) kernel launches
- * of `chunk` tokens each, in order, the state carried between them through
- * `state` (chunk = 0: the whole sequence in one launch). Chunks whose size is
- * a multiple of 512 give bitwise the same results as one launch; other chunk
- * sizes agree within rounding. tile = -1 picks the launch configuration from
- * the chunk size; 0 .. ssu_scan_tile_count()-1 forces one.
+/* Enqueue the scan of `args` on `stream`, chunk after chunk of `chunk` tokens
+ * (chunk = 0: the whole sequence), in order, the state carried between them
+ * through `state`; a chunk is one kernel launch, or two when it ends in a
+ * ragged or unaligned rest (its whole blocks, then the rest). Chunks whose
+ * size is a multiple of 512 give bitwise the same results as one launch;
+ * other chunk sizes agree within rounding. Every configuration with the same
+ * token segment gives the same bits, so a request's results do not depend on
+ * the batch it is scanned in. tile = -1 picks the launch configuration from
+ * the chunk size and the number of channels; 0 .. ssu_scan_tile_count()-1
+ * forces one.
  * Memory: the caller owns every buffer; the library allocates nothing and
  * keeps no pointer after the call. out and state must not overlap each other
  * or any input (the kernel reads inputs through the read-only cache).
@@ -310,7 +314,10 @@ typedef struct ssu_scan_args {
  * Errors (nothing is launched): SSU_ERR_INVALID_ARGUMENT (null pointers,
  * negative sizes or strides, wrong dtypes, non-zero reserved fields,
  * dim % ngroups != 0, tile out of range), SSU_ERR_UNSUPPORTED (non-contiguous
- * token or state axis, D or delta_bias, dstate > 64, batch * dim >= 2^31),
+ * token or state axis, D or delta_bias, dstate > 64, batch * dim >= 2^31; a
+ * forced staged configuration when the channels of a group do not split into
+ * its workgroups' 2, 4 or 8, or when B's or C's state stride is 2^24
+ * elements or more),
  * SSU_ERR_MISALIGNED (elements not aligned to their size), SSU_ERR_HIP
  * (launch failure; earlier chunks may have run). */
 ssu_status ssu_scan(const ssu_scan_args *args, int64_t chunk, int32_t tile, hipStream_t stream);
