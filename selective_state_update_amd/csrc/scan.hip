@@ -64,9 +64,9 @@
 //     LDS once, W * NSW states at a time (a round; d_state above that takes
 //     several rounds), and each wave reads the rows of the state it is working
 //     on just before it needs them, with the carried states and decay rates
-//     kept in LDS. Few registers are live, so four waves fit on each SIMD, and
-//     the B/C traffic falls by CPW: what a large batch (throughput bound)
-//     needs.
+//     kept in LDS. Fewer registers are live (three waves fit on each SIMD at
+//     T = 16, four below), and the B/C traffic falls by CPW: what a large
+//     batch (throughput bound) needs.
 //
 // Invalid tokens (past the end of a ragged last block) get Delta = 0, u = 0
 // and B = C = 0: their decay is exp2(0) = 1 and their input 0, the identity
