@@ -855,7 +855,7 @@ def summarize_scan_counters(a):
     fetch_dir, write_dir = a.summarize_scan_counters.split(",")
     fetch, write = _load_counter(fetch_dir, "FETCH_SIZE"), _load_counter(write_dir, "WRITE_SIZE")
     def is_scan(k):
-        return "ssu_scan_direct_kernel" in k or "ssu_scan_staged_kernel" in k
+        return any(f"ssu_scan_{kind}_kernel" in k for kind in ("direct", "staged", "paired"))
 
     fs = [v for k, v in fetch if is_scan(k)]
     ws = [v for k, v in write if is_scan(k)]

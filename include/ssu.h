@@ -315,9 +315,9 @@ typedef struct ssu_scan_args {
  * negative sizes or strides, wrong dtypes, non-zero reserved fields,
  * dim % ngroups != 0, tile out of range), SSU_ERR_UNSUPPORTED (non-contiguous
  * token or state axis, D or delta_bias, dstate > 64, batch * dim >= 2^31; a
- * forced staged configuration when the channels of a group do not split into
- * its workgroups' 2, 4 or 8, or when B's or C's state stride is 2^24
- * elements or more),
+ * forced staged or paired configuration when the channels of a group do not
+ * split into its workgroups' 2, 4 or 8, or when B's or C's state stride is
+ * 2^24 elements or more),
  * SSU_ERR_MISALIGNED (elements not aligned to their size), SSU_ERR_HIP
  * (launch failure; earlier chunks may have run). */
 ssu_status ssu_scan(const ssu_scan_args *args, int64_t chunk, int32_t tile, hipStream_t stream);

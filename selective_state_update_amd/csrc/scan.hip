@@ -15,8 +15,9 @@
 // Tokens go in blocks of 32 * T (T = 16, 8, 4 or 2 tokens per lane; 512
 // tokens at T = 16). Both halves of a wave (lanes 0-31 and 32-63) see the
 // same block: lane i of either half holds the segment of T tokens starting at
-// i * T, and the two halves scan two different states, so every wave
-// instruction advances two states at once. Per state the recurrence
+// i * T, and the two halves scan two different states of one channel (direct
+// and staged kernels) or the same state of two channels (paired kernel), so
+// every wave instruction advances two scans at once. Per state the recurrence
 // h -> a h + b is a composition of affine maps, and composition is
 // associative:
 //   1. each lane composes its T pairs (a_j, b_j) into one map (P, Q);
@@ -35,23 +36,25 @@
 // block ended with: chunkings whose chunks are multiples of 32 * T give
 // bitwise identical results.
 //
-// Work on tokens alone (the step sizes and their softplus, the inputs
-// Delta u, the output's D u term and its rounding) is not repeated in both
-// halves: of each segment the lower half's lane owns the first T/2 tokens and
-// the upper half's lane the last T/2; each computes its own tokens' values and
-// the two trade what the other needs with one v_permlane32_swap per value.
+// In the direct and staged kernels, work on tokens alone (the step sizes and
+// their softplus, the inputs Delta u, the output's D u term and its rounding)
+// is not repeated in both halves: of each segment the lower half's lane owns
+// the first T/2 tokens and the upper half's lane the last T/2; each computes
+// its own tokens' values and the two trade what the other needs with one
+// v_permlane32_swap per value.
 //
 // y is summed in one fixed order whatever the configuration: states in groups
 // of 4, each group's partial accumulated in state order (fma), the groups
-// added in group order. A wave takes its states in passes of 8: in each pass
-// the lower half scans the first group and the upper half the second, one
-// state of each per step. After a pass the halves trade partials so that each
-// lane holds both groups' partials for the tokens it owns, and adds them in
-// order; partials of a channel's other waves are handed over through LDS. With
-// the same T, every configuration and every chunking on block boundaries gives
-// bitwise the same outputs.
+// added in group order. In the direct and staged kernels a wave takes its
+// states in passes of 8: in each pass the lower half scans the first group
+// and the upper half the second, one state of each per step. After a pass the
+// halves trade partials so that each lane holds both groups' partials for the
+// tokens it owns, and adds them in order; partials of a channel's other waves
+// are handed over through LDS. In the paired kernel each lane adds its own
+// channel's groups as it finishes them. With the same T, every configuration
+// and every chunking on block boundaries gives bitwise the same outputs.
 //
-// Two kernels compute it, with the same fp32 operations in the same order:
+// Three kernels compute it, with the same fp32 operations in the same order:
 //
 //   direct (scan_t{T}_n{NSW}): one workgroup per (request, channel), one wave
 //     per NSW of its states; each wave loads its states' B and C rows straight
@@ -65,8 +68,14 @@
 //     several rounds), and each wave reads the rows of the state it is working
 //     on just before it needs them, with the carried states and decay rates
 //     kept in LDS. Fewer registers are live (three waves fit on each SIMD at
-//     T = 16, four below), and the B/C traffic falls by CPW: what a large
-//     batch (throughput bound) needs.
+//     T = 16, four below), and the B/C traffic falls by CPW.
+//   paired (scan_t{T}_n16_pair_c{2 CPW}): staged in the same way, but each
+//     half of a wave holds its own channel over the whole block and walks
+//     every state of it, so that nothing is traded between the halves: each
+//     lane computes the step sizes of all T tokens of its segment and sums
+//     its own partials and outputs. Both halves step through the same state
+//     at once and read the same staged rows. Fewest instructions per element:
+//     what a large batch (throughput bound) needs.
 //
 // Invalid tokens (past the end of a ragged last block) get Delta = 0, u = 0
 // and B = C = 0: their decay is exp2(0) = 1 and their input 0, the identity
@@ -113,11 +122,18 @@ __device__ __forceinline__ float io_to_f32(uint32_t bits)
         return __uint_as_float(bits << 16);
 }
 
+// fp32 to the I/O type, round to nearest even. For fp16 the value is first
+// made opaque to the compiler: otherwise it may fuse the fma that produced f
+// with this conversion into one mixed-precision instruction that rounds the
+// exact result to fp16 once, instead of to fp32 and then to fp16, and whether
+// it does so depends on the surrounding code, so configurations would differ
+// in the last bit.
 template <bool F16>
 __device__ __forceinline__ uint16_t f32_to_io(float f)
 {
     if constexpr (F16) {
-        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32, round to nearest even
+        asm("" : "+v"(f));
+        return __builtin_bit_cast(uint16_t, static_cast<_Float16>(f));  // v_cvt_f16_f32
     } else {
         uint32_t w = __float_as_uint(f);
         if ((w & 0x7fffffffu) > 0x7f800000u)
@@ -174,9 +190,12 @@ __device__ __forceinline__ void store_seg(uint16_t *row, int64_t tok, int64_t t1
 #pragma unroll
         for (int k = 0; k < (N + 1) / 2; ++k)
             w[k] = v[2 * k] | ((2 * k + 1 < N) ? (static_cast<uint32_t>(v[2 * k + 1]) << 16) : 0u);
-        if constexpr (N == 8) {
-            u32x4 x = {w[0], w[1], w[2], w[3]};
-            *reinterpret_cast<u32x4 *>(p) = x;
+        if constexpr (N >= 8) {
+#pragma unroll
+            for (int q = 0; q < N / 8; ++q) {
+                u32x4 x = {w[4 * q], w[4 * q + 1], w[4 * q + 2], w[4 * q + 3]};
+                *reinterpret_cast<u32x4 *>(p + 8 * q) = x;
+            }
         } else if constexpr (N == 4) {
             u32x2 x = {w[0], w[1]};
             *reinterpret_cast<u32x2 *>(p) = x;
@@ -446,6 +465,25 @@ __device__ __forceinline__ void segment_steps(const uint32_t (&dw)[(T / 2 + 1) /
     }
 }
 
+// Step sizes Delta and inputs Delta u of all T tokens of this lane's segment
+// (from their delta and u bits; tokens at or past t1: the identity), computed
+// in the lane itself: the same operations as segment_steps, so the same bits.
+template <bool F16, int T, bool FAST>
+__device__ __forceinline__ void lane_steps(const uint32_t (&dw)[(T + 1) / 2], const uint32_t (&uw)[(T + 1) / 2],
+                                           float bias, bool softplus, int64_t own, int64_t t1, float (&dl)[T],
+                                           float (&du)[T])
+{
+#pragma unroll
+    for (int j = 0; j < T; ++j) {
+        const float v = fmaf(io_to_f32<F16>(half_of<T>(dw, j)), 1.0f, bias);
+        float sv = softplus ? softplus_f32(v) : v;
+        if (!FAST)
+            sv = own + j < t1 ? sv : 0.0f;
+        dl[j] = sv;
+        du[j] = fmaf(sv, io_to_f32<F16>(half_of<T>(uw, j)), 0.0f);
+    }
+}
+
 // After a pass, yy holds the lower group's partial in the lower half and the
 // upper group's in the upper half, over the whole segment. Trade them so
 // that each lane holds both partials of its own T/2 tokens, and add them to
@@ -624,6 +662,97 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
     }
 }
 
+// Stage round r's B and C rows of one block into LDS: RS rows of B then RS
+// of C, BLOCK tokens each from token blk, as 16-byte pieces spread over the
+// workgroup's NT threads (piece q lands at sBC + 8 q). FAST: the block lies
+// inside the chunk with aligned rows, so every thread requests all its
+// pieces (at most eight at a time) before writing any; otherwise each piece
+// is built from clamped 16-bit reads, one at a time, and tokens at or past t1
+// read as 0. Rows past d_state are staged as zeros. first() runs once: while
+// the first batch of pieces is in flight (FAST), or after the last piece.
+// When the pieces divide evenly (every thread stages the same number, half
+// of them in B rows), a thread's piece `it` lies in row row0 + it * RSTEP of
+// B (first half) or of C (second half) at its fixed column piece, so with
+// every state live its address is a uniform row pointer plus the thread's
+// fixed byte offset (offB, offC; the host keeps RS row strides below 2^30
+// elements).
+template <int BLOCK, int RS, int NT, bool FULL, bool FAST, typename First>
+__device__ __forceinline__ void stage_rows(uint16_t *sBC, const uint16_t *Bbase, const uint16_t *Cbase, int64_t B_n,
+                                           int64_t C_n, int64_t blk, int64_t t1, int r, int dstate, int tid,
+                                           uint32_t offB, uint32_t offC, First first)
+{
+    constexpr int CPR = BLOCK / 8, PIECES = 2 * RS * CPR, ITERS = (PIECES + NT - 1) / NT;
+    constexpr bool kAllPieces = PIECES % NT == 0;
+    constexpr bool kSplitRows = kAllPieces && ITERS % 2 == 0 && NT % CPR == 0;
+    auto piece_src = [&](int q, bool &live) -> const uint16_t * {
+        const int row = q / CPR, k = q - row * CPR;
+        const bool isC = row >= RS;
+        const int n = r * RS + (isC ? row - RS : row);
+        const int nn = FULL ? n : min(n, dstate - 1);
+        live = FULL || n < dstate;
+        return (isC ? Cbase + nn * C_n : Bbase + nn * B_n) + blk + 8 * k;
+    };
+    auto split_src = [&](int it, bool &live) -> const uint16_t * {
+        constexpr int RSTEP = NT / CPR;
+        const bool isC = it >= ITERS / 2;
+        const int nb = r * RS + (isC ? it - ITERS / 2 : it) * RSTEP;  // the piece's row for row0 = 0
+        if constexpr (FULL) {
+            live = true;
+            const uint16_t *rowp = (isC ? Cbase + nb * C_n : Bbase + nb * B_n) + blk;
+            return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(rowp) + (isC ? offC : offB));
+        } else {
+            const int row0 = tid / CPR, col = tid - row0 * CPR;
+            const int n = nb + row0;
+            const int nn = min(n, dstate - 1);
+            live = n < dstate;
+            return (isC ? Cbase + nn * C_n : Bbase + nn * B_n) + blk + 8 * col;
+        }
+    };
+    if constexpr (FAST) {
+        constexpr int BATCH = ITERS < 8 ? ITERS : 8;
+#pragma unroll
+        for (int i0 = 0; i0 < ITERS; i0 += BATCH) {
+            u32x4 v[BATCH];
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int q = tid + (i0 + i) * NT;
+                v[i] = u32x4{0u, 0u, 0u, 0u};
+                if (kAllPieces || q < PIECES) {
+                    bool live;
+                    const uint16_t *src = kSplitRows ? split_src(i0 + i, live) : piece_src(q, live);
+                    const u32x4 x = *reinterpret_cast<const u32x4 *>(src);
+                    v[i] = live ? x : u32x4{0u, 0u, 0u, 0u};
+                }
+            }
+            if (i0 == 0)
+                first();
+#pragma unroll
+            for (int i = 0; i < BATCH; ++i) {
+                const int q = tid + (i0 + i) * NT;
+                if (kAllPieces || q < PIECES)
+                    *reinterpret_cast<u32x4 *>(sBC + 8 * q) = v[i];
+            }
+        }
+    } else {
+#pragma unroll 1
+        for (int q = tid; q < PIECES; q += NT) {
+            bool live;
+            const uint16_t *src = piece_src(q, live);
+            const int64_t t8 = blk + 8 * (q % CPR);
+            uint32_t e[8];
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int64_t t = t8 + j;
+                const uint32_t h = src[(t < t1 ? t : t1 - 1) - t8];
+                e[j] = (live && t < t1) ? h : 0u;
+            }
+            *reinterpret_cast<u32x4 *>(sBC + 8 * q) =
+                u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
+        }
+        first();
+    }
+}
+
 // Layout of one workgroup's LDS (dynamic, 16-byte aligned):
 //   sBC [2 * RS][BLOCK] u16      the round's B rows, then its C rows;
 //   sY  [W - 1][GROUPS][CPW][BLOCK] f32  partials of y (by own token) that
@@ -654,8 +783,6 @@ ssu_scan_staged_kernel(const ScanParams p)
     using S = ScanShape<T, NSW, W, CPW>;
     constexpr int TH = T / 2, BLOCK = S::BLOCK, WT = (T + 1) / 2, WH = (TH + 1) / 2;
     constexpr int RS = S::RS, GROUPS = S::GROUPS, NT = S::NT;
-    constexpr bool kAllPieces = S::PIECES % NT == 0;  // every thread stages ITERS pieces
-    constexpr bool kSplitRows = kAllPieces && S::ITERS % 2 == 0 && NT % S::CPR == 0;
     extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
     uint16_t *const sBC = reinterpret_cast<uint16_t *>(smem);
     float *const sY = reinterpret_cast<float *>(smem + S::BC_BYTES);
@@ -739,95 +866,15 @@ ssu_scan_staged_kernel(const ScanParams p)
 
         for (int r = 0; r < rounds; ++r) {
             // stage the round's B and C rows into LDS (and, in the first
-            // round, compute the step sizes while the pieces are in flight).
-            // Fast blocks request all their 16-byte pieces (at most 8 per
-            // thread at a time) before writing any; ragged or unaligned
-            // blocks build each piece from clamped 16-bit reads, one at a time.
-            {
-                auto piece_src = [&](int q, bool &live) -> const uint16_t * {
-                    const int row = q / S::CPR, k = q - row * S::CPR;
-                    const bool isC = row >= RS;
-                    const int n = r * RS + (isC ? row - RS : row);
-                    const int nn = FULL ? n : min(n, dstate - 1);
-                    live = FULL || n < dstate;
-                    return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * k;
-                };
-                // When the pieces divide evenly (every thread stages the same
-                // number, half of them in B rows), a thread's piece `it` lies
-                // in row row0 + it * RSTEP of B (first half of the iterations)
-                // or of C (second half), at column piece `col`: its address is
-                // the thread's base plus a uniform step.
-                auto split_src = [&](int it, bool &live) -> const uint16_t * {
-                    constexpr int RSTEP = NT / S::CPR;
-                    const bool isC = it >= S::ITERS / 2;
-                    const int nb = r * RS + (isC ? it - S::ITERS / 2 : it) * RSTEP;  // the piece's row for row0 = 0
-                    if constexpr (FULL) {
-                        // a uniform row pointer plus the thread's fixed byte offset
-                        live = true;
-                        const uint16_t *rowp = (isC ? Cbase + nb * p.C_n : Bbase + nb * p.B_n) + blk;
-                        return reinterpret_cast<const uint16_t *>(reinterpret_cast<const char *>(rowp) +
-                                                                  (isC ? split_offC : split_offB));
-                    } else {
-                        const int row0 = tid / S::CPR, col = tid - row0 * S::CPR;
-                        const int n = nb + row0;
-                        const int nn = min(n, dstate - 1);
-                        live = n < dstate;
-                        return (isC ? Cbase + nn * p.C_n : Bbase + nn * p.B_n) + blk + 8 * col;
-                    }
-                };
-                bool stepped = false;
-                if constexpr (fast) {
-                    constexpr int BATCH = S::ITERS < 8 ? S::ITERS : 8;
-#pragma unroll
-                    for (int i0 = 0; i0 < S::ITERS; i0 += BATCH) {
-                        u32x4 v[BATCH];
-#pragma unroll
-                        for (int i = 0; i < BATCH; ++i) {
-                            const int q = tid + (i0 + i) * NT;
-                            v[i] = u32x4{0u, 0u, 0u, 0u};
-                            if (kAllPieces || q < S::PIECES) {
-                                bool live;
-                                const uint16_t *src = kSplitRows ? split_src(i0 + i, live) : piece_src(q, live);
-                                const u32x4 x = *reinterpret_cast<const u32x4 *>(src);
-                                v[i] = live ? x : u32x4{0u, 0u, 0u, 0u};
-                            }
-                        }
-                        if (r == 0 && i0 == 0) {
-                            if (blk == p.t0)
-                                load_states();
-                            steps();
-                            stepped = true;
-                        }
-#pragma unroll
-                        for (int i = 0; i < BATCH; ++i) {
-                            const int q = tid + (i0 + i) * NT;
-                            if (kAllPieces || q < S::PIECES)
-                                *reinterpret_cast<u32x4 *>(sBC + 8 * q) = v[i];
-                        }
-                    }
-                } else {
-#pragma unroll 1
-                    for (int q = tid; q < S::PIECES; q += NT) {
-                        bool live;
-                        const uint16_t *src = piece_src(q, live);
-                        const int64_t t8 = blk + 8 * (q % S::CPR);
-                        uint32_t e[8];
-#pragma unroll
-                        for (int j = 0; j < 8; ++j) {
-                            const int64_t t = t8 + j;
-                            const uint32_t h = src[(t < p.t1 ? t : p.t1 - 1) - t8];
-                            e[j] = (live && t < p.t1) ? h : 0u;
-                        }
-                        *reinterpret_cast<u32x4 *>(sBC + 8 * q) =
-                            u32x4{e[0] | (e[1] << 16), e[2] | (e[3] << 16), e[4] | (e[5] << 16), e[6] | (e[7] << 16)};
-                    }
-                }
-                if (r == 0 && !stepped) {
-                    if (blk == p.t0)
-                        load_states();
-                    steps();
-                }
-            }
+            // round, compute the step sizes while the pieces are in flight)
+            stage_rows<BLOCK, RS, NT, FULL, fast>(sBC, Bbase, Cbase, p.B_n, p.C_n, blk, p.t1, r, dstate, tid,
+                                                   split_offB, split_offC, [&] {
+                                                       if (r == 0) {
+                                                           if (blk == p.t0)
+                                                               load_states();
+                                                           steps();
+                                                       }
+                                                   });
             __syncthreads();
 
             // this wave's states of the round, in passes of two groups: the
@@ -935,6 +982,187 @@ ssu_scan_staged_kernel(const ScanParams p)
     }
 }
 
+// Layout of a paired workgroup's LDS (dynamic, 16-byte aligned):
+//   sBC [2 * RS][BLOCK] u16      the round's B rows, then its C rows;
+//   sH  [NCH][rounds * RS] f32   the carried states (0 past d_state);
+//   sA  [NCH][rounds * RS] f32   A * log2(e) (0 past d_state);
+//   16 bytes of padding (read, never used).
+template <int T, int RS, int CPW>
+struct PairShape {
+    static constexpr int BLOCK = kHalf * T;
+    static constexpr int NCH = 2 * CPW;        // channels: one per half-wave
+    static constexpr int NT = kLanes * CPW;    // threads
+    static constexpr size_t BC_BYTES = size_t(2) * RS * BLOCK * 2;
+    static size_t lds_bytes(int rounds) { return BC_BYTES + size_t(2) * NCH * rounds * RS * 4 + 16; }
+};
+
+// The paired kernel: a workgroup holds 2 * CPW channels of one (request,
+// group) in CPW waves; each half of a wave holds one channel, over the whole
+// block (lane i: tokens i * T .. i * T + T - 1), and walks every state of it,
+// RS states per round with the round's B and C rows staged in LDS as in the
+// staged kernel. Both halves step through the same state at once, so they
+// read the same staged rows. Nothing crosses from one half into the other:
+// each lane computes the step sizes of its own segment and adds its own
+// partials, in the same order as the other kernels (yy over a group of 4
+// states by fma in state order, then y += yy in group order), so the results
+// are bitwise those of the other kernels with the same T.
+template <bool F16, int T, int RS, int CPW, bool FULL, bool ALLFAST>
+__global__ void __launch_bounds__(kLanes * CPW) __attribute__((amdgpu_waves_per_eu(T >= 16 ? 3 : 4)))
+ssu_scan_paired_kernel(const ScanParams p)
+{
+    using S = PairShape<T, RS, CPW>;
+    constexpr int BLOCK = S::BLOCK, NT = S::NT, NCH = S::NCH, WT = (T + 1) / 2;
+    constexpr int CPR = BLOCK / 8;  // 16-byte pieces per staged row
+    extern __shared__ __attribute__((aligned(16))) unsigned char smem[];
+    uint16_t *const sBC = reinterpret_cast<uint16_t *>(smem);
+    float *const sH = reinterpret_cast<float *>(smem + S::BC_BYTES);
+    const int rounds = p.rounds;
+    const int HP = rounds * RS;
+    float *const sA = sH + NCH * HP;
+
+    const int tid = static_cast<int>(threadIdx.x);
+    const int lane = tid & (kLanes - 1);
+    const int li = lane & (kHalf - 1), hl = lane >> 5;
+    const bool half_first = li == 0;
+    const int wv = __builtin_amdgcn_readfirstlane(tid / kLanes);
+    const int c = 2 * wv + hl;  // this half's channel slot
+    const int64_t bd0 = static_cast<int64_t>(blockIdx.x) * NCH;
+    const int64_t b = bd0 / p.dim;  // every channel of the group shares it
+    const int d0 = static_cast<int>(bd0 - b * p.dim);
+    const int d = d0 + c;
+    const int grp = d0 / p.ch_per_group;
+    const int dstate = p.dstate;
+
+    const uint16_t *const Bbase = p.B + b * p.B_b + grp * p.B_g;
+    const uint16_t *const Cbase = p.C + b * p.C_b + grp * p.C_g;
+    const uint16_t *const u_row = p.u + b * p.u_b + d * p.u_d;
+    const uint16_t *const dl_row = p.delta + b * p.dl_b + d * p.dl_d;
+    const float bias = p.bias ? load_ro(p.bias + d) : 0.0f;
+    const float Dd = p.D ? load_ro(p.D + d) : 0.0f;
+    const bool softplus = p.softplus != 0;
+
+    // carried states (plain loads: this kernel writes the state) and decay
+    // rates A * log2(e) into LDS, in the first block after its staging loads
+    // are requested
+    auto load_states = [&]() {
+        for (int i = tid; i < NCH * HP; i += NT) {
+            const int cc = i / HP, n = i - cc * HP;
+            const int nn = FULL ? n : min(n, dstate - 1);
+            const float *st = p.state + b * p.st_b + (d0 + cc) * p.st_d;
+            const float av = load_ro(p.A + (d0 + cc) * p.A_d + nn * p.A_n);
+            sH[i] = (FULL || n < dstate) ? st[nn] : 0.0f;
+            sA[i] = (FULL || n < dstate) ? av * kLog2e : 0.0f;
+        }
+    };
+
+    const uint32_t split_offB = static_cast<uint32_t>(((tid / CPR) * p.B_n + 8 * (tid % CPR)) * 2);
+    const uint32_t split_offC = static_cast<uint32_t>(((tid / CPR) * p.C_n + 8 * (tid % CPR)) * 2);
+    const int lown = li * T;  // this lane's tokens, from the block's start
+    const uint16_t *const sB = sBC + lown;
+    const uint16_t *const sC = sBC + RS * BLOCK + lown;
+
+    auto block = [&](int64_t blk, auto fast_tag) {
+        constexpr bool fast = decltype(fast_tag)::value;
+        const int64_t own = blk + lown;
+
+        uint32_t uw[WT], dw[WT];
+        if constexpr (fast) {
+            load_seg<T, true>(u_row + blk, lown, 0, uw);
+            load_seg<T, true>(dl_row + blk, lown, 0, dw);
+        } else {
+            load_seg<T, false>(u_row, own, p.t1, uw);
+            load_seg<T, false>(dl_row, own, p.t1, dw);
+        }
+        float dl[T], du[T], y[T], dls = 0.0f;
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+            y[j] = -0.0f;
+
+        for (int r = 0; r < rounds; ++r) {
+            stage_rows<BLOCK, RS, NT, FULL, fast>(sBC, Bbase, Cbase, p.B_n, p.C_n, blk, p.t1, r, dstate, tid,
+                                                   split_offB, split_offC, [&] {
+                                                       if (r == 0) {
+                                                           if (blk == p.t0)
+                                                               load_states();
+                                                           lane_steps<F16, T, fast>(dw, uw, bias, softplus, own,
+                                                                                    p.t1, dl, du);
+                                                           dls = step_sum<T>(dl);
+                                                       }
+                                                   });
+            __syncthreads();
+
+            // the round's states in groups of 4; a step's carried value, decay
+            // rate and B row are read from LDS while the step before replays
+            // its tokens, its C row at its own start
+            float *const hrow = sH + c * HP + r * RS;
+            const float *const arow = sA + c * HP + r * RS;
+#pragma unroll 1
+            for (int n0 = 0; n0 < RS; n0 += kGroup) {
+                float yy[T];
+                float hv = hrow[n0], av = arow[n0];
+                uint32_t Bw[WT];
+                lds_seg<T>(sB + n0 * BLOCK, Bw);
+                auto step = [&](int k, auto first_tag) {
+                    const int n = n0 + k;
+                    const int nx = n + 1;  // past the round's last: read, unused (LDS has a padding word)
+                    uint32_t Cw[WT];
+                    lds_seg<T>(sC + n * BLOCK, Cw);
+                    const float e = scan_step<F16, T, true, decltype(first_tag)::value>(
+                        dl, du, dls, av, Bw, Cw, hv, half_first, yy, [&] {
+                            hv = hrow[nx];
+                            av = arow[nx];
+                            lds_seg<T>(sB + nx * BLOCK, Bw);
+                        });
+                    if (li == kHalf - 1)
+                        hrow[n] = e;
+                };
+                step(0, std::true_type{});
+#pragma unroll 1
+                for (int k = 1; k < kGroup; ++k)
+                    step(k, std::false_type{});
+#pragma unroll
+                for (int j = 0; j < T; ++j)
+                    y[j] += yy[j];
+            }
+            // every wave is done with this round's rows before they are
+            // overwritten
+            __syncthreads();
+        }
+
+        // u again for the D u term
+        uint32_t uo[WT];
+        uint16_t o[T];
+        if constexpr (fast)
+            load_seg<T, true>(u_row + blk, lown, 0, uo);
+        else
+            load_seg<T, false>(u_row, own, p.t1, uo);
+#pragma unroll
+        for (int j = 0; j < T; ++j)
+            o[j] = f32_to_io<F16>(fmaf(Dd, io_to_f32<F16>(half_of<T>(uo, j)), y[j]));
+        if constexpr (fast)
+            store_seg<T, true>(p.out + b * p.o_b + d * p.o_d + blk, lown, 0, o);
+        else
+            store_seg<T, false>(p.out + b * p.o_b + d * p.o_d, own, p.t1, o);
+    };
+    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+        if constexpr (ALLFAST) {
+            block(blk, std::true_type{});
+        } else {
+            if (p.vec && blk + BLOCK <= p.t1)
+                block(blk, std::true_type{});
+            else
+                block(blk, std::false_type{});
+        }
+    }
+
+    // final states: every half wrote its own to LDS
+    __syncthreads();
+    for (int i = tid; i < NCH * dstate; i += NT) {
+        const int cc = i / dstate, n = i - cc * dstate;
+        p.state[b * p.st_b + (d0 + cc) * p.st_d + n] = sH[cc * HP + n];
+    }
+}
+
 // Launchers: every configuration takes the channel count and sets its own
 // grid, workgroup size and LDS.
 using ScanFn = hipError_t (*)(const ScanParams &, int64_t channels, hipStream_t);
@@ -965,6 +1193,15 @@ hipError_t launch_staged(const ScanParams &p, int64_t channels, hipStream_t stre
     return hipGetLastError();
 }
 
+template <bool F16, int T, int RS, int CPW, bool FULL, bool ALLFAST>
+hipError_t launch_paired(const ScanParams &p, int64_t channels, hipStream_t stream)
+{
+    using S = PairShape<T, RS, CPW>;
+    hipLaunchKernelGGL((ssu_scan_paired_kernel<F16, T, RS, CPW, FULL, ALLFAST>), dim3(channels / S::NCH),
+                       dim3(S::NT), S::lds_bytes(p.rounds), stream, p);
+    return hipGetLastError();
+}
+
 // A launch configuration: T tokens per lane, NSW states per wave; staged ones
 // also W waves per channel and CPW channels per workgroup. rs: states per
 // round (per wave for direct ones); ealign: the element alignment (of every
@@ -973,7 +1210,7 @@ hipError_t launch_staged(const ScanParams &p, int64_t channels, hipStream_t stre
 // for ragged or unaligned blocks, so fewer registers.
 struct ScanTile {
     int seg, nsw, waves, cpw, rs, ealign;
-    bool staged;
+    bool staged, paired;
     ScanFn fn[2][2][2];
     char name[32];
 };
@@ -988,6 +1225,12 @@ template <bool FULL, bool F16, bool ALLFAST, int T, int NSW, int W, int CPW>
 void set_staged(ScanTile &t)
 {
     t.fn[FULL][F16][ALLFAST] = &launch_staged<F16, T, NSW, W, CPW, FULL, ALLFAST>;
+}
+
+template <bool FULL, bool F16, bool ALLFAST, int T, int RS, int CPW>
+void set_paired(ScanTile &t)
+{
+    t.fn[FULL][F16][ALLFAST] = &launch_paired<F16, T, RS, CPW, FULL, ALLFAST>;
 }
 
 // Direct loads: a lane's own T/2 tokens of u, delta and out, its T-token
@@ -1019,6 +1262,21 @@ ScanTile staged_tile()
     return t;
 }
 
+// Paired ones: rs states per round, cpw = 2 * CPW channels per workgroup (one
+// per half-wave); each lane loads and stores its whole T-token segment.
+template <int T, int RS, int CPW>
+ScanTile paired_tile()
+{
+    ScanTile t{};
+    t.seg = T, t.nsw = RS, t.waves = 1, t.cpw = 2 * CPW, t.rs = RS, t.ealign = 8, t.staged = true, t.paired = true;
+    set_paired<false, false, false, T, RS, CPW>(t), set_paired<false, false, true, T, RS, CPW>(t);
+    set_paired<false, true, false, T, RS, CPW>(t), set_paired<false, true, true, T, RS, CPW>(t);
+    set_paired<true, false, false, T, RS, CPW>(t), set_paired<true, false, true, T, RS, CPW>(t);
+    set_paired<true, true, false, T, RS, CPW>(t), set_paired<true, true, true, T, RS, CPW>(t);
+    std::snprintf(t.name, sizeof t.name, "scan_t%d_n%d_pair_c%d", T, RS, 2 * CPW);
+    return t;
+}
+
 template <int T>
 void add_scan_tiles(ScanTile *&t)
 {
@@ -1028,9 +1286,10 @@ void add_scan_tiles(ScanTile *&t)
     *t++ = staged_tile<T, 16, 1, 8>();
     *t++ = staged_tile<T, 16, 1, 2>();
     *t++ = staged_tile<T, 8, 2, 4>();
+    *t++ = paired_tile<T, 16, 4>();
 }
 
-constexpr int kScanTiles = 24;
+constexpr int kScanTiles = 28;
 
 const ScanTile *scan_tiles(int *count)
 {
@@ -1049,24 +1308,30 @@ const ScanTile *scan_tiles(int *count)
 }
 
 // Default launch configuration, from a sweep of the configurations on MI355X
-// (d_state 16, 4096 fp16 tokens per request, 1, 2, 4 and 16 requests of 1024
-// channels, static chunk 512 and one launch, cold caches): the largest token
-// segment that a launch still fills (32 lanes x T tokens per block); then by
-// the number of channels:
+// (d_state 16, 4096 fp16 tokens per request, 1, 2, 4, 8 and 16 requests of
+// 1024 channels, static chunk 512 and one launch, cold caches): the largest
+// token segment that a launch still fills (32 lanes x T tokens per block);
+// then by the number of channels:
 //   up to 2048:  the direct kernel, one wave of 16 states per channel (one
 //                request: 59.8 us per sequence at chunk 512 and 33.4 in one
 //                launch, against 64.6 and 35.7 with two waves of 8 states
 //                and 61.8 and 39.7 staged; two requests: 79.9 and 50.3,
 //                against 78.4 and 55.5 staged);
-//   above:       staged, one wave of 16 states per channel, four channels per
-//                workgroup (16 requests: 357.0 and 330.7 us, against 390.5
-//                and 335.2 direct; eight channels per workgroup 499.7 and
-//                422.4, two 506.7 and 464.5: fewer waves fit).
-// Where a group's channels do not split into fours, the direct kernel.
+//   above:       paired, eight channels per workgroup (16 requests: 330.5
+//                and 301.4 us, against 352.7 and 323.4 staged with four
+//                channels per workgroup and 390.5 and 335.2 direct; 8
+//                requests: 195.4 and 162.2 against 200.1 and 169.9; four
+//                channels per workgroup: 439.3 and 415.4, LDS holds too few
+//                workgroups; at chunks of 256, 128 and 64 tokens, 16 requests,
+//                7%, 5% and 13% faster than staged).
+// Where a group's channels do not split into eights, staged with four
+// channels per workgroup, and where they do not split into fours either, the
+// direct kernel. Configurations that stage B and C rows need their row
+// strides to fit 32-bit offsets (staged_rows_fit); otherwise direct.
 constexpr int64_t kDirectChannels = 2048;
 
-// Staged kernels address a thread's staging pieces as a 32-bit byte offset
-// from a row pointer, over at most kMaxStates rows of B and of C.
+// The staged and paired kernels address a thread's staging pieces as a 32-bit
+// byte offset from a row pointer, over at most kMaxStates rows of B and of C.
 bool staged_rows_fit(int64_t B_n, int64_t C_n)
 {
     return std::max(B_n, C_n) < (int64_t(1) << 30) / kMaxStates;
@@ -1082,12 +1347,15 @@ int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool sta
             seg = sg;
             break;
         }
-    const bool staged = staged_ok && channels > kDirectChannels && ch_per_group % 4 == 0;
+    const bool wide = staged_ok && channels > kDirectChannels;
+    const bool paired = wide && ch_per_group % 8 == 0;
+    const bool staged = wide && !paired && ch_per_group % 4 == 0;
     for (int i = 0; i < count; ++i) {
         const ScanTile &x = t[i];
-        if (x.seg != seg || x.staged != staged || x.nsw != 16)
+        if (x.seg != seg || x.nsw != 16)
             continue;
-        if (!staged || (x.cpw == 4 && x.waves == 1))
+        if (paired ? (x.paired && x.cpw == 8)
+                   : staged ? (x.staged && !x.paired && x.cpw == 4 && x.waves == 1) : !x.staged)
             return i;
     }
     return 0;

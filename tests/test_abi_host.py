@@ -525,18 +525,20 @@ def test_scan_other_rejections(ssu):
     assert _scan_call(ssu, a, chunk=-1) == 1
     assert _scan_call(ssu, a, tile=ssu._lib.ssu_scan_tile_count()) == 1
     assert _scan_call(ssu, a, tile=-2) == 1
-    assert ssu._lib.ssu_scan_tile_count() == len(ssu.scan_tiles()) == 24
+    assert ssu._lib.ssu_scan_tile_count() == len(ssu.scan_tiles()) == 28
     assert ssu._lib.ssu_scan_tile_name(0).decode().startswith("scan_")
     assert ssu._lib.ssu_scan_tile_name(99) == b""
 
 
-def test_scan_staged_needs_32bit_row_offsets(ssu):
-    """A staged launch configuration addresses its staging pieces as 32-bit
-    byte offsets from a row pointer: B or C state strides of 2^30 / 64 elements
-    or more are refused for it before any launch (the default then picks the
-    direct kernel, which takes 64-bit addresses)."""
+@pytest.mark.parametrize("prefix", ["scan_t16_n16_w1_c4", "scan_t16_n16_pair_c8"])
+def test_scan_staged_needs_32bit_row_offsets(ssu, prefix):
+    """A launch configuration that stages B and C rows in LDS (staged and
+    paired) addresses its staging pieces as 32-bit byte offsets from a row
+    pointer: B or C state strides of 2^30 / 64 elements or more are refused for
+    it before any launch (the default then picks the direct kernel, which takes
+    64-bit addresses)."""
     names = ssu.scan_tiles()
-    staged = next(i for i, n in enumerate(names) if n.startswith("scan_t16_n16_w1_c4"))
+    staged = next(i for i, n in enumerate(names) if n.startswith(prefix))
     a = _scan_args(ssu, dim=32)
     a.B.stride[2] = (1 << 30) // 64
     assert _scan_call(ssu, a, tile=staged) == 2
