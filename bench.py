@@ -730,7 +730,8 @@ def run_scan(a):
                 warm = statistics.median([time_graph_on(g, 10, side) / (10 * calls) for _ in range(5)]) * 1e6
                 del g
                 gbs = nbytes / (us * 1e-6) / 1e9
-                tname = ssu.scan_tiles()[tile] if tile >= 0 else "default"
+                tname = (ssu.scan_tiles()[tile] if tile >= 0
+                         else "default=" + ssu.scan_tiles()[ssu.scan_select_tile(args[0], chunk)])
                 print(f"{k} {chunk} {launches} {us:.2f} {us / 1e3:.4f} {bs * L / us:.2f} {gbs:.1f} "
                       f"{100 * gbs / HBM_PEAK_GBS:.2f} {scan_elements(bs, dim, N, L) / (us * 1e3):.1f} {warm:.2f} "
                       f"{tname} {bs}", file=out, flush=True)

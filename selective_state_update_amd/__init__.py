@@ -35,6 +35,7 @@ __all__ = [
     "make_scan_args",
     "selective_scan",
     "scan_launch",
+    "scan_select_tile",
     "scan_tiles",
     "tile_fits",
     "tiles",
@@ -149,6 +150,8 @@ _lib.ssu_scan_tile_count.argtypes = []
 _lib.ssu_scan_tile_count.restype = _i32
 _lib.ssu_scan_tile_name.argtypes = [_i32]
 _lib.ssu_scan_tile_name.restype = ctypes.c_char_p
+_lib.ssu_scan_select_tile.argtypes = [ctypes.POINTER(ScanArgs), _i64]
+_lib.ssu_scan_select_tile.restype = _i32
 _lib.ssu_abi_version.argtypes = []
 _lib.ssu_abi_version.restype = _i32
 
@@ -535,6 +538,12 @@ def make_scan_args(u, delta, A, B, C, state, D=None, delta_bias=None, delta_soft
         setattr(a, name, _view(t, t.stride(), _dtype_tag(t, (SSU_F32,), name)))
     a.out = _view(out, out.stride(), ut)
     return a, out
+
+
+def scan_select_tile(args, chunk=0):
+    """Index of the configuration ssu_scan picks for prepared ScanArgs and
+    ``chunk`` (see include/ssu.h, ssu_scan_select_tile); -1 for invalid sizes."""
+    return int(_lib.ssu_scan_select_tile(ctypes.byref(args), int(chunk)))
 
 
 def scan_launch(args, chunk=0, tile=-1, stream=None, device=None):

@@ -1309,14 +1309,21 @@ const ScanTile *scan_tiles(int *count)
 
 // Default launch configuration, from a sweep of the configurations on MI355X
 // (d_state 16, 4096 fp16 tokens per request, 1, 2, 4, 8 and 16 requests of
-// 1024 channels, static chunk 512 and one launch, cold caches): the largest
-// token segment that a launch still fills (32 lanes x T tokens per block);
-// then by the number of channels:
-//   up to 2048:  the direct kernel, one wave of 16 states per channel (one
-//                request: 59.8 us per sequence at chunk 512 and 33.4 in one
-//                launch, against 64.6 and 35.7 with two waves of 8 states
-//                and 61.8 and 39.7 staged; two requests: 79.9 and 50.3,
-//                against 78.4 and 55.5 staged);
+// 1024 channels, static chunks 128 to 4096 and one launch, cold caches): the
+// largest token segment that a launch still fills (32 lanes x T tokens per
+// block); then by the number of channels:
+//   up to 1024:  the direct kernel, one wave of 16 states per channel (one
+//                request: 59.7 us per sequence at chunk 512 and 33.4 in one
+//                launch, against 64.6 and 35.7 with two waves of 8 states;
+//                staged the same at chunks up to 512, slower above: 41.5
+//                against 38.9 at chunk 2048, 38.3 against 33.4 in one launch;
+//                paired 81.7 and 60.4);
+//   up to 2048:  staged, four channels per workgroup, where a launch spans at
+//                most 1024 tokens (two requests: 77.1 against 80.3 us at
+//                chunk 512, 65.0 against 66.4 at 1024, 114.4 against 117.4 at
+//                256, 189.8 against 200.6 at 128); direct above (57.6 against
+//                56.5 at chunk 2048, 53.9 against 50.4 in one launch; paired
+//                86.4 and 62.6);
 //   above:       paired, eight channels per workgroup (16 requests: 330.5
 //                and 301.4 us, against 352.7 and 323.4 staged with four
 //                channels per workgroup and 390.5 and 335.2 direct; 8
@@ -1328,7 +1335,7 @@ const ScanTile *scan_tiles(int *count)
 // channels per workgroup, and where they do not split into fours either, the
 // direct kernel. Configurations that stage B and C rows need their row
 // strides to fit 32-bit offsets (staged_rows_fit); otherwise direct.
-constexpr int64_t kDirectChannels = 2048;
+constexpr int64_t kDirectChannels = 1024, kStagedChannels = 2048, kStagedSpan = 1024;
 
 // The staged and paired kernels address a thread's staging pieces as a 32-bit
 // byte offset from a row pointer, over at most kMaxStates rows of B and of C.
@@ -1347,8 +1354,8 @@ int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool sta
             seg = sg;
             break;
         }
-    const bool wide = staged_ok && channels > kDirectChannels;
-    const bool paired = wide && ch_per_group % 8 == 0;
+    const bool wide = staged_ok && (channels > kStagedChannels || (channels > kDirectChannels && span <= kStagedSpan));
+    const bool paired = wide && channels > kStagedChannels && ch_per_group % 8 == 0;
     const bool staged = wide && !paired && ch_per_group % 4 == 0;
     for (int i = 0; i < count; ++i) {
         const ScanTile &x = t[i];
@@ -1359,6 +1366,15 @@ int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool sta
             return i;
     }
     return 0;
+}
+
+// The default for a call (sizes already checked): by the span of one launch,
+// the channels, the channels per group and B's and C's state strides.
+int default_scan_tile(const ssu_scan_args &a, int64_t chunk)
+{
+    const int64_t L = a.seqlen;
+    return default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, static_cast<int64_t>(a.batch) * a.dim,
+                             a.dim / a.ngroups, staged_rows_fit(a.B.stride[2], a.C.stride[2]));
 }
 
 bool is_io(const ssu_view &v) { return v.dtype == SSU_F16 || v.dtype == SSU_BF16; }
@@ -1380,6 +1396,14 @@ const char *ssu_scan_tile_name(int32_t tile)
     int count = 0;
     const ssu::ScanTile *t = ssu::scan_tiles(&count);
     return (tile >= 0 && tile < count) ? t[tile].name : "";
+}
+
+int32_t ssu_scan_select_tile(const ssu_scan_args *a, int64_t chunk)
+{
+    if (!a || chunk < 0 || a->batch < 0 || a->dim <= 0 || a->ngroups <= 0 || a->seqlen < 0 || a->dim % a->ngroups ||
+        a->B.stride[2] < 0 || a->C.stride[2] < 0)
+        return -1;
+    return ssu::default_scan_tile(*a, chunk);
 }
 
 ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStream_t stream)
@@ -1460,8 +1484,7 @@ ssu_status ssu_scan(const ssu_scan_args *a, int64_t chunk, int32_t tile, hipStre
     const int ch_per_group = dim / G;
     const int64_t channels = static_cast<int64_t>(bs) * dim;
     const bool staged_ok = staged_rows_fit(a->B.stride[2], a->C.stride[2]);
-    const int t = tile >= 0 ? tile
-                            : default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, channels, ch_per_group, staged_ok);
+    const int t = tile >= 0 ? tile : default_scan_tile(*a, chunk);
     const ScanTile &T = tiles[t];
     if (ch_per_group % T.cpw)
         return fail(SSU_ERR_UNSUPPORTED, "ssu_scan: %s needs the channels of a group (%d) in multiples of %d", T.name,

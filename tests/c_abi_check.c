@@ -76,6 +76,7 @@ int main(void)
 
     /* the scan */
     EXPECT(ssu_scan_tile_count() > 0 && ssu_scan_tile_name(0)[0] != '\0');
+    EXPECT(ssu_scan_select_tile(NULL, 0) == -1);
     ssu_scan_args sa;
     memset(&sa, 0, sizeof sa);
     sa.dim = 1024, sa.dstate = 16, sa.ngroups = 1, sa.seqlen = 4096, sa.delta_softplus = 1;

@@ -183,6 +183,37 @@ def test_scan_every_tile_more_states(N):
                 assert np.array_equal(o, o0) and np.array_equal(s, s0), (name, n0, chunk)
 
 
+@pytest.mark.parametrize("batch,dim,G,want", [
+    (3, 1024, 1, "scan_t16_n16_pair_c8"),
+    (3, 1028, 1, "scan_t16_n16_w1_c4"),
+    (3, 1032, 2, "scan_t16_n16_w1_c4"),
+    (3, 1026, 1, "scan_t16_n16"),
+    (2, 1024, 1, "scan_t16_n16_w1_c4"),
+])
+def test_scan_default_rule_branches(batch, dim, G, want):
+    """The default rule's branches at chunk 512: above 2048 channels paired
+    where a group's channels split into eights, staged where only into fours,
+    direct otherwise; staged at 2048 channels. The default picks `want`,
+    matches the oracle everywhere (a ragged last block, chunk 512 and one
+    launch, which picks direct at 2048 channels), and equals the forced
+    direct configuration bitwise."""
+    import oracle
+    import selective_state_update_amd as ssu
+
+    p = si.make_scan_problem(batch, dim, 16, 1100, G, io="f16", seed=dim + G + batch, zero_state=False)
+    ds = DeviceScan(p)
+    a, _ = ssu.make_scan_args(ds.u, ds.delta, ds.A, ds.B, ds.C, ds.state0.clone(), ds.D, ds.bias)
+    names = ssu.scan_tiles()
+    assert names[ssu.scan_select_tile(a, 512)] == want
+    r = oracle_scan(oracle.get(), p)
+    direct = names.index("scan_t16_n16")
+    for chunk in (512, 0):
+        o, s = ds.run(chunk=chunk)
+        check(p, o, s, r, f"dim {dim} G {G} {want} chunk {chunk}")
+        od, sd = ds.run(chunk=chunk, tile=direct)
+        assert np.array_equal(o, od) and np.array_equal(s.view(np.uint32), sd.view(np.uint32)), chunk
+
+
 @pytest.mark.parametrize("L", [1, 7, 63, 64, 65, 511, 513, 1000])
 @pytest.mark.parametrize("io", ["f16", "bf16"])
 def test_scan_ragged_lengths(L, io):
