@@ -304,6 +304,39 @@ def test_scan_unaligned_views():
     check(p, o, s, oracle_scan(oracle.get(), p), "unaligned chunk 100")
 
 
+def test_scan_unaligned_views_every_tile():
+    """Every launch configuration on views that are not aligned for vector
+    access (the staged and paired kernels then stage B and C element by
+    element): bitwise equal to the same configuration on aligned views, and
+    configurations with the same token segment bitwise equal to each other."""
+    torch = gu.torch_mod()
+    import selective_state_update_amd as ssu
+
+    p = si.make_scan_problem(2, 32, 20, 1300, 2, io="f16", seed=63, zero_state=False)
+    ds = DeviceScan(p)
+
+    def shifted(t):
+        big = torch.zeros(t.shape[:-1] + (t.shape[-1] + 3,), dtype=t.dtype, device=t.device)
+        big[..., 1:1 + t.shape[-1]] = t
+        return big[..., 1:1 + t.shape[-1]]
+
+    views = dict(u=shifted(ds.u), delta=shifted(ds.delta), B=shifted(ds.B), C=shifted(ds.C))
+    first = {}
+    for tile, name in enumerate(ssu.scan_tiles()):
+        oa, sa = ds.run(chunk=512, tile=tile)
+        ou, su = ds.run(chunk=512, tile=tile, views=views)
+        assert np.array_equal(ou, oa) and np.array_equal(su.view(np.uint32), sa.view(np.uint32)), name
+        seg = name.split("_")[1]
+        if seg in first:
+            n0, o0, s0 = first[seg]
+            assert np.array_equal(oa, o0) and np.array_equal(sa.view(np.uint32), s0.view(np.uint32)), (name, n0)
+        else:
+            first[seg] = (name, oa, sa)
+    import oracle
+
+    check(p, first["t16"][1], first["t16"][2], oracle_scan(oracle.get(), p), "unaligned every tile")
+
+
 def test_scan_batch_and_strided_state():
     """Several requests with a state that is a strided view into a larger
     buffer (rows of a state pool), and the output of one request unaffected by
