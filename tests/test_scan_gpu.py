@@ -156,13 +156,14 @@ def test_scan_every_tile():
             check(p, o, s, r, f"{name} chunk {chunk}")
 
 
-@pytest.mark.parametrize("N", [17, 32, 48, 64])
+@pytest.mark.parametrize("N", [1, 5, 17, 32, 48, 64])
 def test_scan_every_tile_more_states(N):
-    """Every launch configuration at d_state above one wave's 16 states (the
-    staged configurations then stage their rows in several rounds, the direct
-    ones run several waves per channel), with a ragged tail and a chunk that
-    splits blocks: within tolerance of the oracle, and the configurations with
-    the same token segment bitwise equal to each other."""
+    """Every launch configuration at d_state other than 16: below it (a
+    partial round, the missing states staged as zeros) and above it (the
+    staged and paired configurations then stage their rows in several rounds,
+    the direct ones run several waves per channel), with a ragged tail and a
+    chunk that splits blocks: within tolerance of the oracle, and the
+    configurations with the same token segment bitwise equal to each other."""
     import oracle
     import selective_state_update_amd as ssu
 
@@ -374,24 +375,28 @@ def test_scan_empty():
     assert out.shape == (0, 16, 5)
 
 
-def test_scan_graph_replays():
-    """The chunked scan captured in a HIP graph: every replay (state reset
-    between replays by an eager copy) matches the eager result bitwise."""
+@pytest.mark.parametrize("tile_name", ["default", "scan_t16_n16_w1_c4", "scan_t16_n16_pair_c8"])
+def test_scan_graph_replays(tile_name):
+    """The chunked scan captured in a HIP graph, in the default configuration
+    and forced to the staged and paired kernels: every replay (state reset
+    between replays by an eager copy) matches the eager default result
+    bitwise."""
     import selective_state_update_amd as ssu
 
     torch = gu.torch_mod()
     name, chunk, p = _config_case(0, False)
+    tile = -1 if tile_name == "default" else ssu.scan_tiles().index(tile_name)
     ds = DeviceScan(p)
     o_ref, s_ref = ds.run(chunk=chunk)
     state = ds.state0.clone()
     args, out = ssu.make_scan_args(ds.u, ds.delta, ds.A, ds.B, ds.C, state, ds.D, ds.bias)
     s = torch.cuda.Stream()
     with torch.cuda.stream(s):
-        ssu.scan_launch(args, chunk, stream=s)  # warm up outside the capture
+        ssu.scan_launch(args, chunk, tile, stream=s)  # warm up outside the capture
     torch.cuda.synchronize()
     g = torch.cuda.CUDAGraph()
     with torch.cuda.graph(g, stream=s):
-        ssu.scan_launch(args, chunk, stream=s)
+        ssu.scan_launch(args, chunk, tile, stream=s)
     for rep in range(3):
         state.copy_(ds.state0)
         out.zero_()
