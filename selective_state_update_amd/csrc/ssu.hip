@@ -45,6 +45,7 @@
 #include <cstdlib>
 #include <cstring>
 #include <new>
+#include <type_traits>
 #include <utility>
 #include <vector>
 
@@ -81,14 +82,13 @@ struct Params {
 
 // ---------------------------------------------------------------- device --
 
-// fp32 -> bf16, round to nearest even; NaN stays a quiet NaN.
+// fp32 -> bf16, round to nearest even (gfx950's v_cvt_pk_bf16_f32; NaN stays
+// NaN). Kept opaque to the compiler so that it is never fused with the fma
+// that produces its operand.
 __device__ __forceinline__ uint16_t bf16_round(float f)
 {
-    uint32_t u = __float_as_uint(f);
-    if ((u & 0x7fffffffu) > 0x7f800000u)
-        return static_cast<uint16_t>((u >> 16) | 0x40u);
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return static_cast<uint16_t>(u >> 16);
+    asm volatile("" : "+v"(f));
+    return __builtin_bit_cast(uint16_t, static_cast<__bf16>(f));
 }
 
 template <int CTRL>
@@ -142,6 +142,29 @@ __device__ __forceinline__ float pick(bool sel, float a, float b)
     return __uint_as_float((__float_as_uint(a) & m) | (__float_as_uint(b) & ~m));
 }
 
+// base + off bytes, for a uniform base and a per-lane 32-bit byte offset: the
+// offset stays a 32-bit value at the access, so the access can take the base
+// from scalar registers and the offset from one vector register (no 64-bit
+// address arithmetic per access).
+// A pointer that is the same in every lane, held in scalar registers.
+template <typename T>
+__device__ __forceinline__ T *uniform_ptr(T *ptr)
+{
+    const uint64_t v = reinterpret_cast<uint64_t>(ptr);
+    const uint32_t lo = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v));
+    const uint32_t hi = __builtin_amdgcn_readfirstlane(static_cast<uint32_t>(v >> 32));
+    using G = __attribute__((address_space(1))) T;  // global memory: global, not flat, accesses
+    return (T *)reinterpret_cast<G *>((static_cast<uint64_t>(hi) << 32) | lo);
+}
+
+template <typename T>
+__device__ __forceinline__ T *lane_at(T *base, uint32_t off)
+{
+    asm volatile("" : "+v"(off));  // (volatile: not hoisted into a loop-carried address)
+    using C = std::conditional_t<std::is_const_v<T>, const char, char>;
+    return reinterpret_cast<T *>(reinterpret_cast<C *>(base) + off);
+}
+
 // Sums of R rows, each split over an aligned group of LPR lanes (LPR in
 // 4..32, R in 1..16), as a reduce-scatter: at level k every lane keeps half of
 // its rows, adds its partner's partial of each kept row and sends the other
@@ -149,46 +172,135 @@ __device__ __forceinline__ float pick(bool sel, float a, float b)
 // levels that remain sum that row as a plain butterfly. Each row's total is
 // the sum over the same pairings in the same order as summing the row alone
 // (fp32 addition commutes), so its bits do not depend on R. On return y[0 ..
-// KEEP) hold the totals of rows first + i, and x[] the matching x values.
+// KEEP) hold the totals of rows first(lane) + i, and the lanes with
+// writer(lane) hold each row once.
+//
+// With 32 lanes per row the first level pairs lane i with i ^ 16 through
+// v_permlane16_swap, which exchanges the odd 16-lane rows of one register
+// with the even rows of another: given a pair of rows (lo, hi), the lower
+// 16 lanes get their partner's lo beside their own and the upper 16 their
+// partner's hi, so the two registers' sum is the kept row in every lane, with
+// no select. The other levels go from the widest pairing to the narrowest
+// (row mirror, half-row mirror, quad permutes), and the choice of kept rows
+// at level k is bit (4, 3, 2^3, 1)[k] of the lane. With 4 to 16 lanes per row
+// the levels go the other way (quad permutes, half-row mirror, row mirror) and
+// the choice is keep_upper().
 template <int LPR, int R>
 struct RowSums {
     static constexpr int log2(int v) { return v <= 1 ? 0 : 1 + log2(v / 2); }
     static constexpr int LEVELS = log2(LPR);
     static constexpr int SPLIT = log2(R) < LEVELS ? log2(R) : LEVELS;
     static constexpr int KEEP = R >> SPLIT;
+    static constexpr bool WIDE = LPR == 32;
     static_assert(LPR >= 4 && LPR <= 32 && (LPR & (LPR - 1)) == 0, "LPR");
     static_assert(R >= 1 && R <= 16 && (R & (R - 1)) == 0, "R");
 
-    template <int K>
-    __device__ __forceinline__ static void level(float (&y)[R], float (&x)[R], int lane, int &first)
+    // lane masks of the 32-lane levels, widest first
+    static constexpr int wide_mask(int k) { return k == 0 ? 16 : k == 1 ? 15 : k == 2 ? 7 : k == 3 ? 2 : 1; }
+    // With 32 lanes per row, lanes that end up holding the same rows differ
+    // only in these bits (the remaining levels' masks, a suffix of 16, 15, 7,
+    // 2, 1, span exactly the bits below their widest).
+    static constexpr int plain_bits()
     {
-        if constexpr (K < LEVELS) {
-            if constexpr (K < SPLIT) {
-                constexpr int HALF = R >> (K + 1);
-                const bool up = keep_upper(lane, K);
-#pragma unroll
-                for (int i = 0; i < HALF; ++i) {
-                    const float lo = y[i], hi = y[i + HALF];
-                    y[i] = pick(up, hi, lo) + partner<K>(pick(up, lo, hi));
-                    x[i] = pick(up, x[i + HALF], x[i]);
-                }
-                first += up ? HALF : 0;
-            } else {
-#pragma unroll
-                for (int i = 0; i < KEEP; ++i)
-                    y[i] += partner<K>(y[i]);
-            }
-            level<K + 1>(y, x, lane, first);
+        int m = 0;
+        for (int k = SPLIT; k < LEVELS; ++k)
+            m |= wide_mask(k);
+        return m;
+    }
+
+    __device__ __forceinline__ static bool keeps_upper(int lane, int k)
+    {
+        if constexpr (WIDE) {
+            const int b1 = (lane >> 1) & 1, b2 = (lane >> 2) & 1, b3 = (lane >> 3) & 1, b4 = (lane >> 4) & 1;
+            return (k == 0 ? b4 : k == 1 ? b3 : k == 2 ? (b2 ^ b3) : b1) != 0;
+        } else {
+            return keep_upper(lane, k);
         }
     }
 
-    // Returns the index of the first row this lane holds.
-    __device__ __forceinline__ static int run(float (&y)[R], float (&x)[R], int lane)
+    // The first of the rows a lane holds at the end: a function of its bits.
+    __device__ __forceinline__ static int first(int lane)
     {
-        int first = 0;
-        level<0>(y, x, lane, first);
-        return first;
+        int f = 0;
+#pragma unroll
+        for (int k = 0; k < SPLIT; ++k)
+            f += keeps_upper(lane, k) ? (R >> (k + 1)) : 0;
+        return f;
     }
+
+    // One lane of each group that holds the same rows (c = the lane within
+    // its row group). With fewer lanes per row, lanes c < R hold rows first(c)
+    // one to one.
+    __device__ __forceinline__ static bool writer(int c)
+    {
+        if constexpr (WIDE)
+            return (c & plain_bits()) == 0;
+        else
+            return R >= LPR || c < R;
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float wide_partner(float v)
+    {
+        static_assert(K >= 1 && K <= 4, "level");
+        if constexpr (K == 1)
+            return dpp<0x140>(v);  // row_mirror: lane i <-> 15 - i of each 16
+        else if constexpr (K == 2)
+            return dpp<0x141>(v);  // row_half_mirror: lane i <-> 7 - i of each 8
+        else if constexpr (K == 3)
+            return dpp<0x4E>(v);   // quad_perm [2,3,0,1]
+        else
+            return dpp<0xB1>(v);   // quad_perm [1,0,3,2]
+    }
+
+    template <int K>
+    __device__ __forceinline__ static float level_partner(float v)
+    {
+        if constexpr (WIDE)
+            return wide_partner<K>(v);
+        else
+            return partner<K>(v);
+    }
+
+    // the sum of a pair's kept row in every lane (see above)
+    __device__ __forceinline__ static float swap16_sum(float lo, float hi)
+    {
+        const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(lo), __float_as_uint(hi), false, false);
+        return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+    }
+
+    template <int K>
+    __device__ __forceinline__ static void level(float (&y)[R], int lane)
+    {
+        if constexpr (K < LEVELS) {
+            if constexpr (WIDE && K == 0) {
+                if constexpr (SPLIT > 0) {
+                    constexpr int HALF = R / 2;
+#pragma unroll
+                    for (int i = 0; i < HALF; ++i)
+                        y[i] = swap16_sum(y[i], y[i + HALF]);
+                } else {
+                    y[0] = swap16_sum(y[0], y[0]);
+                }
+            } else if constexpr (K < SPLIT) {
+                constexpr int HALF = R >> (K + 1);
+                const bool up = keeps_upper(lane, K);
+#pragma unroll
+                for (int i = 0; i < HALF; ++i) {
+                    const float lo = y[i], hi = y[i + HALF];
+                    const float send = pick(up, lo, hi);
+                    y[i] = pick(up, hi, lo) + level_partner<K>(send);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < KEEP; ++i)
+                    y[i] += level_partner<K>(y[i]);
+            }
+            level<K + 1>(y, lane);
+        }
+    }
+
+    __device__ __forceinline__ static void run(float (&y)[R], int lane) { level<0>(y, lane); }
 };
 
 // One lane's share of one tile: `rows_per_group` consecutive state rows of one
@@ -205,8 +317,12 @@ struct Work {
     static constexpr int ROWS_WAVE = RPI * R;
     static_assert(LPR >= 4 && LPR <= 32, "dstate");
 
+    using RS = RowSums<LPR, R>;
+
     bool live;
-    int b, h, grp, c, sub, wrow, p0;
+    int b, h, grp, c, sub, wrow, p0, fr;
+    const uint16_t *xh;  // x of this wave's first row, token 0 (uniform)
+    uint16_t *oh;        // out of this wave's first row, token 0 (uniform)
     float *sp;
     int64_t jstep;
     f32x4 s[R][VEC];
@@ -214,20 +330,26 @@ struct Work {
     float bias, Ah, Dh;
 
     // One token's operands for this lane: its columns of B and C (bf16
-    // pairs) and the x of its rows (bf16 in the upper half of each word).
+    // pairs), the x of its rows and of the rows whose out it writes (bf16 in
+    // the upper half of each word).
     struct Ops {
         u32x2 Bw[VEC], Cw[VEC];
         uint32_t xbits[R];
+        uint32_t xo[RS::KEEP];
     };
     Ops op;  // token 0's, requested by fetch()
 
-    // This lane's columns of B and C for token t (8-byte vector loads).
+    // This lane's columns of B and C for token t (8-byte vector loads at a
+    // uniform row address plus the lane's 32-bit offset).
     __device__ __forceinline__ void load_bc(const Params &p, int t, Ops &o) const
     {
+        const auto *const Bu = reinterpret_cast<const u32x2 *>(p.B + (b * p.B_b + t * p.B_t + grp * p.B_g));
+        const auto *const Cu = reinterpret_cast<const u32x2 *>(p.C + (b * p.C_b + t * p.C_t + grp * p.C_g));
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            o.Bw[v] = *reinterpret_cast<const u32x2 *>(p.B + b * p.B_b + t * p.B_t + grp * p.B_g + 4 * c + 128 * v);
-            o.Cw[v] = *reinterpret_cast<const u32x2 *>(p.C + b * p.C_b + t * p.C_t + grp * p.C_g + 4 * c + 128 * v);
+            const uint32_t off = static_cast<uint32_t>(8 * c + 256 * v);  // bytes
+            o.Bw[v] = *lane_at(Bu, off);
+            o.Cw[v] = *lane_at(Cu, off);
         }
     }
 
@@ -244,7 +366,7 @@ struct Work {
     // address (scalar loads); otherwise each lane reads its own values.
     __device__ __forceinline__ void load_x(const Params &p, int t, Ops &o) const
     {
-        const uint16_t *xrow = p.x + b * p.x_b + t * p.x_t + h * p.x_h + wrow;
+        const uint16_t *xrow = xh + t * p.x_t;
         if constexpr (RPI == 2) {
             // one byte permute per row: this lane's half of the word into the
             // upper half (byte selectors 0-3 name the word's bytes, 0x0C a zero)
@@ -256,8 +378,13 @@ struct Work {
         } else {
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                o.xbits[j] = static_cast<uint32_t>(xrow[sub + j * RPI]) << 16;
+                o.xbits[j] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + j * RPI))) << 16;
         }
+        // the rows this lane's out values belong to: a lane's own load
+        // instead of a select over its rows' x values
+#pragma unroll
+        for (int i = 0; i < RS::KEEP; ++i)
+            o.xo[i] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + (fr + i) * RPI))) << 16;
     }
 
     // delta = softplus(dt + dt_bias) (or dt + dt_bias) and the decay
@@ -286,13 +413,19 @@ struct Work {
         const bool per_head = p.ptiles == 0;
         const int t = per_head ? 0 : g % p.ptiles;
         const int bh = per_head ? g * (rows_group / ROWS_WAVE) + wave : g / p.ptiles;
-        h = bh % p.nheads;
-        b = bh / p.nheads;
-        grp = h / p.heads_per_group;
+        // (uniform values that the divisions leave in vector registers:
+        // moved to scalar ones once, so that every address built from them
+        // is scalar arithmetic)
+        h = __builtin_amdgcn_readfirstlane(bh % p.nheads);
+        b = __builtin_amdgcn_readfirstlane(bh / p.nheads);
+        grp = __builtin_amdgcn_readfirstlane(h / p.heads_per_group);
         c = lane % LPR;    // column chunk
         sub = lane / LPR;  // row within one instruction
-        wrow = per_head ? 0 : t * rows_group + wave * ROWS_WAVE;  // first row of this wave (uniform)
+        fr = RS::first(sub * LPR + c);
+        wrow = __builtin_amdgcn_readfirstlane(per_head ? 0 : t * rows_group + wave * ROWS_WAVE);  // first row of this wave
         p0 = wrow + sub;
+        xh = uniform_ptr(p.x + (b * p.x_b + h * p.x_h + wrow));
+        oh = uniform_ptr(p.out + (b * p.o_b + h * p.o_h + wrow));
 
         // B and C do not depend on the slot: requested first (vector-memory
         // counters retire in order, so anything issued after the state stream
@@ -331,37 +464,34 @@ struct Work {
     template <bool LAST>
     __device__ __forceinline__ void step(const Params &p, int t, const Ops &o, float delta, float dA)
     {
-        float Bv[VEC][4], Cv[VEC][4];
+        // delta * B[n] and C[n] of this lane's columns
+        float dB[VEC][4], Cv[VEC][4];
 #pragma unroll
         for (int v = 0; v < VEC; ++v) {
-            Bv[v][0] = __uint_as_float(o.Bw[v].x << 16);
-            Bv[v][1] = __uint_as_float(o.Bw[v].x & 0xffff0000u);
-            Bv[v][2] = __uint_as_float(o.Bw[v].y << 16);
-            Bv[v][3] = __uint_as_float(o.Bw[v].y & 0xffff0000u);
+            dB[v][0] = delta * __uint_as_float(o.Bw[v].x << 16);
+            dB[v][1] = delta * __uint_as_float(o.Bw[v].x & 0xffff0000u);
+            dB[v][2] = delta * __uint_as_float(o.Bw[v].y << 16);
+            dB[v][3] = delta * __uint_as_float(o.Bw[v].y & 0xffff0000u);
             Cv[v][0] = __uint_as_float(o.Cw[v].x << 16);
             Cv[v][1] = __uint_as_float(o.Cw[v].x & 0xffff0000u);
             Cv[v][2] = __uint_as_float(o.Cw[v].y << 16);
             Cv[v][3] = __uint_as_float(o.Cw[v].y & 0xffff0000u);
         }
-        float xv[R];
-#pragma unroll
-        for (int j = 0; j < R; ++j)
-            xv[j] = __uint_as_float(o.xbits[j]);
 
         // Update in registers (write back after the last token) and form each
         // lane's partial output.
         float y[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const float dx = delta * xv[j];
+            const float xj = __uint_as_float(o.xbits[j]);
             float acc = 0.0f;
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
                 f32x4 &q = s[j][v];
-                q.x = fmaf(q.x, dA, dx * Bv[v][0]);
-                q.y = fmaf(q.y, dA, dx * Bv[v][1]);
-                q.z = fmaf(q.z, dA, dx * Bv[v][2]);
-                q.w = fmaf(q.w, dA, dx * Bv[v][3]);
+                q.x = fmaf(q.x, dA, xj * dB[v][0]);
+                q.y = fmaf(q.y, dA, xj * dB[v][1]);
+                q.z = fmaf(q.z, dA, xj * dB[v][2]);
+                q.w = fmaf(q.w, dA, xj * dB[v][3]);
                 acc = (v == 0) ? q.x * Cv[v][0] : fmaf(q.x, Cv[v][0], acc);
                 acc = fmaf(q.y, Cv[v][1], acc);
                 acc = fmaf(q.z, Cv[v][2], acc);
@@ -375,16 +505,15 @@ struct Work {
             }
         }
 
-        // Row totals: this lane ends up with KEEP of them, rows first + i.
-        // When R < LPR several lanes of a row group hold each row; lane c < R
-        // is its one writer (the map from c to first is one to one on those).
-        using RS = RowSums<LPR, R>;
-        const int first = RS::run(y, xv, sub * LPR + c);  // the wave lane
-        uint16_t *op = p.out + b * p.o_b + t * p.o_t + h * p.o_h + p0;
-        if (R >= LPR || c < R) {
+        // Row totals: this lane ends up with KEEP of them, rows fr + i.
+        // When R < LPR several lanes of a row group hold each row; one of
+        // them writes it.
+        RS::run(y, sub * LPR + c);  // the wave lane
+        uint16_t *const orow = oh + t * p.o_t;
+        if (RS::writer(c)) {
 #pragma unroll
             for (int i = 0; i < RS::KEEP; ++i)
-                op[(first + i) * RPI] = bf16_round(fmaf(Dh, xv[i], y[i]));
+                *lane_at(orow, 2u * (sub + (fr + i) * RPI)) = bf16_round(fmaf(Dh, __uint_as_float(o.xo[i]), y[i]));
         }
     }
 
