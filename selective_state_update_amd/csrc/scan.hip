@@ -547,27 +547,41 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
     }
     const bool vec = p.vec != 0;
 
-    auto block = [&](int64_t blk, auto fast_tag) {
+    // FIRSTB: the launch's first block, which also reads the carried states
+    // and decay rates
+    auto block = [&](int64_t blk, auto fast_tag, auto first_tag) {
         constexpr bool fast = decltype(fast_tag)::value;
+        constexpr bool FIRSTB = decltype(first_tag)::value;
         const int64_t seg = blk + li * T, own = seg + hl * TH;
 
-        // every load of the block first, so that one wait covers them all
+        // every load of the block first. In the first block in the order of
+        // use: u and delta (the step sizes), the carried states and decay
+        // rates, then the B and C rows step by step; vector-memory counters
+        // retire in order, so the step sizes start once u and delta are in
+        // and each step waits only for its own rows, which is what a launch
+        // of one block, whose loads all come from far memory, gains from
+        // (the scheduling barriers keep the compiler from reordering the
+        // groups). Later blocks leave the order to the compiler.
         uint32_t uw[WH], dw[WH], Bw[STEPS][WT], Cw[STEPS][WT];
+        float hraw[STEPS], araw[STEPS];
         load_seg<TH, fast>(u_row, own, p.t1, uw);
         load_seg<TH, fast>(dl_row, own, p.t1, dw);
+        if constexpr (FIRSTB) {
+            __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                hraw[s] = st[row[s]];
+                araw[s] = load_ro(p.A + d * p.A_d + row[s] * p.A_n);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+        }
 #pragma unroll
         for (int s = 0; s < STEPS; ++s) {
             load_seg<T, fast>(B_row + row[s] * p.B_n, seg, p.t1, Bw[s]);
             load_seg<T, fast>(C_row + row[s] * p.C_n, seg, p.t1, Cw[s]);
         }
-        if (blk == p.t0) {
-#pragma unroll
-            for (int s = 0; s < STEPS; ++s) {
-                const float h = st[row[s]], av = load_ro(p.A + d * p.A_d + row[s] * p.A_n);
-                hv[s] = live[s] ? h : 0.0f;
-                A2[s] = live[s] ? av * kLog2e : 0.0f;
-            }
-        }
+        if constexpr (FIRSTB)
+            __builtin_amdgcn_sched_barrier(0);
         if constexpr (!FULL) {
 #pragma unroll
             for (int s = 0; s < STEPS; ++s)
@@ -581,6 +595,13 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
         float dl[T], du[T];
         segment_steps<F16, T, fast>(dw, uw, bias, softplus, own, p.t1, dl, du);
         const float dls = step_sum<T>(dl);
+        if constexpr (FIRSTB) {
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                hv[s] = live[s] ? hraw[s] : 0.0f;
+                A2[s] = live[s] ? araw[s] * kLog2e : 0.0f;
+            }
+        }
 
         // y of the tokens this lane owns: starting from -0 (which adds exactly),
         // the groups' partials added in group order
@@ -642,16 +663,20 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
             store_seg<TH, fast>(o_row, own, p.t1, o);
         }
     };
-    for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+    auto run_block = [&](int64_t blk, auto first_tag) {
         if constexpr (ALLFAST) {
-            block(blk, std::true_type{});
+            block(blk, std::true_type{}, first_tag);
         } else {
             if (vec && blk + BLOCK <= p.t1)
-                block(blk, std::true_type{});
+                block(blk, std::true_type{}, first_tag);
             else
-                block(blk, std::false_type{});
+                block(blk, std::false_type{}, first_tag);
         }
-    }
+    };
+    if (p.t0 < p.t1)
+        run_block(p.t0, std::true_type{});
+    for (int64_t blk = p.t0 + BLOCK; blk < p.t1; blk += BLOCK)
+        run_block(blk, std::false_type{});
 
     // final states: the first lane of each half writes its half's
     if (li == 0) {

@@ -380,11 +380,23 @@ struct Work {
             for (int j = 0; j < R; ++j)
                 o.xbits[j] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + j * RPI))) << 16;
         }
-        // the rows this lane's out values belong to: a lane's own load
-        // instead of a select over its rows' x values
+        // the rows this lane's out values belong to: with 8 or more rows per
+        // lane (the configurations of the instruction-bound K-token launches)
+        // a lane's own load, which is cheaper than a select over its rows'
+        // x values; with fewer, the select (no extra load in a memory-bound
+        // launch). The same value either way.
 #pragma unroll
-        for (int i = 0; i < RS::KEEP; ++i)
-            o.xo[i] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + (fr + i) * RPI))) << 16;
+        for (int i = 0; i < RS::KEEP; ++i) {
+            if constexpr (R >= 8) {
+                o.xo[i] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + (fr + i) * RPI))) << 16;
+            } else {
+                uint32_t v = o.xbits[0];
+#pragma unroll
+                for (int j = 1; j < R; ++j)
+                    v = (fr + i == j) ? o.xbits[j] : v;
+                o.xo[i] = v;
+            }
+        }
     }
 
     // delta = softplus(dt + dt_bias) (or dt + dt_bias) and the decay
