@@ -500,9 +500,12 @@ __device__ __forceinline__ void pass_partials(const float (&yy)[T], float (&lo)[
     }
 }
 
-template <bool F16, int T, int NSW, int MAXW, bool FULL, bool ALLFAST>
+// ONEB: the launch's tokens fit in one block (whole and aligned): that block
+// alone, its loads in the order of use (see below).
+template <bool F16, int T, int NSW, int MAXW, bool FULL, bool ALLFAST, bool ONEB = false>
 __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const ScanParams p)
 {
+    static_assert(!ONEB || ALLFAST, "a one-block launch takes the aligned path");
     constexpr int TH = T / 2, BLOCK = kHalf * T, WT = (T + 1) / 2, WH = (TH + 1) / 2;
     constexpr int STEPS = NSW / 2;          // states per half of the wave
     constexpr int GROUPS = NSW / kGroup;
@@ -547,26 +550,25 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
     }
     const bool vec = p.vec != 0;
 
-    // FIRSTB: the launch's first block, which also reads the carried states
-    // and decay rates
-    auto block = [&](int64_t blk, auto fast_tag, auto first_tag) {
+    auto block = [&](int64_t blk, auto fast_tag) {
         constexpr bool fast = decltype(fast_tag)::value;
-        constexpr bool FIRSTB = decltype(first_tag)::value;
         const int64_t seg = blk + li * T, own = seg + hl * TH;
 
-        // every load of the block first. In the first block in the order of
-        // use: u and delta (the step sizes), the carried states and decay
+        // every load of the block first. In a one-block launch in the order
+        // of use: u and delta (the step sizes), the carried states and decay
         // rates, then the B and C rows step by step; vector-memory counters
         // retire in order, so the step sizes start once u and delta are in
-        // and each step waits only for its own rows, which is what a launch
-        // of one block, whose loads all come from far memory, gains from
-        // (the scheduling barriers keep the compiler from reordering the
-        // groups). Later blocks leave the order to the compiler.
+        // and each step waits only for its own rows (the scheduling barriers
+        // keep the compiler from reordering the groups): such a launch's
+        // loads all come from far memory and nothing else hides them.
+        // Otherwise all of a block's loads are issued before any is used, so
+        // that one wait covers them, and in the first block the states and
+        // rates follow them.
         uint32_t uw[WH], dw[WH], Bw[STEPS][WT], Cw[STEPS][WT];
         float hraw[STEPS], araw[STEPS];
-        load_seg<TH, fast>(u_row, own, p.t1, uw);
-        load_seg<TH, fast>(dl_row, own, p.t1, dw);
-        if constexpr (FIRSTB) {
+        if constexpr (ONEB) {
+            load_seg<TH, fast>(u_row, own, p.t1, uw);
+            load_seg<TH, fast>(dl_row, own, p.t1, dw);
             __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) {
@@ -574,14 +576,30 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
                 araw[s] = load_ro(p.A + d * p.A_d + row[s] * p.A_n);
             }
             __builtin_amdgcn_sched_barrier(0);
-        }
 #pragma unroll
-        for (int s = 0; s < STEPS; ++s) {
-            load_seg<T, fast>(B_row + row[s] * p.B_n, seg, p.t1, Bw[s]);
-            load_seg<T, fast>(C_row + row[s] * p.C_n, seg, p.t1, Cw[s]);
-        }
-        if constexpr (FIRSTB)
+            for (int s = 0; s < STEPS; ++s) {
+                load_seg<T, fast>(B_row + row[s] * p.B_n, seg, p.t1, Bw[s]);
+                load_seg<T, fast>(C_row + row[s] * p.C_n, seg, p.t1, Cw[s]);
+            }
             __builtin_amdgcn_sched_barrier(0);
+        } else {
+            load_seg<TH, fast>(u_row, own, p.t1, uw);
+            load_seg<TH, fast>(dl_row, own, p.t1, dw);
+#pragma unroll
+            for (int s = 0; s < STEPS; ++s) {
+                load_seg<T, fast>(B_row + row[s] * p.B_n, seg, p.t1, Bw[s]);
+                load_seg<T, fast>(C_row + row[s] * p.C_n, seg, p.t1, Cw[s]);
+            }
+            if (blk == p.t0) {
+#pragma unroll
+                for (int s = 0; s < STEPS; ++s) {
+                    const float h = st[row[s]], av = load_ro(p.A + d * p.A_d + row[s] * p.A_n);
+                    hv[s] = live[s] ? h : 0.0f;
+                    A2[s] = live[s] ? av * kLog2e : 0.0f;
+                }
+            }
+        }
+        // states past d_state read a valid row; their B and C count as zero
         if constexpr (!FULL) {
 #pragma unroll
             for (int s = 0; s < STEPS; ++s)
@@ -591,11 +609,10 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
                     Cw[s][k] = live[s] ? Cw[s][k] : 0u;
                 }
         }
-
         float dl[T], du[T];
         segment_steps<F16, T, fast>(dw, uw, bias, softplus, own, p.t1, dl, du);
         const float dls = step_sum<T>(dl);
-        if constexpr (FIRSTB) {
+        if constexpr (ONEB) {
 #pragma unroll
             for (int s = 0; s < STEPS; ++s) {
                 hv[s] = live[s] ? hraw[s] : 0.0f;
@@ -663,20 +680,21 @@ __global__ void __launch_bounds__(kLanes * MAXW) ssu_scan_direct_kernel(const Sc
             store_seg<TH, fast>(o_row, own, p.t1, o);
         }
     };
-    auto run_block = [&](int64_t blk, auto first_tag) {
-        if constexpr (ALLFAST) {
-            block(blk, std::true_type{}, first_tag);
-        } else {
-            if (vec && blk + BLOCK <= p.t1)
-                block(blk, std::true_type{}, first_tag);
-            else
-                block(blk, std::false_type{}, first_tag);
+    if constexpr (ONEB) {
+        if (p.t0 < p.t1)
+            block(p.t0, std::true_type{});
+    } else {
+        for (int64_t blk = p.t0; blk < p.t1; blk += BLOCK) {
+            if constexpr (ALLFAST) {
+                block(blk, std::true_type{});
+            } else {
+                if (vec && blk + BLOCK <= p.t1)
+                    block(blk, std::true_type{});
+                else
+                    block(blk, std::false_type{});
+            }
         }
-    };
-    if (p.t0 < p.t1)
-        run_block(p.t0, std::true_type{});
-    for (int64_t blk = p.t0 + BLOCK; blk < p.t1; blk += BLOCK)
-        run_block(blk, std::false_type{});
+    }
 
     // final states: the first lane of each half writes its half's
     if (li == 0) {
@@ -1198,6 +1216,13 @@ hipError_t launch_direct(const ScanParams &p, int64_t channels, hipStream_t stre
     const int waves = (p.dstate + NSW - 1) / NSW;
     if constexpr (NSW == 16) {
         if (waves == 1) {  // the one-wave instantiation has the whole register file
+            if constexpr (ALLFAST) {
+                if (p.t1 - p.t0 <= static_cast<int64_t>(kHalf) * T) {  // one block
+                    hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, T, NSW, 1, FULL, true, true>), dim3(channels),
+                                       dim3(kLanes), 0, stream, p);
+                    return hipGetLastError();
+                }
+            }
             hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, T, NSW, 1, FULL, ALLFAST>), dim3(channels), dim3(kLanes),
                                0, stream, p);
             return hipGetLastError();
