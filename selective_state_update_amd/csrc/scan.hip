@@ -1228,7 +1228,6 @@ hipError_t launch_direct(const ScanParams &p, int64_t channels, hipStream_t stre
             return hipGetLastError();
         }
     }
-
     hipLaunchKernelGGL((ssu_scan_direct_kernel<F16, T, NSW, kMaxStates / NSW, FULL, ALLFAST>), dim3(channels),
                        dim3(waves * kLanes), 0, stream, p);
     return hipGetLastError();
@@ -1386,6 +1385,10 @@ const ScanTile *scan_tiles(int *count)
 // direct kernel. Configurations that stage B and C rows need their row
 // strides to fit 32-bit offsets (staged_rows_fit); otherwise direct.
 constexpr int64_t kDirectChannels = 1024, kStagedChannels = 2048, kStagedSpan = 1024;
+// A launch of one block: the direct kernel's one-block instantiation, up to
+// this many channels (measured against staged and paired at 2 to 16 requests
+// of 1024 channels and 1 to 16 tokens per lane).
+constexpr int64_t kOneBlockDirectChannels = 8192;
 
 // The staged and paired kernels address a thread's staging pieces as a 32-bit
 // byte offset from a row pointer, over at most kMaxStates rows of B and of C.
@@ -1404,7 +1407,9 @@ int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool sta
             seg = sg;
             break;
         }
-    const bool wide = staged_ok && (channels > kStagedChannels || (channels > kDirectChannels && span <= kStagedSpan));
+    const bool one_block = span <= int64_t(kHalf) * seg && channels <= kOneBlockDirectChannels;
+    const bool wide = staged_ok && !one_block &&
+                      (channels > kStagedChannels || (channels > kDirectChannels && span <= kStagedSpan));
     const bool paired = wide && channels > kStagedChannels && ch_per_group % 8 == 0;
     const bool staged = wide && !paired && ch_per_group % 4 == 0;
     for (int i = 0; i < count; ++i) {

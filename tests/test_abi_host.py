@@ -549,25 +549,28 @@ def test_scan_staged_needs_32bit_row_offsets(ssu, prefix):
 @pytest.mark.parametrize("batch,dim,G,L,chunk,bstride,want", [
     (1, 1024, 1, 4096, 512, None, "scan_t16_n16"),          # up to 1024 channels: direct
     (1, 1024, 1, 4096, 128, None, "scan_t4_n16"),
-    (2, 1024, 1, 4096, 512, None, "scan_t16_n16_w1_c4"),    # up to 2048: staged for spans up to 1024
-    (2, 1024, 1, 4096, 1024, None, "scan_t16_n16_w1_c4"),
-    (2, 1024, 1, 4096, 256, None, "scan_t8_n16_w1_c4"),
+    (2, 1024, 1, 4096, 512, None, "scan_t16_n16"),          # a launch of one block: direct up to 8192 channels
+    (2, 1024, 1, 4096, 256, None, "scan_t8_n16"),
+    (4, 1024, 1, 4096, 128, None, "scan_t4_n16"),
+    (8, 1024, 1, 4096, 512, None, "scan_t16_n16"),
+    (9, 1024, 1, 4096, 512, None, "scan_t16_n16_pair_c8"),  # above 8192: paired
+    (2, 1024, 1, 4096, 1024, None, "scan_t16_n16_w1_c4"),   # up to 2048: staged for spans up to 1024
     (2, 1024, 1, 4096, 2048, None, "scan_t16_n16"),         # direct for longer spans
     (2, 1024, 1, 4096, 0, None, "scan_t16_n16"),
-    (2, 1026, 1, 4096, 512, None, "scan_t16_n16"),          # 1026 is not in fours: direct
-    (3, 700, 1, 4096, 512, None, "scan_t16_n16_w1_c4"),     # 2100 channels above 2048, 700 not in eights
-    (3, 1024, 1, 4096, 512, None, "scan_t16_n16_pair_c8"),  # above: paired
+    (2, 1026, 1, 4096, 1024, None, "scan_t16_n16"),         # 1026 is not in fours: direct
+    (3, 700, 1, 4096, 1024, None, "scan_t16_n16_w1_c4"),    # 2100 channels above 2048, 700 not in eights
+    (3, 1024, 1, 4096, 1024, None, "scan_t16_n16_pair_c8"), # above: paired
     (16, 1024, 1, 4096, 0, None, "scan_t16_n16_pair_c8"),
-    (3, 1028, 1, 4096, 512, None, "scan_t16_n16_w1_c4"),    # a group's channels in fours only: staged
-    (3, 1026, 1, 4096, 512, None, "scan_t16_n16"),          # not in fours either: direct
-    (3, 1024, 2, 4096, 512, None, "scan_t16_n16_pair_c8"),  # 512 channels per group
-    (3, 1032, 2, 4096, 512, None, "scan_t16_n16_w1_c4"),    # 516 per group
+    (3, 1028, 1, 4096, 1024, None, "scan_t16_n16_w1_c4"),   # a group's channels in fours only: staged
+    (3, 1026, 1, 4096, 1024, None, "scan_t16_n16"),         # not in fours either: direct
+    (3, 1024, 2, 4096, 1024, None, "scan_t16_n16_pair_c8"), # 512 channels per group
+    (3, 1032, 2, 4096, 1024, None, "scan_t16_n16_w1_c4"),   # 516 per group
     (16, 1024, 1, 4096, 256, None, "scan_t8_n16_pair_c8"),  # the segment follows the launch's span
     (16, 1024, 1, 4096, 128, None, "scan_t4_n16_pair_c8"),
     (16, 1024, 1, 4096, 100, None, "scan_t2_n16_pair_c8"),
     (1, 64, 1, 300, 0, None, "scan_t8_n16"),
     (1, 64, 1, 300, 5000, None, "scan_t8_n16"),             # a chunk longer than L spans L
-    (16, 1024, 1, 4096, 512, (1 << 30) // 64, "scan_t16_n16"),  # row offsets beyond 32 bits: direct
+    (16, 1024, 1, 4096, 1024, (1 << 30) // 64, "scan_t16_n16"),  # row offsets beyond 32 bits: direct
 ])
 def test_scan_select_tile(ssu, batch, dim, G, L, chunk, bstride, want):
     """The configuration ssu_scan picks by default, as ssu_scan_select_tile

@@ -184,20 +184,22 @@ def test_scan_every_tile_more_states(N):
                 assert np.array_equal(o, o0) and np.array_equal(s, s0), (name, n0, chunk)
 
 
-@pytest.mark.parametrize("batch,dim,G,want", [
-    (3, 1024, 1, "scan_t16_n16_pair_c8"),
-    (3, 1028, 1, "scan_t16_n16_w1_c4"),
-    (3, 1032, 2, "scan_t16_n16_w1_c4"),
-    (3, 1026, 1, "scan_t16_n16"),
-    (2, 1024, 1, "scan_t16_n16_w1_c4"),
+@pytest.mark.parametrize("batch,dim,G,chunk,want", [
+    (3, 1024, 1, 1024, "scan_t16_n16_pair_c8"),
+    (3, 1028, 1, 1024, "scan_t16_n16_w1_c4"),
+    (3, 1032, 2, 1024, "scan_t16_n16_w1_c4"),
+    (3, 1026, 1, 1024, "scan_t16_n16"),
+    (2, 1024, 1, 1024, "scan_t16_n16_w1_c4"),
+    (3, 1024, 1, 512, "scan_t16_n16"),
 ])
-def test_scan_default_rule_branches(batch, dim, G, want):
-    """The default rule's branches at chunk 512: above 2048 channels paired
-    where a group's channels split into eights, staged where only into fours,
-    direct otherwise; staged at 2048 channels. The default picks `want`,
-    matches the oracle everywhere (a ragged last block, chunk 512 and one
-    launch, which picks direct at 2048 channels), and equals the forced
-    direct configuration bitwise."""
+def test_scan_default_rule_branches(batch, dim, G, chunk, want):
+    """The default rule's branches: at chunk 1024 (two blocks) above 2048
+    channels paired where a group's channels split into eights, staged where
+    only into fours, direct otherwise, and staged at 2048 channels; at chunk
+    512 (one block) direct. The default picks `want`, matches the oracle
+    everywhere (a ragged last block, the chunk and one launch, which picks
+    direct at 2048 channels), and equals the forced direct configuration
+    bitwise."""
     import oracle
     import selective_state_update_amd as ssu
 
@@ -205,14 +207,14 @@ def test_scan_default_rule_branches(batch, dim, G, want):
     ds = DeviceScan(p)
     a, _ = ssu.make_scan_args(ds.u, ds.delta, ds.A, ds.B, ds.C, ds.state0.clone(), ds.D, ds.bias)
     names = ssu.scan_tiles()
-    assert names[ssu.scan_select_tile(a, 512)] == want
+    assert names[ssu.scan_select_tile(a, chunk)] == want
     r = oracle_scan(oracle.get(), p)
     direct = names.index("scan_t16_n16")
-    for chunk in (512, 0):
-        o, s = ds.run(chunk=chunk)
-        check(p, o, s, r, f"dim {dim} G {G} {want} chunk {chunk}")
-        od, sd = ds.run(chunk=chunk, tile=direct)
-        assert np.array_equal(o, od) and np.array_equal(s.view(np.uint32), sd.view(np.uint32)), chunk
+    for c in (chunk, 0):
+        o, s = ds.run(chunk=c)
+        check(p, o, s, r, f"dim {dim} G {G} {want} chunk {c}")
+        od, sd = ds.run(chunk=c, tile=direct)
+        assert np.array_equal(o, od) and np.array_equal(s.view(np.uint32), sd.view(np.uint32)), c
 
 
 @pytest.mark.parametrize("L", [1, 7, 63, 64, 65, 511, 513, 1000])
