@@ -329,9 +329,9 @@ const char *ssu_scan_tile_name(int32_t tile);
 
 /* The configuration ssu_scan(args, chunk, -1, ...) launches, from the tokens
  * one launch spans (chunk, or L if chunk is 0 or longer), the number of
- * channels (batch * dim), the channels of a group (dim / ngroups) and B's and
- * C's state strides; only those fields of `args` are read (no pointer is
- * touched). Returns -1 if args is null or those sizes are invalid (negative
+ * channels (batch * dim), the channels of a group (dim / ngroups), dstate and
+ * B's and C's state strides; only those fields of `args` are read (no
+ * pointer is touched). Returns -1 if args is null or those sizes are invalid (negative
  * chunk, batch, seqlen or strides, dim or ngroups below 1, ngroups not
  * dividing dim). */
 int32_t ssu_scan_select_tile(const ssu_scan_args *args, int64_t chunk);

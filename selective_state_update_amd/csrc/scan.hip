@@ -1385,9 +1385,10 @@ const ScanTile *scan_tiles(int *count)
 // direct kernel. Configurations that stage B and C rows need their row
 // strides to fit 32-bit offsets (staged_rows_fit); otherwise direct.
 constexpr int64_t kDirectChannels = 1024, kStagedChannels = 2048, kStagedSpan = 1024;
-// A launch of one block: the direct kernel's one-block instantiation, up to
-// this many channels (measured against staged and paired at 2 to 16 requests
-// of 1024 channels and 1 to 16 tokens per lane).
+// A launch of one block with up to 16 states per channel (one wave): the
+// direct kernel's one-block instantiation, up to this many channels
+// (measured against staged and paired at 2 to 16 requests of 1024 channels,
+// d_state 16, 2 to 16 tokens per lane).
 constexpr int64_t kOneBlockDirectChannels = 8192;
 
 // The staged and paired kernels address a thread's staging pieces as a 32-bit
@@ -1397,7 +1398,7 @@ bool staged_rows_fit(int64_t B_n, int64_t C_n)
     return std::max(B_n, C_n) < (int64_t(1) << 30) / kMaxStates;
 }
 
-int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool staged_ok)
+int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, int dstate, bool staged_ok)
 {
     int count = 0;
     const ScanTile *t = scan_tiles(&count);
@@ -1407,7 +1408,7 @@ int default_scan_tile(int64_t span, int64_t channels, int ch_per_group, bool sta
             seg = sg;
             break;
         }
-    const bool one_block = span <= int64_t(kHalf) * seg && channels <= kOneBlockDirectChannels;
+    const bool one_block = span <= int64_t(kHalf) * seg && channels <= kOneBlockDirectChannels && dstate <= 16;
     const bool wide = staged_ok && !one_block &&
                       (channels > kStagedChannels || (channels > kDirectChannels && span <= kStagedSpan));
     const bool paired = wide && channels > kStagedChannels && ch_per_group % 8 == 0;
@@ -1429,7 +1430,7 @@ int default_scan_tile(const ssu_scan_args &a, int64_t chunk)
 {
     const int64_t L = a.seqlen;
     return default_scan_tile(chunk > 0 ? std::min(chunk, L) : L, static_cast<int64_t>(a.batch) * a.dim,
-                             a.dim / a.ngroups, staged_rows_fit(a.B.stride[2], a.C.stride[2]));
+                             a.dim / a.ngroups, static_cast<int>(a.dstate), staged_rows_fit(a.B.stride[2], a.C.stride[2]));
 }
 
 bool is_io(const ssu_view &v) { return v.dtype == SSU_F16 || v.dtype == SSU_BF16; }

@@ -546,6 +546,18 @@ def test_scan_staged_needs_32bit_row_offsets(ssu, prefix):
     assert err.startswith("ssu_scan") and "strides" in err
 
 
+@pytest.mark.parametrize("batch,dim,G,L,chunk,N,want", [
+    (2, 1024, 1, 4096, 512, 32, "scan_t16_n16_w1_c4"),   # one block, more than 16 states: not the one-block rule
+    (3, 1024, 1, 4096, 512, 64, "scan_t16_n16_pair_c8"),
+    (2, 1024, 1, 4096, 512, 1, "scan_t16_n16"),
+])
+def test_scan_select_tile_states(ssu, batch, dim, G, L, chunk, N, want):
+    """The one-block rule is for up to 16 states per channel (one wave)."""
+    a = _scan_args(ssu, batch=batch, dim=dim, G=G, L=L, N=N)
+    t = ssu.scan_select_tile(a, chunk)
+    assert t >= 0 and ssu.scan_tiles()[t] == want
+
+
 @pytest.mark.parametrize("batch,dim,G,L,chunk,bstride,want", [
     (1, 1024, 1, 4096, 512, None, "scan_t16_n16"),          # up to 1024 channels: direct
     (1, 1024, 1, 4096, 128, None, "scan_t4_n16"),
