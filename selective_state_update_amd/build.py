@@ -52,18 +52,26 @@ def build(extra=(), out: str = LIB, verbose: bool = False) -> str:
 
 PROBE_SRC = os.path.join(HERE, "csrc", "valu_rate_probe.hip")
 PROBE = os.path.join(HERE, "valu_rate_probe")
+MATH_PROBE_SRC = os.path.join(HERE, "csrc", "math_probe.hip")
+MATH_PROBE = os.path.join(HERE, "math_probe")
 
 
-def build_probe(out: str = PROBE) -> str:
-    """The VALU issue-rate probe (a standalone program, same code-generation
-    flags as the library)."""
+def _build_program(src: str, out: str) -> str:
     flags = [f for f in FLAGS if f not in ("-fPIC", "-shared")]
-    cmd = [HIPCC, *flags, "-o", out + ".tmp", PROBE_SRC]
+    cmd = [HIPCC, *flags, "-I", os.path.join(HERE, "csrc"), "-o", out + ".tmp", src]
     res = subprocess.run(cmd, capture_output=True, text=True)
     if res.returncode != 0:
         raise RuntimeError("probe build failed:\n" + " ".join(cmd) + "\n" + res.stdout + res.stderr)
     os.replace(out + ".tmp", out)
     return out
+
+
+def build_probe(out: str = PROBE) -> str:
+    """The standalone probe programs, with the library's code-generation flags:
+    the VALU issue-rate probe (returned) and the exhaustive check of the
+    kernels' shared fp32 helpers (math_probe)."""
+    _build_program(MATH_PROBE_SRC, MATH_PROBE)
+    return _build_program(PROBE_SRC, out)
 
 
 if __name__ == "__main__":

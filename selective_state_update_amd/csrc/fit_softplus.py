@@ -1,4 +1,4 @@
-"""Recompute the polynomial in scan.hip's softplus_f32.
+"""Recompute the polynomial in softplus_f32 (internal.h).
 
 log1p(e) = 2 atanh(s) with s = e / (2 + e), and for e in (0, 1], s is in
 (0, 1/3]. softplus_f32 evaluates 2 atanh(s) as s * q(s^2), q a degree-4

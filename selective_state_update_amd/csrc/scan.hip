@@ -99,7 +99,6 @@ constexpr int kHalf = 32;
 constexpr int kMaxStates = 64;
 constexpr int kGroup = 4;          // states per partial sum of y
 constexpr int kPass = 2 * kGroup;  // states per pass of a wave: a group per half
-constexpr float kLog2e = 1.44269504088896340736f;
 
 using u32x4 = uint32_t __attribute__((ext_vector_type(4)));
 
@@ -294,37 +293,6 @@ __device__ __forceinline__ void swap_halves(float &x, float &y)
 __device__ __forceinline__ float half_last(float v, int lane)
 {
     return __int_as_float(__builtin_amdgcn_ds_bpermute(((lane & kHalf) | (kHalf - 1)) << 2, __float_as_int(v)));
-}
-
-constexpr float kLn2Hi = 0.693147182464599609375f;      // (float)ln 2
-constexpr float kLn2Lo = -1.904654323148236e-09f;       // ln 2 - kLn2Hi
-
-// softplus(v) = max(v, 0) + log1p(e) with e = exp(-|v|) in (0, 1], and
-// log1p(e) = 2 atanh(s) = s q(s^2), s = e / (2 + e) in (0, 1/3]. q is a
-// degree-4 polynomial fitted to 2 atanh(sqrt z) / sqrt z on z in [0, 1/9] by
-// the Remez exchange (relative error 4e-9, under a tenth of an fp32 ulp;
-// fit_softplus.py beside this file recomputes it). e is the hardware exp2 of
-// t = -|v| log2(e) in fp32, times exp(r) ~ 1 + r for the residual
-// r = -|v| - t ln 2 (ln 2 split in two, each product exact in an fma), so the
-// rounding of t costs nothing. -|v| is clamped at -128, where exp2 is already
-// 0 in fp32, so that infinite v give e = 0 rather than inf - inf; the
-// positive part is a select that lets NaN through (fmaxf would drop it):
-// softplus(+inf) = +inf, softplus(-inf) = 0, softplus(NaN) = NaN, and every
-// finite v gives the same bits as without the clamp.
-__device__ __forceinline__ float softplus_f32(float v)
-{
-    const float x = __builtin_amdgcn_fmed3f(-fabsf(v), -128.0f, 0.0f);  // NaN: carried by the select below
-    const float t = x * kLog2e;
-    const float ex = __builtin_amdgcn_exp2f(t);
-    const float r = fmaf(-t, kLn2Lo, fmaf(-t, kLn2Hi, x));
-    const float e = fmaf(ex, r, ex);
-    const float sv = e * __builtin_amdgcn_rcpf(2.0f + e);
-    const float z = sv * sv;
-    float q = fmaf(2.817833424e-01f, z, 2.796060145e-01f);
-    q = fmaf(q, z, 4.002490938e-01f);
-    q = fmaf(q, z, 6.666631699e-01f);
-    q = fmaf(q, z, 2.0f);
-    return fmaf(sv, q, v <= 0.0f ? 0.0f : v);
 }
 
 // One state per half over one block of 32 * T tokens, in this lane's segment

@@ -400,12 +400,13 @@ struct Work {
     }
 
     // delta = softplus(dt + dt_bias) (or dt + dt_bias) and the decay
-    // exp(A * delta) from a bf16 dt bit pattern.
+    // exp(A * delta) from a bf16 dt bit pattern (the fp32 softplus and exp
+    // of internal.h: a few ulp each, NaN and infinities kept).
     __device__ __forceinline__ void discretize(const Params &p, uint32_t bits, float &delta, float &dA) const
     {
         const float u = __uint_as_float(bits << 16) + bias;
-        delta = p.softplus ? fmaxf(u, 0.0f) + log1pf(expf(-fabsf(u))) : u;
-        dA = expf(Ah * delta);
+        delta = p.softplus ? softplus_f32(u) : u;
+        dA = exp_f32(Ah * delta);
     }
 
     // graw: workgroup-order tile id (>= total_groups: nothing to do).
