@@ -860,6 +860,29 @@ int select_tile(const ssu_config &c, int32_t batch, int32_t ntokens)
         if (id >= 0)
             return id;
     }
+    if (ntokens <= 1) {
+        // One token below 32 MiB of state: about one wave per SIMD (1024 on
+        // the chip), each streaming an equal share, i.e. as many loads per
+        // lane as the call has MiB of state (a power of two, 2 to 16), in
+        // two-wave groups from 8 loads per lane. From a sweep of every
+        // configuration at H16 batch 1 to 64 and at H8 / H64 (us per call:
+        // 4 MiB 3.39 with four loads against 3.75 with two; 8 MiB 4.79 with
+        // eight in two-wave groups against 5.41; 16 MiB 7.01-7.16 with
+        // sixteen against 8.14-8.28; 2 MiB and below two loads, within 1% of
+        // the fastest). Where the shape has no such configuration, fewer
+        // loads.
+        int loads = 2;
+        while (loads < 16 && (static_cast<int64_t>(loads) << 20) < state_bytes)
+            loads *= 2;
+        for (; loads >= 1; loads /= 2) {
+            const int W = loads >= 8 ? 2 : 1;
+            int id = pick(loads, W, 0);
+            if (id < 0 && W > 1)
+                id = pick(loads, 1, 0);
+            if (id >= 0)
+                return id;
+        }
+    }
     const int64_t target_groups = 1024;
     int fallback = -1;
     for (int loads : {2, 1}) {

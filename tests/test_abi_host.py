@@ -168,14 +168,16 @@ def test_forced_tile_accepted_iff_it_fits(ssu, H, N, P):
 
 
 @pytest.mark.parametrize("bs,K,name", [
-    (512, 1, "n128_r8_w1_nt_xcd_g12"), (128, 1, "n128_r8_w1_nt_xcd_g12"), (8, 1, "n128_r4_w2_nt_xcd"),
+    (512, 1, "n128_r8_w1_nt_xcd_g12"), (128, 1, "n128_r8_w1_nt_xcd_g12"), (64, 1, "n128_r8_w1_nt_xcd_g12"),
+    (32, 1, "n128_r32_w2_nt_xcd"), (16, 1, "n128_r16_w2_nt_xcd"), (8, 1, "n128_r8_w1_nt_xcd"),
+    (4, 1, "n128_r4_w1_nt_xcd"), (1, 1, "n128_r4_w1_nt_xcd"),
     (512, 2, "n128_r8_w1_nt_xcd"), (512, 3, "n128_r8_w1_nt_xcd"), (512, 4, "n128_r8_w1_nt_xcd"),
     (512, 8, "n128_r16_w1_nt_xcd"), (512, 16, "n128_r16_w2_nt_xcd"),
     (128, 4, "n128_r16_w1_nt_xcd"), (128, 16, "n128_r16_w2_nt_xcd"),
 ])
 def test_launch_rule_at_the_swept_points(ssu, bs, K, name):
     """The launch table picks, at H16 P64 N128, the configurations the tile
-    sweeps measured fastest (or within 0.2% of it)."""
+    sweeps measured fastest (or within 1% of it)."""
     st, h = _create(ssu)
     assert st == 0
     i = ssu._lib.ssu_select_tile_tokens(h, bs, K) if K > 1 else ssu._lib.ssu_select_tile(h, bs)
