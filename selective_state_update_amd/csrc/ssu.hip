@@ -327,15 +327,23 @@ struct Work {
     int64_t jstep;
     f32x4 s[R][VEC];
     uint32_t dtbits;
+    uint32_t dtlane, dtshift;  // LANEDT: the word holding the dt of token `lane`, its bit offset
     float bias, Ah, Dh;
 
     // One token's operands for this lane: its columns of B and C (bf16
-    // pairs), the x of its rows and of the rows whose out it writes (bf16 in
-    // the upper half of each word).
+    // pairs), the x of its rows and of the rows whose out it writes. The x
+    // words hold the bf16 in the upper half (the fp32 value it stands for),
+    // except those read by the lane's own 16-bit loads (XRAW, XORAW), which
+    // hold it in the lower half until step() uses them: a value shifted where
+    // it is loaded would make the wave wait for that load (and for the state
+    // loads issued before it) before anything else, e.g. the discretisation
+    // of the first tokens, could run.
+    static constexpr bool XRAW = RPI != 2;
+    static constexpr bool XORAW = XRAW || R >= 8;
     struct Ops {
         u32x2 Bw[VEC], Cw[VEC];
         uint32_t xbits[R];
-        uint32_t xo[RS::KEEP];
+        uint32_t xo[R >= 8 ? RS::KEEP : 1];  // R >= 8: the x of the out rows
     };
     Ops op;  // token 0's, requested by fetch()
 
@@ -378,24 +386,34 @@ struct Work {
         } else {
 #pragma unroll
             for (int j = 0; j < R; ++j)
-                o.xbits[j] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + j * RPI))) << 16;
+                o.xbits[j] = *lane_at(xrow, 2u * (sub + j * RPI));
         }
         // the rows this lane's out values belong to: with 8 or more rows per
         // lane (the configurations of the instruction-bound K-token launches)
         // a lane's own load, which is cheaper than a select over its rows'
-        // x values; with fewer, the select (no extra load in a memory-bound
-        // launch). The same value either way.
+        // x values; with fewer, step() selects them (no extra load in a
+        // memory-bound launch). The same value either way.
+        if constexpr (R >= 8) {
 #pragma unroll
-        for (int i = 0; i < RS::KEEP; ++i) {
-            if constexpr (R >= 8) {
-                o.xo[i] = static_cast<uint32_t>(*lane_at(xrow, 2u * (sub + (fr + i) * RPI))) << 16;
-            } else {
-                uint32_t v = o.xbits[0];
+            for (int i = 0; i < RS::KEEP; ++i)
+                o.xo[i] = *lane_at(xrow, 2u * (sub + (fr + i) * RPI));
+        }
+    }
+
+    // The x word of out row fr + i (see Ops).
+    __device__ __forceinline__ uint32_t xout(const Ops &o, int i) const
+    {
+        if constexpr (R >= 8) {
+            return o.xo[i];
+        } else {
+            uint32_t v = o.xbits[0];
 #pragma unroll
-                for (int j = 1; j < R; ++j)
-                    v = (fr + i == j) ? o.xbits[j] : v;
-                o.xo[i] = v;
+            for (int j = 1; j < R; ++j) {
+                uint32_t xj = o.xbits[j];
+                asm("" : "+v"(xj));
+                v = (fr + i == j) ? xj : v;
             }
+            return v;
         }
     }
 
@@ -411,8 +429,12 @@ struct Work {
 
     // graw: workgroup-order tile id (>= total_groups: nothing to do).
     // PRIO: the caller raised the wave's priority; it is lowered once the
-    // state loads are issued.
-    template <bool PRIO = false>
+    // state loads are issued. LANEDT: each lane also requests the word that
+    // holds the dt of token min(lane, p.ntokens - 1) ahead of the state, so
+    // that the tokens' discretisation can run while the state is in flight
+    // (the bits are taken out of the word where they are used, so that
+    // nothing here waits for the load).
+    template <bool PRIO = false, bool LANEDT = false>
     __device__ __forceinline__ void fetch(const Params &p, int graw, int rows_group, int wave, int lane)
     {
         if (graw >= p.total_groups) {
@@ -450,6 +472,12 @@ struct Work {
         live = slot >= 0 && slot < p.pool_slots;
         if (!live)
             return;  // padding entry: no state traffic, out rows untouched
+        if constexpr (LANEDT) {
+            const int tok = min(lane, p.ntokens - 1);
+            const int64_t dte = b * p.dt_b + tok * p.dt_t + h * p.dt_h + p.dt_off;
+            dtlane = p.dt_words[dte >> 1];
+            dtshift = static_cast<uint32_t>(dte & 1) * 16u;
+        }
 
         // State loads: all R * VEC dwordx4 of this lane are requested up front.
         sp = p.state + slot * p.s_slot + h * p.s_head + static_cast<int64_t>(p0) * p.s_row + 4 * c;
@@ -496,7 +524,7 @@ struct Work {
         float y[R];
 #pragma unroll
         for (int j = 0; j < R; ++j) {
-            const float xj = __uint_as_float(o.xbits[j]);
+            const float xj = __uint_as_float(XRAW ? o.xbits[j] << 16 : o.xbits[j]);
             float acc = 0.0f;
 #pragma unroll
             for (int v = 0; v < VEC; ++v) {
@@ -525,8 +553,11 @@ struct Work {
         uint16_t *const orow = oh + t * p.o_t;
         if (RS::writer(c)) {
 #pragma unroll
-            for (int i = 0; i < RS::KEEP; ++i)
-                *lane_at(orow, 2u * (sub + (fr + i) * RPI)) = bf16_round(fmaf(Dh, __uint_as_float(o.xo[i]), y[i]));
+            for (int i = 0; i < RS::KEEP; ++i) {
+                const uint32_t xw = xout(o, i);
+                const float xo = __uint_as_float(XORAW ? xw << 16 : xw);
+                *lane_at(orow, 2u * (sub + (fr + i) * RPI)) = bf16_round(fmaf(Dh, xo, y[i]));
+            }
         }
     }
 
@@ -558,7 +589,8 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_kernel(const Params p)
 // alternate without register copies), and the per-token discretisation is
 // done 64 tokens at a time, one token per lane (the same fp32 operations as
 // the one-token kernel, so the same bits), then read back with a uniform lane
-// read.
+// read; the first 64 tokens' dt are requested ahead of the state, so their
+// discretisation overlaps the state's flight instead of following it.
 template <int N, int R, int W, bool NT>
 __global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params p)
 {
@@ -570,47 +602,52 @@ __global__ void __launch_bounds__(64 * W) ssu_decode_tokens_kernel(const Params 
     // computing tokens on state that has arrived (fetch() drops the priority
     // after the state loads), so the state stream starts sooner.
     __builtin_amdgcn_s_setprio(2);
-    w.template fetch<true>(p, static_cast<int>(blockIdx.x), WK::ROWS_WAVE * W, wave, lane);
-    if (!w.live)
-        return;
-    const int K = p.ntokens;
-    float lane_delta = 0.0f, lane_dA = 1.0f;
-    // (delta, dA) of token t, discretising tokens t .. t+63 when t starts a
-    // group of 64
-    auto disc = [&](int t, float &delta, float &dA) {
-        const int tl = t & 63;
-        if (tl == 0 && t + lane < K) {
-            const int64_t dte = w.b * p.dt_b + (t + lane) * p.dt_t + w.h * p.dt_h + p.dt_off;
-            const uint32_t dtw = p.dt_words[dte >> 1];
-            w.discretize(p, (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu), lane_delta, lane_dA);
+    w.template fetch<true, true>(p, static_cast<int>(blockIdx.x), WK::ROWS_WAVE * W, wave, lane);
+    // (the tokens under the branch, not after an early return: the state's
+    // and x's loads then stay unconsumed until their first use below)
+    if (w.live) {
+        const int K = p.ntokens;
+        float lane_delta = 0.0f, lane_dA = 1.0f;
+        // tokens 0 .. 63 from the dt words requested before the state (lanes
+        // past the last token repeat it; their values are never read)
+        w.discretize(p, (w.dtlane >> w.dtshift) & 0xffffu, lane_delta, lane_dA);
+        // (delta, dA) of token t, discretising tokens t .. t+63 when t > 0 starts
+        // a group of 64
+        auto disc = [&](int t, float &delta, float &dA) {
+            const int tl = t & 63;
+            if (tl == 0 && t > 0 && t + lane < K) {
+                const int64_t dte = w.b * p.dt_b + (t + lane) * p.dt_t + w.h * p.dt_h + p.dt_off;
+                const uint32_t dtw = p.dt_words[dte >> 1];
+                w.discretize(p, (dte & 1) ? (dtw >> 16) : (dtw & 0xffffu), lane_delta, lane_dA);
+            }
+            delta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_delta), tl));
+            dA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_dA), tl));
+        };
+        typename WK::Ops o1;
+        float delta, dA;
+        int t = 0;
+        for (; t + 2 < K; t += 2) {  // tokens t (operands w.op) and t+1 (o1)
+            w.load_bc(p, t + 1, o1);
+            w.load_x(p, t + 1, o1);
+            disc(t, delta, dA);
+            w.template step<false>(p, t, w.op, delta, dA);
+            w.load_bc(p, t + 2, w.op);
+            w.load_x(p, t + 2, w.op);
+            disc(t + 1, delta, dA);
+            w.template step<false>(p, t + 1, o1, delta, dA);
         }
-        delta = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_delta), tl));
-        dA = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(lane_dA), tl));
-    };
-    typename WK::Ops o1;
-    float delta, dA;
-    int t = 0;
-    for (; t + 2 < K; t += 2) {  // tokens t (operands w.op) and t+1 (o1)
-        w.load_bc(p, t + 1, o1);
-        w.load_x(p, t + 1, o1);
-        disc(t, delta, dA);
-        w.template step<false>(p, t, w.op, delta, dA);
-        w.load_bc(p, t + 2, w.op);
-        w.load_x(p, t + 2, w.op);
-        disc(t + 1, delta, dA);
-        w.template step<false>(p, t + 1, o1, delta, dA);
-    }
-    // one or two tokens left, the first with operands w.op
-    if (t + 1 < K) {
-        w.load_bc(p, t + 1, o1);
-        w.load_x(p, t + 1, o1);
-        disc(t, delta, dA);
-        w.template step<false>(p, t, w.op, delta, dA);
-        disc(t + 1, delta, dA);
-        w.template step<true>(p, t + 1, o1, delta, dA);
-    } else {
-        disc(t, delta, dA);
-        w.template step<true>(p, t, w.op, delta, dA);
+        // one or two tokens left, the first with operands w.op
+        if (t + 1 < K) {
+            w.load_bc(p, t + 1, o1);
+            w.load_x(p, t + 1, o1);
+            disc(t, delta, dA);
+            w.template step<false>(p, t, w.op, delta, dA);
+            disc(t + 1, delta, dA);
+            w.template step<true>(p, t + 1, o1, delta, dA);
+        } else {
+            disc(t, delta, dA);
+            w.template step<true>(p, t, w.op, delta, dA);
+        }
     }
 }
 
