@@ -400,7 +400,10 @@ struct Work {
         }
     }
 
-    // The x word of out row fr + i (see Ops).
+    // The x word of out row fr + i (see Ops). The selects go through an
+    // opaque copy of each word: written plainly, the compiler turns the chain
+    // into an array read at a run-time index and moves the operand set to
+    // scratch memory.
     __device__ __forceinline__ uint32_t xout(const Ops &o, int i) const
     {
         if constexpr (R >= 8) {
