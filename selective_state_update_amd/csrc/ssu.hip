@@ -717,6 +717,9 @@ template <bool NT>
 void add_n128(std::vector<Tile> &v)
 {
     const std::initializer_list<int> caps = {2, 3, 4, 5, 6, 7, 8, 10, 12, 16};
+    // (the four-load one-wave kernel also at 14 and 20 groups per CU: the
+    // caps of 2- and 3-token calls on large batches)
+    const std::initializer_list<int> caps_r4w1 = {2, 3, 4, 5, 6, 7, 8, 10, 12, 14, 16, 20};
     add_kernel<128, 1, 1, NT>(v, caps);
     add_kernel<128, 1, 2, NT>(v, caps);
     add_kernel<128, 1, 4, NT>(v, caps);
@@ -725,7 +728,7 @@ void add_n128(std::vector<Tile> &v)
     add_kernel<128, 2, 2, NT>(v, caps);
     add_kernel<128, 2, 4, NT>(v, caps);
     add_kernel<128, 2, 8, NT>(v, caps);
-    add_kernel<128, 4, 1, NT>(v, caps);
+    add_kernel<128, 4, 1, NT>(v, caps_r4w1);
     add_kernel<128, 4, 2, NT>(v, caps);
     add_kernel<128, 4, 4, NT>(v, caps);
     add_kernel<128, 4, 8, NT>(v, caps);
@@ -890,11 +893,18 @@ int select_tile(const ssu_config &c, int32_t batch, int32_t ntokens)
         // capped at 12), and from 16 tokens two-wave groups (batch 512:
         // 154.6 us against 156.8 us with one wave). At 4 tokens four loads
         // lead at batch 512 (96.6 against 98.6 us), eight at batch 128 (29.2
-        // against 30.1 us).
+        // against 30.1 us). Between one token and four the best residency
+        // rises with the work per wave: at batch 512 2 tokens take 91.0 us at
+        // 14 groups per CU (12: 93.4, 16: 91.2, uncapped 92.4) and 3 tokens
+        // 92.3 us at 20 (16: 93.5, uncapped 92.9); at batch 128 uncapped
+        // leads from 2 tokens on. Shapes without such a cap run uncapped.
         const bool big = state_bytes >= (int64_t(128) << 20);
         const int loads = (ntokens >= 8 || (ntokens >= 4 && !big)) ? 8 : 4;
         const int waves = ntokens >= 16 ? 2 : 1;
-        int id = pick(loads, waves, ntokens > 1 ? 0 : 12);
+        const int cap = ntokens == 1 ? 12 : !big ? 0 : ntokens == 2 ? 14 : ntokens == 3 ? 20 : 0;
+        int id = pick(loads, waves, cap);
+        if (id < 0 && ntokens > 1 && cap > 0)
+            id = pick(loads, waves, 0);
         if (id < 0 && waves > 1)
             id = pick(loads, 1, 0);
         if (id >= 0)

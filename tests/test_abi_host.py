@@ -171,7 +171,8 @@ def test_forced_tile_accepted_iff_it_fits(ssu, H, N, P):
     (512, 1, "n128_r8_w1_nt_xcd_g12"), (128, 1, "n128_r8_w1_nt_xcd_g12"), (64, 1, "n128_r8_w1_nt_xcd_g12"),
     (32, 1, "n128_r32_w2_nt_xcd"), (16, 1, "n128_r16_w2_nt_xcd"), (8, 1, "n128_r8_w1_nt_xcd"),
     (4, 1, "n128_r4_w1_nt_xcd"), (1, 1, "n128_r4_w1_nt_xcd"),
-    (512, 2, "n128_r8_w1_nt_xcd"), (512, 3, "n128_r8_w1_nt_xcd"), (512, 4, "n128_r8_w1_nt_xcd"),
+    (512, 2, "n128_r8_w1_nt_xcd_g14"), (512, 3, "n128_r8_w1_nt_xcd_g20"), (512, 4, "n128_r8_w1_nt_xcd"),
+    (256, 2, "n128_r8_w1_nt_xcd_g14"), (128, 2, "n128_r8_w1_nt_xcd"), (128, 3, "n128_r8_w1_nt_xcd"),
     (512, 8, "n128_r16_w1_nt_xcd"), (512, 16, "n128_r16_w2_nt_xcd"),
     (128, 4, "n128_r16_w1_nt_xcd"), (128, 16, "n128_r16_w2_nt_xcd"),
 ])
