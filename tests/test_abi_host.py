@@ -192,8 +192,8 @@ def test_select_tile_tokens_fits_shape(ssu, N, P):
     st, h = _create(ssu, dstate=N, headdim=P)
     assert st == 0
     t = ssu.tiles()
-    for bs in (1, 8, 128, 512, 1024):
-        for K in (2, 4, 8, 16, 64):
+    for bs in (1, 8, 128, 512, 1024, 4096):
+        for K in (2, 3, 4, 8, 16, 64):
             i = ssu._lib.ssu_select_tile_tokens(h, bs, K)
             assert i >= 0
             assert t[i]["dstate"] == N and ssu.tile_fits(t[i], 16, P)
