@@ -5,7 +5,7 @@ configurations give bitwise-identical output and state.
 
 At every point, in the launch configuration the library picks:
   * every request against the CPU oracle, state and out, at the points that
-    move at most 64 MiB of state per call (batch x heads <= 2048: 272 of the
+    move at most 256 MiB of state per call (batch x heads <= 8192: 528 of the
     920 points); three sampled requests (all heads) at the larger points;
   * untouched pool slots bitwise unchanged;
   * a rerun from the restored pool bitwise identical (determinism);
@@ -22,7 +22,7 @@ pytestmark = [pytest.mark.gpu, pytest.mark.slow]
 
 BATCHES = sorted({bs for (_, bs) in si.sweep_points()})
 # (request, head) units up to which every request is compared with the oracle
-FULL_CHECK_UNITS = 2048
+FULL_CHECK_UNITS = 8192
 
 
 @pytest.fixture(autouse=True)
