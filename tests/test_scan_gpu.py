@@ -500,13 +500,10 @@ def test_scan_nonfinite_inputs():
     assert not bad.any(), "finite states"
 
 
-def test_scan_many_requests_sampled():
+def test_scan_many_requests():
     """The saturation workload: 16 requests x 1024 channels, d_state 16, 4096
     fp16 tokens, static chunk 512. Chunk 512 is bitwise equal to one launch,
-    and sampled (request, channel) pairs, the corners among them, match the
-    oracle's scan of that pair alone."""
-    import dataclasses
-
+    and every output and final state matches the oracle's scan."""
     import oracle
 
     p = si.make_scan_problem(16, 1024, 16, 4096, io="f16", seed=17, zero_state=False)
@@ -515,11 +512,5 @@ def test_scan_many_requests_sampled():
     out1, st1 = ds.run(chunk=0)
     assert np.array_equal(out512, out1), "chunk 512 and one launch differ (out)"
     assert np.array_equal(st512.view(np.uint32), st1.view(np.uint32)), "chunk 512 and one launch differ (state)"
-    rng = np.random.default_rng(17)
-    pairs = [(0, 0), (15, 1023), (7, 512)] + [(int(rng.integers(16)), int(rng.integers(1024))) for _ in range(5)]
-    for b, d in pairs:
-        q = dataclasses.replace(p, batch=1, dim=1, u=p.u[b:b + 1, d:d + 1], delta=p.delta[b:b + 1, d:d + 1],
-                                B=p.B[b:b + 1], C=p.C[b:b + 1], A=p.A[d:d + 1], D=p.D[d:d + 1],
-                                delta_bias=p.delta_bias[d:d + 1], state=p.state[b:b + 1, d:d + 1])
-        r = oracle_scan(oracle.get(), q)
-        check(q, out512[b:b + 1, d:d + 1], st512[b:b + 1, d:d + 1], r, f"request {b} channel {d}")
+    r = oracle_scan(oracle.get(), p)
+    check(p, out512, st512, r, "16 requests x 1024 channels")

@@ -149,11 +149,12 @@ def test_tokens_padding():
     assert np.array_equal(pool.cpu().numpy()[untouched], tp.base.pool[untouched])
 
 
-@pytest.mark.parametrize("K,tile", [(4, "n128_r8_w1_nt_xcd"), (8, "n128_r16_w1_nt_xcd"),
+@pytest.mark.parametrize("K,tile", [(2, "n128_r8_w1_nt_xcd_g14"), (3, "n128_r8_w1_nt_xcd_g20"),
+                                    (4, "n128_r8_w1_nt_xcd"), (8, "n128_r16_w1_nt_xcd"),
                                     (16, "n128_r16_w2_nt_xcd")])
-def test_tokens_headline_shape_sampled(ref, K, tile):
+def test_tokens_headline_shape(ref, K, tile):
     """H16 P64 N128, batch 512, K tokens (the state read and written once), in
-    the launch configuration the library picks for K: sampled requests against
+    the launch configuration the library picks for K: every request against
     the oracle's scan."""
     import selective_state_update_amd as ssu
 
@@ -168,7 +169,7 @@ def test_tokens_headline_shape_sampled(ref, K, tile):
     d = tp.device(pool)
     out = h.update_tokens(d["pool"], d["idx"], d["x"], d["B"], d["C"], d["dt"], d["A"], d["D"], d["dt_bias"])
     torch.cuda.synchronize()
-    sample = np.array([0, 77, 300, 511])
+    sample = np.arange(bs)
     sl = torch.from_numpy(tp.base.idx[sample].astype(np.int64)).cuda()
     r = tp.oracle(ref, before[sl].cpu().numpy(), sample=sample)
     gu.assert_state(pool[sl].cpu().numpy(), r["state"], "tokens headline")
